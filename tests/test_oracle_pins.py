@@ -1,0 +1,368 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle itself.
+
+The pages print no worked numerical example (How We Built TLX: listings 1 and 2 show code
+only), so every pin here is a closed form, an exactness invariant, brute force on tiny
+inputs, or a library routine (numpy's BLAS matmul, scipy's logistic function) that the
+oracle does not use.  Each is chosen so that a plausible slip (dropped term, wrong sign,
+swapped index, transposed operand, wrong group or user lookup) fails at least one test.
+"""
+from fractions import Fraction
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import workloads as wl
+from workloads import B_KN, B_NK, EPI_BIAS, EPI_BIAS_SILU, EPI_NONE, EPI_SILU
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+def dec(b):
+    return wl.bf16_bits_to_f32(b).astype(np.float64)
+
+
+def rand_bf16(rng, shape, lo=-1.0, hi=1.0):
+    return wl.f32_to_bf16_bits(rng.uniform(lo, hi, shape).astype(np.float32))
+
+
+def int_bf16(rng, shape, lo=-4, hi=4):
+    """Small integers: exact in bfloat16, and every partial sum stays an exact integer."""
+    return wl.f32_to_bf16_bits(rng.integers(lo, hi + 1, shape).astype(np.float32))
+
+
+def to_layout(Bkn, layout):
+    return Bkn if layout == B_KN else np.ascontiguousarray(Bkn.T)
+
+
+# ---------------------------------------------------------------------------------------
+# plain gemm
+# ---------------------------------------------------------------------------------------
+TINY = [(1, 1, 1), (1, 7, 3), (5, 1, 9), (3, 17, 2), (17, 5, 16), (8, 8, 8), (2, 33, 31), (13, 11, 64)]
+
+
+@pytest.mark.parametrize("layout", [B_KN, B_NK])
+@pytest.mark.parametrize("M,N,K", TINY)
+def test_gemm_brute_force_tiny(M, N, K, layout):
+    """Pure-Python triple loop (ascending k, double): equal to the last bit."""
+    rng = np.random.default_rng(1000 + M * 31 + N * 7 + K)
+    A = rand_bf16(rng, (M, K))
+    Bkn = rand_bf16(rng, (K, N))
+    got = oracle.gemm(A, to_layout(Bkn, layout), layout)
+    a, b = dec(A).tolist(), dec(Bkn).tolist()
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += a[i][k] * b[k][j]
+            assert got[i, j] == s
+
+
+@pytest.mark.parametrize("layout", [B_KN, B_NK])
+@pytest.mark.parametrize("M,N,K", [(67, 129, 96), (128, 64, 300), (33, 250, 1024)])
+def test_gemm_vs_numpy_medium(M, N, K, layout):
+    rng = np.random.default_rng(M + N + K)
+    A = rand_bf16(rng, (M, K))
+    Bkn = rand_bf16(rng, (K, N))
+    ref = dec(A) @ dec(Bkn)
+    got = oracle.gemm(A, to_layout(Bkn, layout), layout)
+    scale = np.abs(dec(A)) @ np.abs(dec(Bkn))
+    assert np.all(np.abs(got - ref) <= 1e-13 * scale + 1e-300)
+
+
+@pytest.mark.parametrize("layout", [B_KN, B_NK])
+def test_gemm_integer_exact(layout):
+    """Integer entries: every sum is exact in double, so any correct order agrees exactly."""
+    rng = np.random.default_rng(7)
+    M, N, K = 96, 80, 520
+    A = int_bf16(rng, (M, K))
+    Bkn = int_bf16(rng, (K, N))
+    ref = dec(A) @ dec(Bkn)
+    got = oracle.gemm(A, to_layout(Bkn, layout), layout)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("layout", [B_KN, B_NK])
+def test_gemm_identity_and_permutation(layout):
+    rng = np.random.default_rng(11)
+    M, K = 40, 48
+    A = rand_bf16(rng, (M, K))
+    eye = wl.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    assert np.array_equal(oracle.gemm(A, to_layout(eye, layout), layout), dec(A))
+    # P . B permutes the rows of B: (P B)[i] = B[perm[i]]
+    perm = rng.permutation(K)
+    P = np.zeros((K, K), np.float32)
+    P[np.arange(K), perm] = 1.0
+    Bkn = rand_bf16(rng, (K, 24))
+    got = oracle.gemm(wl.f32_to_bf16_bits(P), to_layout(Bkn, layout), layout)
+    assert np.array_equal(got, dec(Bkn)[perm])
+    # A . P^T permutes the columns of A
+    got = oracle.gemm(A, to_layout(wl.f32_to_bf16_bits(P.T.copy()), layout), layout)
+    assert np.array_equal(got, dec(A)[:, perm])
+
+
+def test_gemm_all_ones_and_rank_one():
+    M, N, K = 9, 13, 777
+    ones_a = wl.f32_to_bf16_bits(np.ones((M, K), np.float32))
+    ones_b = wl.f32_to_bf16_bits(np.ones((K, N), np.float32))
+    assert np.all(oracle.gemm(ones_a, ones_b, B_KN) == K)
+    # (u 1^T)(1 v^T) = K u v^T
+    u = np.arange(-4, M - 4, dtype=np.float32)
+    v = np.arange(1, N + 1, dtype=np.float32)
+    A = wl.f32_to_bf16_bits(np.repeat(u[:, None], K, axis=1))
+    B = wl.f32_to_bf16_bits(np.repeat(v[None, :], K, axis=0))
+    assert np.array_equal(oracle.gemm(A, B, B_KN), K * np.outer(u, v).astype(np.float64))
+    assert np.array_equal(oracle.gemm(A, np.ascontiguousarray(B.T), B_NK),
+                          K * np.outer(u, v).astype(np.float64))
+
+
+def test_gemm_rows_subset_and_strides():
+    rng = np.random.default_rng(3)
+    A = rand_bf16(rng, (50, 64))
+    B = rand_bf16(rng, (64, 40))
+    full = oracle.gemm(A, B, B_KN)
+    rows = [49, 0, 17, 17, 3]
+    assert np.array_equal(oracle.gemm(A, B, B_KN, rows=rows), full[rows])
+    with pytest.raises(oracle.OracleError):
+        oracle.gemm(A, B, B_KN, rows=[50])
+
+
+def test_gemm_zero_k_is_bias_epilogue():
+    A = np.zeros((3, 0), np.uint16)
+    B = np.zeros((0, 4), np.uint16)
+    bias = np.array([1.0, -2.0, 0.0, 3.0], np.float32)
+    got = oracle.gemm(A, B, B_KN, bias, EPI_BIAS)
+    assert np.array_equal(got, np.tile(bias.astype(np.float64), (3, 1)))
+
+
+# ---------------------------------------------------------------------------------------
+# epilogue
+# ---------------------------------------------------------------------------------------
+def test_silu_values():
+    xs = np.array([-30.0, -5.0, -1.0, -0.25, 0.0, 1e-8, 0.5, 1.0, 3.0, 20.0, 100.0])
+    ref = xs * scipy.special.expit(xs)
+    got = np.array([oracle.silu(x) for x in xs])
+    assert np.allclose(got, ref, rtol=1e-15, atol=0)
+    # odd-part identity: silu(x) - silu(-x) = x
+    for x in xs:
+        assert math.isclose(oracle.silu(x) - oracle.silu(-x), x, rel_tol=1e-15, abs_tol=1e-300)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(800.0) == 800.0
+    neg = oracle.silu(-800.0)
+    assert neg == 0.0 and math.copysign(1.0, neg) < 0
+
+
+@pytest.mark.parametrize("epi", [EPI_NONE, EPI_BIAS, EPI_SILU, EPI_BIAS_SILU])
+def test_epilogue_order(epi):
+    """Bias is added to the sum before SiLU; a zero A isolates the epilogue."""
+    rng = np.random.default_rng(5)
+    K, N = 16, 12
+    A = wl.f32_to_bf16_bits(np.zeros((2, K), np.float32))
+    A2 = rand_bf16(rng, (2, K))
+    B = rand_bf16(rng, (K, N))
+    bias = (rng.standard_normal(N) * 2).astype(np.float32)
+    b64 = bias.astype(np.float64)
+    got0 = oracle.gemm(A, B, B_KN, bias, epi)
+    acc = dec(A2) @ dec(B)
+    got = oracle.gemm(A2, B, B_KN, bias, epi)
+    if epi == EPI_NONE:
+        exp0, exp = np.zeros((2, N)), acc
+    elif epi == EPI_BIAS:
+        exp0, exp = np.tile(b64, (2, 1)), acc + b64
+    elif epi == EPI_SILU:
+        exp0, exp = np.zeros((2, N)), acc * scipy.special.expit(acc)
+    else:
+        exp0 = np.tile(b64 * scipy.special.expit(b64), (2, 1))
+        exp = (acc + b64) * scipy.special.expit(acc + b64)
+    assert np.allclose(got0, exp0, rtol=1e-14, atol=0)
+    assert np.allclose(got, exp, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------------------
+# rounding
+# ---------------------------------------------------------------------------------------
+def _all_finite_bf16():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        vals = wl.bf16_bits_to_f32(bits).astype(np.float64)
+    ok = np.isfinite(vals)
+    return bits[ok], vals[ok]
+
+
+_BITS, _VALS = _all_finite_bf16()
+_ORDER = np.argsort(_VALS, kind="stable")
+
+
+def _nearest_bf16_brute(v: float) -> int:
+    """Exhaustive nearest-even search with exact rational distances."""
+    vals, bits = _VALS[_ORDER], _BITS[_ORDER]
+    maxv = float(vals.max())
+    half_ulp_top = Fraction(2) ** 119  # spacing at the top binade is 2^120
+    if Fraction(v) >= Fraction(maxv) + half_ulp_top:
+        return 0x7F80
+    if Fraction(v) <= -(Fraction(maxv) + half_ulp_top):
+        return 0xFF80
+    pos = np.searchsorted(vals, v)
+    cands = set()
+    for p in range(max(0, pos - 3), min(len(vals), pos + 3)):
+        cands.add(p)
+    best = None
+    for p in cands:
+        d = abs(Fraction(float(vals[p])) - Fraction(v))
+        key = (d, int(bits[p]) & 1)  # ties: even significand wins
+        if best is None or key < best[0]:
+            best = (key, int(bits[p]), float(vals[p]))
+    b = best[1]
+    if best[2] == 0.0:  # zero keeps the sign of v
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0x0000
+    return b
+
+
+def test_round_bf16_brute_force():
+    rng = np.random.default_rng(9)
+    xs = list(rng.standard_normal(300) * 10.0 ** rng.integers(-40, 38, 300))
+    # exact ties between neighbours, both parities, and values a hair off a tie
+    for base in (1.0, 1.0078125, 3.0, 1e-30, 2.0 ** -130):
+        f = Fraction(base)
+        b16 = wl.f32_to_bf16_bits(np.array([base], np.float32))[0]
+        lo = float(wl.bf16_bits_to_f32(np.array([b16], np.uint16))[0])
+        nxt = float(wl.bf16_bits_to_f32(np.array([b16 + 1], np.uint16))[0])
+        mid = (Fraction(lo) + Fraction(nxt)) / 2
+        xs += [float(mid), math.nextafter(float(mid), math.inf), math.nextafter(float(mid), -math.inf),
+               -float(mid)]
+        del f
+    xs += [0.0, -0.0, 2.0 ** -140, -(2.0 ** -140), 2.0 ** -149, 3.3e38, 3.39e38, 3.4e38, -3.4e38,
+           2.0 ** 128 - 2.0 ** 119, math.nextafter(2.0 ** 128 - 2.0 ** 119, 0.0)]
+    got = oracle.round_bf16(np.array(xs))
+    for x, g in zip(xs, got):
+        assert int(g) == _nearest_bf16_brute(x), (x, hex(int(g)))
+
+
+def test_round_f32_is_nearest():
+    rng = np.random.default_rng(10)
+    xs = rng.standard_normal(1000) * 1e3
+    got = oracle.round_f32(xs)
+    for x, g in zip(xs, got):
+        g = float(g)
+        up = float(np.nextafter(np.float32(g), np.float32(np.inf)))
+        dn = float(np.nextafter(np.float32(g), np.float32(-np.inf)))
+        d = abs(Fraction(g) - Fraction(float(x)))
+        assert d <= abs(Fraction(up) - Fraction(float(x)))
+        assert d <= abs(Fraction(dn) - Fraction(float(x)))
+
+
+# ---------------------------------------------------------------------------------------
+# grouped gemm
+# ---------------------------------------------------------------------------------------
+def _offsets(counts):
+    off = np.zeros(len(counts) + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    return off
+
+
+@pytest.mark.parametrize("layout", [B_KN, B_NK])
+def test_grouped_scaled_identity_pins_group_of_each_row(layout):
+    """W_g = (g+1) I: row r must come back as (g(r)+1) X[r], exactly, empty groups included."""
+    counts = np.array([3, 0, 5, 1, 0, 0, 7, 2])
+    G, K = len(counts), 32
+    M = int(counts.sum())
+    rng = np.random.default_rng(12)
+    X = int_bf16(rng, (M, K))
+    W = np.stack([wl.f32_to_bf16_bits((g + 1) * np.eye(K, dtype=np.float32)) for g in range(G)])
+    if layout == B_NK:
+        W = np.ascontiguousarray(W.transpose(0, 2, 1))
+    got = oracle.grouped_gemm(X, W, layout, _offsets(counts))
+    grp = np.repeat(np.arange(G), counts)
+    assert np.array_equal(got, (grp[:, None] + 1) * dec(X))
+
+
+@pytest.mark.parametrize("layout", [B_KN, B_NK])
+def test_grouped_equals_concatenated_per_group(layout):
+    w = wl.grouped(21, 6, 150, 40, 24, w_layout=layout, with_bias=True, epi=EPI_BIAS_SILU,
+                   counts=np.array([10, 0, 90, 1, 49, 0]))
+    got = oracle.grouped_gemm(w.X, w.W, layout, w.offsets, w.bias, EPI_BIAS_SILU)
+    parts = []
+    for g in range(w.G):
+        lo, hi = w.offsets[g], w.offsets[g + 1]
+        Wg = dec(w.W[g]) if layout == B_KN else dec(w.W[g]).T
+        acc = dec(w.X[lo:hi]) @ Wg + w.bias[g].astype(np.float64)
+        parts.append(acc * scipy.special.expit(acc))
+    ref = np.concatenate(parts)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    # and against the oracle's own plain gemm, group by group, exactly
+    for g in range(w.G):
+        lo, hi = w.offsets[g], w.offsets[g + 1]
+        if hi > lo:
+            one = oracle.gemm(w.X[lo:hi], w.W[g], layout, w.bias[g], EPI_BIAS_SILU)
+            assert np.array_equal(got[lo:hi], one)
+
+
+def test_grouped_single_group_is_dense():
+    rng = np.random.default_rng(13)
+    X = rand_bf16(rng, (33, 24))
+    W = rand_bf16(rng, (1, 24, 16))
+    assert np.array_equal(oracle.grouped_gemm(X, W, B_KN, [0, 33]), oracle.gemm(X, W[0], B_KN))
+
+
+def test_grouped_rejects_bad_offsets():
+    X = np.zeros((4, 8), np.uint16)
+    W = np.zeros((2, 8, 8), np.uint16)
+    for off in ([1, 2, 4], [0, 3, 2], [0, 2, 5], [0, 5, 4]):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.grouped_gemm(X, W, B_KN, off)
+        assert e.value.code == 2
+
+
+# ---------------------------------------------------------------------------------------
+# broadcast gemm
+# ---------------------------------------------------------------------------------------
+def test_broadcast_block_identities():
+    """W = [I; 0] returns the gathered user rows; W = [0; I] returns the candidate rows."""
+    rng = np.random.default_rng(14)
+    U, Ku, Kc, Mc = 5, 16, 16, 23
+    Xu = rand_bf16(rng, (U, Ku))
+    Xc = rand_bf16(rng, (Mc, Kc))
+    idx = rng.integers(0, U, Mc).astype(np.int32)
+    top = np.concatenate([np.eye(Ku), np.zeros((Kc, Ku))]).astype(np.float32)
+    bot = np.concatenate([np.zeros((Ku, Kc)), np.eye(Kc)]).astype(np.float32)
+    for W, want in ((top, dec(Xu)[idx]), (bot, dec(Xc))):
+        Wb = wl.f32_to_bf16_bits(W)
+        assert np.array_equal(oracle.broadcast_gemm(Xu, Xc, idx, Wb, B_KN), want)
+        assert np.array_equal(oracle.broadcast_gemm(Xu, Xc, idx, np.ascontiguousarray(Wb.T), B_NK), want)
+
+
+@pytest.mark.parametrize("layout", [B_KN, B_NK])
+def test_broadcast_equals_materialised_gemm(layout):
+    w = wl.broadcast(15, 4, 48, 24, 40, cmin=3, cmax=20, w_layout=layout, with_bias=True,
+                     epi=EPI_BIAS, shuffle=True)
+    got = oracle.broadcast_gemm(w.Xu, w.Xc, w.idx, w.W, layout, w.bias, EPI_BIAS)
+    Z = np.concatenate([dec(w.Xu)[w.idx], dec(w.Xc)], axis=1)
+    Wd = dec(w.W) if layout == B_KN else dec(w.W).T
+    ref = Z @ Wd + w.bias.astype(np.float64)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    # the same materialised input through the oracle's plain gemm agrees exactly
+    Zb = np.concatenate([w.Xu[w.idx], w.Xc], axis=1)
+    assert np.array_equal(got, oracle.gemm(Zb, w.W, layout, w.bias, EPI_BIAS))
+
+
+def test_broadcast_row_permutation():
+    w = wl.broadcast(16, 3, 16, 8, 24, cmin=2, cmax=9)
+    base = oracle.broadcast_gemm(w.Xu, w.Xc, w.idx, w.W, B_KN)
+    perm = np.random.default_rng(1).permutation(w.Mc)
+    got = oracle.broadcast_gemm(w.Xu, w.Xc[perm], w.idx[perm], w.W, B_KN)
+    assert np.array_equal(got, base[perm])
+
+
+def test_broadcast_rejects_bad_index():
+    Xu = np.zeros((2, 8), np.uint16)
+    Xc = np.zeros((3, 8), np.uint16)
+    W = np.zeros((16, 8), np.uint16)
+    for idx in ([0, 1, 2], [0, -1, 1]):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.broadcast_gemm(Xu, Xc, idx, W, B_KN)
+        assert e.value.code == 3
