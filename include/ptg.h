@@ -1,0 +1,183 @@
+/*
+ * ptg.h - C ABI of the pipelined tiled GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the tiled matrix product of the standard Triton matmul in
+ * "How We Built TLX: A Hardware-Native GPU Compiler for Production ML at Scale"
+ * (section "Introducing TLX", listing 1: C = A.B with an fp32 accumulator), organised as
+ * the producer / consumer / epilogue pipeline of listing 2 of the same section, and two
+ * production forms of it from that page: the grouped GEMM of mixture-of-experts layers
+ * (section "Case Study 3: Distributed Grouped GEMM for LLM Pretraining") and the
+ * in-kernel broadcast linear compression (section "Case Study 2: In-Kernel Broadcast
+ * Optimization for RecSys", subsection "TLX Provides a Building Block for the Final Stage
+ * of This Optimization").
+ *
+ * Conventions shared by every call
+ *   - Element types: every A, B, X, W operand is bfloat16 (raw 16-bit storage).  Outputs
+ *     are float32 or bfloat16 (round to nearest, ties to even).  Products accumulate in
+ *     float32.  Bias vectors are float32.
+ *   - Layouts: matrices are row-major with a leading dimension (elements between rows).
+ *     The second operand is either "KN" (K x N row-major, the plain B of C = A.B) or "NK"
+ *     (N x K row-major, i.e. B transposed).
+ *   - Memory: every matrix/vector pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains it past the call's completion on the stream.
+ *     Host pointers are only the ptg_problem arrays, read during the call.  Scratch memory
+ *     is supplied by the caller (see the *_workspace queries).
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *     call only enqueues work and returns; results are ready when the stream reaches them.
+ *   - Alignment: device pointers must be 16-byte aligned, K and N multiples of 8 and
+ *     leading dimensions multiples of 8 elements (16 bytes), else PTG_ERR_UNSUPPORTED.
+ *   - Sizes: M = 0 or N = 0 is a valid no-op.  K = 0 is rejected (PTG_ERR_UNSUPPORTED).
+ *   - Errors are returned, never thrown; ptg_last_error() holds a thread-local message for
+ *     the last failing call on the calling thread.  Preconditions on device-resident data
+ *     (group offsets, user indices) are not read by the host; violating them is undefined
+ *     unless checked with the *_check helpers below.
+ *   - Calls are reentrant; the library keeps no state between calls apart from the per-
+ *     thread error text and a per-device cache of device properties.
+ */
+#ifndef PTG_H_
+#define PTG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PTG_OK = 0,
+    PTG_ERR_INVALID_ARG = 1,   /* null pointer with nonzero extent, negative size, ld too small */
+    PTG_ERR_UNSUPPORTED = 2,   /* alignment, K or N not a multiple of 8, size limits, bad enum */
+    PTG_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace query */
+    PTG_ERR_HIP = 4,           /* a HIP runtime call failed (launch error, bad stream, no device) */
+    PTG_ERR_DEVICE_CHECK = 5   /* a *_check helper found invalid device-resident data */
+} ptg_status;
+
+typedef enum { PTG_BF16 = 0, PTG_F32 = 1 } ptg_dtype;               /* output element type */
+typedef enum { PTG_B_KN = 0, PTG_B_NK = 1 } ptg_layout;             /* second-operand layout */
+typedef enum {
+    PTG_EPI_NONE = 0,       /* out = acc */
+    PTG_EPI_BIAS = 1,       /* out = acc + bias[n] */
+    PTG_EPI_SILU = 2,       /* out = silu(acc),         silu(v) = v / (1 + exp(-v)) */
+    PTG_EPI_BIAS_SILU = 3   /* out = silu(acc + bias[n]) */
+} ptg_epilogue;
+
+/*
+ * ptg_gemm - C = epi(A.B + bias), one pipelined persistent launch.
+ * The operation of listing 1 ("Introducing TLX": acc = 0; for each K block acc += A.B;
+ * store), with the epilogue stage of listing 2 extended by a fused bias and SiLU.
+ *   M, N, K   problem size (M, N >= 0; K > 0; N, K multiples of 8)
+ *   A         bf16 [M x K], row stride lda >= K
+ *   B         bf16, [K x N] with row stride ldb >= N (PTG_B_KN) or [N x K] with ldb >= K (PTG_B_NK)
+ *   C         [M x N] of c_dtype, row stride ldc >= N; fully overwritten, never read
+ *   bias      float32 [N], required by the BIAS epilogues, ignored otherwise (may be NULL)
+ */
+ptg_status ptg_gemm(int64_t M, int64_t N, int64_t K,
+                    const void* A, int64_t lda,
+                    const void* B, int64_t ldb, ptg_layout b_layout,
+                    void* C, int64_t ldc, ptg_dtype c_dtype,
+                    const float* bias, ptg_epilogue epi, void* stream);
+
+/*
+ * ptg_grouped_gemm - mixture-of-experts grouped GEMM ("Case Study 3: Distributed Grouped GEMM
+ * for LLM Pretraining": the grouped matrix products of the experts).  Rows of X and Y are
+ * sorted by expert; expert g owns rows [offsets[g], offsets[g+1]) and multiplies W_g:
+ *   Y[r] = epi(X[r] . W_g + bias[g])
+ *   G             number of experts, 1 <= G <= 1024
+ *   M_total, N, K X is bf16 [M_total x K] dense (ld = K); Y is [M_total x N] dense (ld = N)
+ *   W             bf16, G matrices back to back: [G x K x N] (PTG_B_KN) or [G x N x K] (PTG_B_NK)
+ *   group_offsets DEVICE int32 [G + 1]: offsets[0] = 0, nondecreasing, offsets[G] = M_total.
+ *                 Empty groups are allowed.  Read only on the device (no host sync).
+ *   bias          float32 [G x N] for the BIAS epilogues, else ignored
+ * Rows of Y that belong to no group cannot exist under the precondition; every row is written.
+ */
+ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K,
+                            const void* X, const void* W, ptg_layout w_layout,
+                            const int32_t* group_offsets,
+                            void* Y, ptg_dtype y_dtype,
+                            const float* bias, ptg_epilogue epi, void* stream);
+
+/* ptg_grouped_gemm_check - validates group_offsets on the device (0 at both ends as stated,
+ * nondecreasing), synchronises `stream`, and returns PTG_OK or PTG_ERR_DEVICE_CHECK. */
+ptg_status ptg_grouped_gemm_check(int32_t G, int64_t M_total, const int32_t* group_offsets,
+                                  void* stream);
+
+/*
+ * Batch of independent GEMMs in one persistent launch (the pointer-array form of the grouped
+ * GEMM): problem p computes C_p = epi(A_p . B_p + bias_p) with B_p stored K x N (KN).
+ * Short problems keep the pipeline full across problem boundaries ("Case Study 2", final
+ * stage: stages share circular buffers without draining the pipeline).
+ *   ptg_gemm_batch_workspace(count) - bytes of device workspace needed for `count` problems.
+ *   ptg_gemm_batch_prepare - validates the host array `problems` (count >= 1), writes the
+ *       problem table and its tile prefix into `workspace` (device) and synchronises `stream`
+ *       so that `problems` may be freed on return.  Rewrite it whenever a pointer or shape
+ *       changes.
+ *   ptg_gemm_batch_run - launches the batch recorded in `workspace` (no host work, no sync).
+ *   ptg_gemm_batch - prepare followed by run.
+ */
+typedef struct {
+    int64_t M, N, K;          /* M >= 0, N and K multiples of 8, K > 0 */
+    const void* A;            /* bf16 [M x K], row stride lda */
+    const void* B;            /* bf16 [K x N], row stride ldb (KN layout) */
+    void* C;                  /* [M x N] of the batch's c_dtype, row stride ldc */
+    const float* bias;        /* float32 [N] (BIAS epilogues) or NULL */
+    int64_t lda, ldb, ldc;
+} ptg_problem;
+
+size_t ptg_gemm_batch_workspace(int32_t count);
+ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, ptg_epilogue epi,
+                                  void* workspace, size_t ws_bytes, void* stream);
+ptg_status ptg_gemm_batch_run(int32_t count, const void* workspace, size_t ws_bytes,
+                              ptg_dtype c_dtype, ptg_epilogue epi, void* stream);
+ptg_status ptg_gemm_batch(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype,
+                          ptg_epilogue epi, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * ptg_broadcast_gemm - in-kernel broadcast linear compression ("Case Study 2: In-Kernel
+ * Broadcast Optimization for RecSys"): user features are consumed at their natural batch
+ * size U, candidate features at Mc, and the broadcast happens inside the computation:
+ *   Y[r] = epi([Xu[user_idx[r]] | Xc[r]] . W + bias)
+ * computed by matmul decomposition: P = Xu . W[0:Ku] once per user (fp32, in `workspace`),
+ * then Y = epi(Xc . W[Ku:Ku+Kc] + P[user_idx] + bias); Xu[user_idx] is never materialised.
+ *   U, Mc         users and candidates (U >= 1, Mc >= 0)
+ *   Ku, Kc, N     user width, candidate width, output width (multiples of 8; Ku, Kc > 0)
+ *   Xu            bf16 [U x Ku] dense;  Xc bf16 [Mc x Kc] dense
+ *   user_idx      DEVICE int32 [Mc], each in [0, U); any order
+ *   W             bf16 [(Ku + Kc) x N] (PTG_B_KN, rows 0..Ku-1 meet the user features) or
+ *                 [N x (Ku + Kc)] (PTG_B_NK, columns 0..Ku-1 meet the user features)
+ *   Y             [Mc x N] of y_dtype, dense
+ *   bias          float32 [N] for the BIAS epilogues
+ *   workspace     DEVICE scratch of at least ptg_broadcast_gemm_workspace(U, N) bytes
+ */
+size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N);
+ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N,
+                              const void* Xu, const void* Xc, const int32_t* user_idx,
+                              const void* W, ptg_layout w_layout,
+                              void* Y, ptg_dtype y_dtype,
+                              const float* bias, ptg_epilogue epi,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ptg_broadcast_gemm_check - validates 0 <= user_idx[r] < U on the device, synchronises
+ * `stream`, returns PTG_OK or PTG_ERR_DEVICE_CHECK. */
+ptg_status ptg_broadcast_gemm_check(int64_t U, int64_t Mc, const int32_t* user_idx, void* stream);
+
+/* Text of a status code (static storage), and the calling thread's last error detail. */
+const char* ptg_status_string(ptg_status s);
+const char* ptg_last_error(void);
+
+/* ptg_watchdog - every wait of the pipeline is bounded; a wait that gives up (which a correct
+ * launch never does) sets a per-device word instead of hanging.  Reads that word of the
+ * current device into *value and clears it when `clear` is nonzero.  Synchronous. */
+ptg_status ptg_watchdog(uint32_t* value, int32_t clear);
+
+/* Library version, and the tile configuration the dense path would pick for (M, N, K):
+ * writes BM, BN, BK, stages, consumer waves, producer waves into cfg[0..5].  For tests and
+ * logging; returns PTG_ERR_INVALID_ARG for a NULL cfg. */
+int32_t ptg_version(void);
+ptg_status ptg_describe_config(int64_t M, int64_t N, int64_t K, ptg_layout b_layout, int32_t cfg[6]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTG_H_ */

@@ -1,0 +1,264 @@
+"""Pipelined tiled GEMM for AMD Instinct MI355X (gfx950): Python binding of libptg.so.
+
+Each function has the name of a C ABI entry point (include/ptg.h) without the ``ptg_``
+prefix and only marshals arguments: tensors become device pointers, torch's current HIP
+stream becomes the ``stream`` argument, and a non-OK status raises :class:`PtgError`.
+All work runs in the library's kernels; there is no fallback path, and a missing
+libptg.so raises ImportError at the first call.
+
+PyTorch provides device memory and streams only.  bfloat16 tensors carry the bf16
+operands; outputs are float32 or bfloat16 tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _ffi
+
+__all__ = [
+    "PtgError", "B_KN", "B_NK", "EPI_NONE", "EPI_BIAS", "EPI_SILU", "EPI_BIAS_SILU",
+    "gemm", "grouped_gemm", "grouped_gemm_check", "gemm_batch_workspace", "gemm_batch_prepare",
+    "gemm_batch_run", "gemm_batch", "broadcast_gemm_workspace", "broadcast_gemm",
+    "broadcast_gemm_check", "watchdog", "version", "describe_config", "status_string",
+    "last_error", "library_path",
+]
+
+B_KN, B_NK = 0, 1
+EPI_NONE, EPI_BIAS, EPI_SILU, EPI_BIAS_SILU = 0, 1, 2, 3
+_BF16, _F32 = 0, 1
+
+
+class PtgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_ffi.STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _lib():
+    return _ffi.load()
+
+
+def library_path() -> str:
+    return _ffi.LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return _lib().ptg_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _lib().ptg_last_error().decode()
+
+
+def version() -> int:
+    return int(_lib().ptg_version())
+
+
+def _check(status: int) -> None:
+    if status != _ffi.PTG_OK:
+        raise PtgError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return _BF16
+    if dtype == torch.float32:
+        return _F32
+    raise ValueError(f"output dtype must be bfloat16 or float32, not {dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dims: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got {t.dim()}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _rowmajor_ld(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a row-major matrix view (unit stride along the last axis)."""
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name} must be row-major (unit stride in the last dimension)")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def describe_config(M: int, N: int, K: int, b_layout: int = B_KN):
+    cfg = (ctypes.c_int32 * 6)()
+    _check(_lib().ptg_describe_config(M, N, K, b_layout, cfg))
+    return dict(zip(("BM", "BN", "BK", "stages", "consumers", "producers"), list(cfg)))
+
+
+def watchdog(clear: bool = True) -> int:
+    v = ctypes.c_uint32(0)
+    _check(_lib().ptg_watchdog(ctypes.byref(v), 1 if clear else 0))
+    return int(v.value)
+
+
+# ------------------------------------------------------------------------------------------
+def gemm(A: torch.Tensor, B: torch.Tensor, *, b_layout: int = B_KN, out: Optional[torch.Tensor] = None,
+         out_dtype: torch.dtype = torch.bfloat16, bias: Optional[torch.Tensor] = None,
+         epi: int = EPI_NONE, stream=None) -> torch.Tensor:
+    """C = epi(A.B + bias).  A [M, K] bf16; B [K, N] (B_KN) or [N, K] (B_NK) bf16."""
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    M, K = A.shape
+    N = B.shape[1] if b_layout == B_KN else B.shape[0]
+    kb = B.shape[0] if b_layout == B_KN else B.shape[1]
+    if kb != K:
+        raise ValueError(f"inner dimensions differ: A has K={K}, B has {kb}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    _need(out, "out", out.dtype, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}]")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1)
+    _check(_lib().ptg_gemm(M, N, K, _ptr(A), _rowmajor_ld(A, "A"), _ptr(B), _rowmajor_ld(B, "B"),
+                           b_layout, _ptr(out), _rowmajor_ld(out, "out"), _dtype_code(out.dtype),
+                           _ptr(bias), epi, _stream(stream)))
+    return out
+
+
+def grouped_gemm(X: torch.Tensor, W: torch.Tensor, group_offsets: torch.Tensor, *,
+                 w_layout: int = B_KN, out: Optional[torch.Tensor] = None,
+                 out_dtype: torch.dtype = torch.bfloat16, bias: Optional[torch.Tensor] = None,
+                 epi: int = EPI_NONE, stream=None) -> torch.Tensor:
+    """Y[r] = epi(X[r].W[g] + bias[g]) for offsets[g] <= r < offsets[g+1] (offsets on device)."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 3)
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    M, K = X.shape
+    G = W.shape[0]
+    N = W.shape[2] if w_layout == B_KN else W.shape[1]
+    if group_offsets.shape[0] != G + 1:
+        raise ValueError("group_offsets must have G + 1 entries")
+    if not (X.is_contiguous() and W.is_contiguous() and group_offsets.is_contiguous()):
+        raise ValueError("X, W and group_offsets must be contiguous")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    if not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be a contiguous [{M}, {N}] tensor")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 2)
+    _check(_lib().ptg_grouped_gemm(G, M, N, K, _ptr(X), _ptr(W), w_layout, _ptr(group_offsets),
+                                   _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi, _stream(stream)))
+    return out
+
+
+def grouped_gemm_check(group_offsets: torch.Tensor, M_total: int, stream=None) -> None:
+    """Raises PtgError (PTG_ERR_DEVICE_CHECK) when the device offsets break the precondition."""
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    _check(_lib().ptg_grouped_gemm_check(group_offsets.shape[0] - 1, M_total, _ptr(group_offsets),
+                                         _stream(stream)))
+
+
+def gemm_batch_workspace(count: int) -> int:
+    return int(_lib().ptg_gemm_batch_workspace(count))
+
+
+def _problem_array(problems: Sequence):
+    arr = (_ffi.ProblemStruct * len(problems))()
+    for i, pr in enumerate(problems):
+        A, B, C = pr[0], pr[1], pr[2]
+        bias = pr[3] if len(pr) > 3 else None
+        _need(A, f"A[{i}]", torch.bfloat16, 2)
+        _need(B, f"B[{i}]", torch.bfloat16, 2)
+        if C.dim() != 2 or C.device.type != "cuda":
+            raise ValueError(f"C[{i}] must be a 2-D GPU tensor")
+        M, K = A.shape
+        if B.shape[0] != K or tuple(C.shape) != (M, B.shape[1]):
+            raise ValueError(f"problem {i}: shapes do not match")
+        s = arr[i]
+        s.M, s.N, s.K = M, B.shape[1], K
+        s.A, s.B, s.C, s.bias = _ptr(A), _ptr(B), _ptr(C), _ptr(bias)
+        s.lda, s.ldb, s.ldc = _rowmajor_ld(A, "A"), _rowmajor_ld(B, "B"), _rowmajor_ld(C, "C")
+    return arr
+
+
+def gemm_batch_prepare(problems: Sequence, epi: int, workspace: torch.Tensor, stream=None) -> None:
+    """Record problems [(A, B, C[, bias]), ...] (B stored K x N) in a device workspace."""
+    arr = _problem_array(problems)
+    _check(_lib().ptg_gemm_batch_prepare(len(problems), arr, epi, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def gemm_batch_run(count: int, workspace: torch.Tensor, out_dtype: torch.dtype, epi: int,
+                   stream=None) -> None:
+    _check(_lib().ptg_gemm_batch_run(count, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _dtype_code(out_dtype), epi, _stream(stream)))
+
+
+def gemm_batch(problems: Sequence, epi: int, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Prepare and run a batch in one call; returns the workspace used."""
+    if workspace is None:
+        dev = problems[0][0].device
+        workspace = torch.empty(gemm_batch_workspace(len(problems)), dtype=torch.uint8, device=dev)
+    arr = _problem_array(problems)
+    out_dtype = problems[0][2].dtype
+    _check(_lib().ptg_gemm_batch(len(problems), arr, _dtype_code(out_dtype), epi, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return workspace
+
+
+def broadcast_gemm_workspace(U: int, N: int) -> int:
+    return int(_lib().ptg_broadcast_gemm_workspace(U, N))
+
+
+def broadcast_gemm(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W: torch.Tensor, *,
+                   w_layout: int = B_KN, out: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.bfloat16, bias: Optional[torch.Tensor] = None,
+                   epi: int = EPI_NONE, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Y[r] = epi([Xu[user_idx[r]] | Xc[r]].W + bias) without materialising Xu[user_idx]."""
+    _need(Xu, "Xu", torch.bfloat16, 2)
+    _need(Xc, "Xc", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    _need(user_idx, "user_idx", torch.int32, 1)
+    U, Ku = Xu.shape
+    Mc, Kc = Xc.shape
+    N = W.shape[1] if w_layout == B_KN else W.shape[0]
+    kw = W.shape[0] if w_layout == B_KN else W.shape[1]
+    if kw != Ku + Kc:
+        raise ValueError(f"W must have Ku + Kc = {Ku + Kc} rows of reduction, has {kw}")
+    if user_idx.shape[0] != Mc:
+        raise ValueError("user_idx must have one entry per candidate row")
+    for t, name in ((Xu, "Xu"), (Xc, "Xc"), (W, "W"), (user_idx, "user_idx")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is None:
+        out = torch.empty((Mc, N), dtype=out_dtype, device=Xc.device)
+    if not out.is_contiguous() or tuple(out.shape) != (Mc, N):
+        raise ValueError(f"out must be a contiguous [{Mc}, {N}] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(broadcast_gemm_workspace(U, N), 16), dtype=torch.uint8,
+                                device=Xc.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1)
+    _check(_lib().ptg_broadcast_gemm(U, Mc, Ku, Kc, N, _ptr(Xu), _ptr(Xc), _ptr(user_idx), _ptr(W),
+                                     w_layout, _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+    return out
+
+
+def broadcast_gemm_check(U: int, user_idx: torch.Tensor, stream=None) -> None:
+    """Raises PtgError (PTG_ERR_DEVICE_CHECK) when an index is outside [0, U)."""
+    _need(user_idx, "user_idx", torch.int32, 1)
+    _check(_lib().ptg_broadcast_gemm_check(U, user_idx.shape[0], _ptr(user_idx), _stream(stream)))

@@ -1,0 +1,350 @@
+// ptg_api.cpp - the C ABI: argument validation, error reporting and dispatch to the
+// pipelined kernels.  Nothing here touches the GPU before every host-checkable
+// precondition has passed, so invalid calls fail the same way with or without a device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <vector>
+
+#include "../../include/ptg.h"
+#include "ptg_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ptg_status fail(ptg_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ptg_status hip_fail(hipError_t e, const char* what) {
+  return fail(PTG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bad_dim(int64_t x) { return x < 0; }
+
+#define PTG_TRY(body)                                                  \
+  try {                                                                \
+    body                                                               \
+  } catch (const std::exception& ex) {                                 \
+    return fail(PTG_ERR_HIP, "internal error: %s", ex.what());         \
+  } catch (...) {                                                      \
+    return fail(PTG_ERR_HIP, "internal error");                        \
+  }
+
+bool valid_epi(int e) { return e >= PTG_EPI_NONE && e <= PTG_EPI_BIAS_SILU; }
+bool needs_bias(int e) { return e == PTG_EPI_BIAS || e == PTG_EPI_BIAS_SILU; }
+
+// Checks shared by every operand pair: sizes, multiples of 8, alignment, 31-bit offsets.
+ptg_status check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K))
+    return fail(PTG_ERR_INVALID_ARG, "%s: negative size (M=%lld N=%lld K=%lld)", fn, (long long)M,
+                (long long)N, (long long)K);
+  if (K == 0) return fail(PTG_ERR_UNSUPPORTED, "%s: K = 0 is not supported", fn);
+  if (K % 8 || N % 8)
+    return fail(PTG_ERR_UNSUPPORTED, "%s: N and K must be multiples of 8 (N=%lld K=%lld)", fn,
+                (long long)N, (long long)K);
+  if (M > ptg::kMaxDim || N > ptg::kMaxDim || K > ptg::kMaxDim)
+    return fail(PTG_ERR_UNSUPPORTED, "%s: a dimension exceeds 2^30", fn);
+  return PTG_OK;
+}
+
+// The kernels address one tile of each operand with 31-bit byte offsets.
+bool fits31(int64_t rows, int64_t ld, int64_t cols) {
+  const int64_t bytes = ((rows > 0 ? rows - 1 : 0) * ld + cols) * 2;
+  return bytes < ((int64_t)1 << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ptg_status_string(ptg_status s) {
+  switch (s) {
+    case PTG_OK: return "PTG_OK";
+    case PTG_ERR_INVALID_ARG: return "PTG_ERR_INVALID_ARG";
+    case PTG_ERR_UNSUPPORTED: return "PTG_ERR_UNSUPPORTED";
+    case PTG_ERR_WORKSPACE: return "PTG_ERR_WORKSPACE";
+    case PTG_ERR_HIP: return "PTG_ERR_HIP";
+    case PTG_ERR_DEVICE_CHECK: return "PTG_ERR_DEVICE_CHECK";
+  }
+  return "PTG_ERR_UNKNOWN";
+}
+
+const char* ptg_last_error(void) { return g_err; }
+
+int32_t ptg_version(void) { return 1; }
+
+ptg_status ptg_describe_config(int64_t M, int64_t N, int64_t K, ptg_layout b_layout, int32_t cfg[6]) {
+  if (!cfg) return fail(PTG_ERR_INVALID_ARG, "ptg_describe_config: cfg is NULL");
+  ptg::dense_config(M, N, K, b_layout == PTG_B_KN, cfg);
+  return PTG_OK;
+}
+
+ptg_status ptg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, ptg_layout b_layout, void* C, int64_t ldc, ptg_dtype c_dtype,
+                    const float* bias, ptg_epilogue epi, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_gemm";
+    ptg_status st = check_mnk(fn, M, N, K);
+    if (st) return st;
+    if (b_layout != PTG_B_KN && b_layout != PTG_B_NK) return fail(PTG_ERR_UNSUPPORTED, "%s: bad layout", fn);
+    if (c_dtype != PTG_BF16 && c_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
+    if (!valid_epi(epi)) return fail(PTG_ERR_UNSUPPORTED, "%s: bad epilogue", fn);
+    if (M == 0 || N == 0) return PTG_OK;
+    if (!A || !B || !C) return fail(PTG_ERR_INVALID_ARG, "%s: null operand", fn);
+    if (needs_bias(epi) && !bias) return fail(PTG_ERR_INVALID_ARG, "%s: epilogue needs a bias", fn);
+    const int64_t b_row = b_layout == PTG_B_KN ? N : K;
+    if (lda < K || ldb < b_row || ldc < N) return fail(PTG_ERR_INVALID_ARG, "%s: leading dimension too small", fn);
+    if (lda % 8 || ldb % 8 || (c_dtype == PTG_BF16 ? ldc % 8 : ldc % 4))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: leading dimensions must be multiples of 16 bytes", fn);
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (bias && !aligned16(bias)))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned", fn);
+    const bool kn = b_layout == PTG_B_KN;
+    if (!fits31(256, lda, K) || !(kn ? fits31(K, ldb, 256) : fits31(256, ldb, K)) || !fits31(512, ldc, 2 * N))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand tile exceeds 2 GiB of addressing", fn);
+    ptg::DenseLaunch d{};
+    d.A = A; d.B = B; d.C = C; d.bias = needs_bias(epi) ? bias : nullptr;
+    d.lda = lda; d.ldb = ldb; d.ldc = ldc;
+    d.M = M; d.N = N; d.K = K;
+    d.b_kn = kn; d.epi = epi; d.out_f32 = c_dtype == PTG_F32;
+    hipError_t e = ptg::launch_dense(d, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PTG_OK;
+  })
+}
+
+ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, const void* X,
+                            const void* W, ptg_layout w_layout, const int32_t* group_offsets,
+                            void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                            void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_grouped_gemm";
+    if (G <= 0) return fail(PTG_ERR_INVALID_ARG, "%s: G must be positive", fn);
+    if (G > ptg::kMaxGroups) return fail(PTG_ERR_UNSUPPORTED, "%s: G exceeds %d", fn, ptg::kMaxGroups);
+    ptg_status st = check_mnk(fn, M_total, N, K);
+    if (st) return st;
+    if (w_layout != PTG_B_KN && w_layout != PTG_B_NK) return fail(PTG_ERR_UNSUPPORTED, "%s: bad layout", fn);
+    if (y_dtype != PTG_BF16 && y_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
+    if (!valid_epi(epi)) return fail(PTG_ERR_UNSUPPORTED, "%s: bad epilogue", fn);
+    if (M_total == 0 || N == 0) return PTG_OK;
+    if (!X || !W || !Y || !group_offsets) return fail(PTG_ERR_INVALID_ARG, "%s: null operand", fn);
+    if (needs_bias(epi) && !bias) return fail(PTG_ERR_INVALID_ARG, "%s: epilogue needs a bias", fn);
+    if (M_total >= ((int64_t)1 << 31)) return fail(PTG_ERR_UNSUPPORTED, "%s: M_total must fit int32 offsets", fn);
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || (bias && !aligned16(bias)) ||
+        (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (offsets 4-byte)", fn);
+    const bool kn = w_layout == PTG_B_KN;
+    if (!fits31(256, K, K) || !(kn ? fits31(K, N, 256) : fits31(256, K, K)))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand tile exceeds 2 GiB of addressing", fn);
+    ptg::GroupedLaunch g{};
+    g.X = X; g.W = W; g.Y = Y; g.bias = needs_bias(epi) ? bias : nullptr; g.offsets = group_offsets;
+    g.M_total = M_total; g.N = N; g.K = K; g.G = G;
+    g.b_kn = kn; g.epi = epi; g.out_f32 = y_dtype == PTG_F32;
+    hipError_t e = ptg::launch_grouped(g, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PTG_OK;
+  })
+}
+
+ptg_status ptg_grouped_gemm_check(int32_t G, int64_t M_total, const int32_t* group_offsets, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_grouped_gemm_check";
+    if (G <= 0 || M_total < 0 || !group_offsets) return fail(PTG_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    int bad = 0;
+    hipError_t e = ptg::check_offsets(group_offsets, G, M_total, reinterpret_cast<hipStream_t>(stream), &bad);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (bad) return fail(PTG_ERR_DEVICE_CHECK, "%s: group offsets violate the precondition", fn);
+    return PTG_OK;
+  })
+}
+
+ptg_status ptg_broadcast_gemm_check(int64_t U, int64_t Mc, const int32_t* user_idx, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_broadcast_gemm_check";
+    if (U <= 0 || Mc < 0 || (Mc > 0 && !user_idx)) return fail(PTG_ERR_INVALID_ARG, "%s: bad arguments", fn);
+    if (Mc == 0) return PTG_OK;
+    int bad = 0;
+    hipError_t e = ptg::check_index(user_idx, Mc, U, reinterpret_cast<hipStream_t>(stream), &bad);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (bad) return fail(PTG_ERR_DEVICE_CHECK, "%s: a user index is outside [0, U)", fn);
+    return PTG_OK;
+  })
+}
+
+size_t ptg_gemm_batch_workspace(int32_t count) {
+  if (count <= 0) return 0;
+  return ptg::batch_workspace_bytes(count);
+}
+
+static ptg_status validate_problem(const char* fn, int32_t p, const ptg_problem& q, ptg_epilogue epi) {
+  if (q.M < 0 || q.N < 0 || q.K < 0) return fail(PTG_ERR_INVALID_ARG, "%s: problem %d: negative size", fn, p);
+  if (q.K == 0) return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: K = 0", fn, p);
+  if (q.K % 8 || q.N % 8) return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: N and K must be multiples of 8", fn, p);
+  if (q.M >= ((int64_t)1 << 30) || q.N >= ((int64_t)1 << 30) || q.K >= ((int64_t)1 << 30))
+    return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: dimension too large", fn, p);
+  if (q.M == 0 || q.N == 0) return PTG_OK;
+  if (!q.A || !q.B || !q.C) return fail(PTG_ERR_INVALID_ARG, "%s: problem %d: null operand", fn, p);
+  if (needs_bias(epi) && !q.bias) return fail(PTG_ERR_INVALID_ARG, "%s: problem %d: epilogue needs a bias", fn, p);
+  if (q.lda < q.K || q.ldb < q.N || q.ldc < q.N) return fail(PTG_ERR_INVALID_ARG, "%s: problem %d: leading dimension too small", fn, p);
+  if (q.lda % 8 || q.ldb % 8 || q.ldc % 8) return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: leading dimensions must be multiples of 8", fn, p);
+  if (!aligned16(q.A) || !aligned16(q.B) || !aligned16(q.C) || (q.bias && !aligned16(q.bias)))
+    return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: pointers must be 16-byte aligned", fn, p);
+  if (!fits31(256, q.lda, q.K) || !fits31(q.K, q.ldb, 256))
+    return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: operand tile exceeds 2 GiB of addressing", fn, p);
+  return PTG_OK;
+}
+
+ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, ptg_epilogue epi,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_gemm_batch_prepare";
+    if (count <= 0 || !problems) return fail(PTG_ERR_INVALID_ARG, "%s: count must be positive and problems non-null", fn);
+    if (count > ptg::kMaxBatch) return fail(PTG_ERR_UNSUPPORTED, "%s: count exceeds %d", fn, ptg::kMaxBatch);
+    if (!valid_epi(epi)) return fail(PTG_ERR_UNSUPPORTED, "%s: bad epilogue", fn);
+    const size_t need = ptg::batch_workspace_bytes(count);
+    if (!workspace || ws_bytes < need)
+      return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
+    std::vector<char> host(need, 0);
+    auto* hdr = reinterpret_cast<ptg::BatchHeader*>(host.data());
+    auto* pre = reinterpret_cast<int32_t*>(host.data() + sizeof(ptg::BatchHeader));
+    auto* rec = reinterpret_cast<ptg::BatchProblem*>(host.data() + sizeof(ptg::BatchHeader) +
+                                                     ptg::batch_prefix_bytes(count));
+    int64_t total = 0;
+    for (int32_t p = 0; p < count; ++p) {
+      const ptg_problem& q = problems[p];
+      ptg_status st = validate_problem(fn, p, q, epi);
+      if (st) return st;
+      ptg::BatchProblem& r = rec[p];
+      r.A = q.A; r.B = q.B; r.C = q.C; r.bias = needs_bias(epi) ? q.bias : nullptr;
+      r.lda = q.lda; r.ldb = q.ldb; r.ldc = q.ldc;
+      r.M = (int32_t)q.M; r.N = (int32_t)q.N; r.K = (int32_t)q.K;
+      const bool empty = q.M == 0 || q.N == 0;
+      r.tiles_m = empty ? 0 : (int32_t)((q.M + ptg::kBatchBM - 1) / ptg::kBatchBM);
+      r.tiles_n = empty ? 0 : (int32_t)((q.N + ptg::kBatchBN - 1) / ptg::kBatchBN);
+      pre[p] = (int32_t)total;
+      total += (int64_t)r.tiles_m * r.tiles_n;
+      if (total >= ((int64_t)1 << 31)) return fail(PTG_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    }
+    pre[count] = (int32_t)total;
+    hdr->magic = ptg::kBatchMagic;
+    hdr->count = count;
+    hdr->total_tiles = (int32_t)total;
+    hdr->bm = ptg::kBatchBM;
+    hdr->bn = ptg::kBatchBN;
+    hdr->epi = epi;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PTG_OK;
+  })
+}
+
+ptg_status ptg_gemm_batch_run(int32_t count, const void* workspace, size_t ws_bytes, ptg_dtype c_dtype,
+                              ptg_epilogue epi, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_gemm_batch_run";
+    if (count <= 0) return fail(PTG_ERR_INVALID_ARG, "%s: count must be positive", fn);
+    if (count > ptg::kMaxBatch) return fail(PTG_ERR_UNSUPPORTED, "%s: count exceeds %d", fn, ptg::kMaxBatch);
+    if (c_dtype != PTG_BF16 && c_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
+    if (!valid_epi(epi)) return fail(PTG_ERR_UNSUPPORTED, "%s: bad epilogue", fn);
+    const size_t need = ptg::batch_workspace_bytes(count);
+    if (!workspace || ws_bytes < need)
+      return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    ptg::BatchLaunch b{};
+    b.workspace = workspace; b.count = count; b.epi = epi; b.out_f32 = c_dtype == PTG_F32;
+    hipError_t e = ptg::launch_batch(b, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PTG_OK;
+  })
+}
+
+ptg_status ptg_gemm_batch(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype, ptg_epilogue epi,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  ptg_status st = ptg_gemm_batch_prepare(count, problems, epi, workspace, ws_bytes, stream);
+  if (st) return st;
+  return ptg_gemm_batch_run(count, workspace, ws_bytes, c_dtype, epi, stream);
+}
+
+size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N) {
+  if (U <= 0 || N <= 0) return 0;
+  return (size_t)U * (size_t)N * sizeof(float);
+}
+
+ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
+                              const void* Xc, const int32_t* user_idx, const void* W, ptg_layout w_layout,
+                              void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_broadcast_gemm";
+    if (U <= 0 || Mc < 0 || Ku < 0 || Kc < 0 || N < 0)
+      return fail(PTG_ERR_INVALID_ARG, "%s: bad sizes (U must be positive)", fn);
+    if (Ku == 0 || Kc == 0) return fail(PTG_ERR_UNSUPPORTED, "%s: Ku and Kc must be positive", fn);
+    if (Ku % 8 || Kc % 8 || N % 8) return fail(PTG_ERR_UNSUPPORTED, "%s: Ku, Kc and N must be multiples of 8", fn);
+    if (U > ptg::kMaxDim || Mc > ptg::kMaxDim || Ku + Kc > ptg::kMaxDim || N > ptg::kMaxDim)
+      return fail(PTG_ERR_UNSUPPORTED, "%s: a dimension exceeds 2^30", fn);
+    if (w_layout != PTG_B_KN && w_layout != PTG_B_NK) return fail(PTG_ERR_UNSUPPORTED, "%s: bad layout", fn);
+    if (y_dtype != PTG_BF16 && y_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
+    if (!valid_epi(epi)) return fail(PTG_ERR_UNSUPPORTED, "%s: bad epilogue", fn);
+    if (Mc == 0 || N == 0) return PTG_OK;
+    if (!Xu || !Xc || !user_idx || !W || !Y) return fail(PTG_ERR_INVALID_ARG, "%s: null operand", fn);
+    if (needs_bias(epi) && !bias) return fail(PTG_ERR_INVALID_ARG, "%s: epilogue needs a bias", fn);
+    const size_t need = ptg_broadcast_gemm_workspace(U, N);
+    if (!workspace || ws_bytes < need)
+      return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (!aligned16(Xu) || !aligned16(Xc) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace) ||
+        (bias && !aligned16(bias)) || (reinterpret_cast<uintptr_t>(user_idx) & 3u))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (indices 4-byte)", fn);
+    const int64_t Kt = Ku + Kc;
+    const bool kn = w_layout == PTG_B_KN;
+    if (!fits31(256, Ku, Ku) || !fits31(256, Kc, Kc) || !(kn ? fits31(Kt, N, 256) : fits31(256, Kt, Kt)))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand tile exceeds 2 GiB of addressing", fn);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    float* P = reinterpret_cast<float*>(workspace);
+    // Matmul decomposition: the user half of W meets each user's features once ...
+    ptg::DenseLaunch u{};
+    u.A = Xu; u.lda = Ku;
+    u.B = W; u.ldb = kn ? N : Kt;
+    u.C = P; u.ldc = N;
+    u.M = U; u.N = N; u.K = Ku;
+    u.b_kn = kn; u.epi = PTG_EPI_NONE; u.out_f32 = 1;
+    hipError_t e = ptg::launch_dense(u, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    // ... and the candidate half runs per candidate, adding P[user_idx[r]] in the epilogue.
+    ptg::DenseLaunch c{};
+    c.A = Xc; c.lda = Kc;
+    c.B = kn ? static_cast<const void*>(static_cast<const char*>(W) + Ku * N * 2)
+             : static_cast<const void*>(static_cast<const char*>(W) + Ku * 2);
+    c.ldb = kn ? N : Kt;
+    c.C = Y; c.ldc = N;
+    c.bias = needs_bias(epi) ? bias : nullptr;
+    c.gidx = user_idx; c.P = P; c.ldp = N; c.p_rows = U;
+    c.M = Mc; c.N = N; c.K = Kc;
+    c.b_kn = kn; c.epi = epi; c.out_f32 = y_dtype == PTG_F32;
+    e = ptg::launch_dense(c, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PTG_OK;
+  })
+}
+
+ptg_status ptg_watchdog(uint32_t* value, int32_t clear) {
+  PTG_TRY({
+    if (!value) return fail(PTG_ERR_INVALID_ARG, "ptg_watchdog: value is NULL");
+    hipError_t e = ptg::read_watchdog(value, clear);
+    if (e != hipSuccess) return hip_fail(e, "ptg_watchdog");
+    return PTG_OK;
+  })
+}
+
+}  // extern "C"

@@ -1,0 +1,591 @@
+// ptg_device.hpp - gfx950 device code of the pipelined tiled GEMM.
+//
+// One persistent workgroup per compute unit runs a three-role software pipeline, the
+// structure of listing 2 in "How We Built TLX" (section "Introducing TLX"): producer waves
+// move A and B tiles into a multistage LDS ring, consumer waves run the matrix cores on
+// the staged tiles, and an epilogue stage turns the fp32 accumulators into the output.
+// The page's roles are re-expressed for CDNA4:
+//   - Producer waves issue buffer loads that write straight into LDS (16 bytes per lane,
+//     bypassing registers), the gfx950 counterpart of an asynchronous tile copy.  Each
+//     producer tracks its copies with the vector-memory counter and then bumps the slot's
+//     "full" counter in LDS.
+//   - The ring's handoff uses monotone LDS counters instead of hardware barriers: slot
+//     s = g mod STAGES holds k-step g; "full[s]" counts producer arrivals and "empty[s]"
+//     counts consumer releases.  A producer never refills a slot before every consumer has
+//     released it, and a consumer never reads a slot before every producer has filled it
+//     (the page's multistage-buffer rule; "TLX in Production" reading notes on the same
+//     listing).  Counters only grow, so no phase bit is needed.
+//   - Consumer waves read operand fragments with ds_read_b128 (K-contiguous tiles) or the
+//     transposing ds_read_b64_tr_b16 (N-contiguous tiles), issue v_mfma_f32_32x32x16_bf16
+//     into fp32 accumulators held in registers, release the slot as soon as the last
+//     fragment of a k-step has landed in registers, and run the epilogue on their own
+//     accumulators (a wave cannot hand 64 KB of accumulators to another wave on CDNA4).
+//   - The producer is also the tile scheduler: it publishes each tile's epilogue metadata
+//     in a small LDS ring next to the data, so the consumers never wait on global memory
+//     for scheduling and the pipeline keeps running across tile (and problem) boundaries.
+//
+// Layouts in LDS.  A tile is BM rows of BK bf16 (K contiguous).  A B tile is BN rows of
+// BK (layout NK) or BK rows of BN (layout KN).  Rows are cut in 16-byte chunks and the
+// chunk index is XOR-swizzled with a function of the row, so that the fragment reads of
+// one MFMA operand hit distinct LDS banks; the producer realises the swizzle by choosing
+// which global chunk each lane fetches (the LDS side of a DMA load is always linear).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptg {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+enum : int { EPI_NONE = 0, EPI_BIAS = 1, EPI_SILU = 2, EPI_BIAS_SILU = 3 };
+enum : int { OUT_BF16 = 0, OUT_F32 = 1 };
+
+// A voffset at or above 2^31 is outside every buffer descriptor built here (their record
+// counts stay below 2^31), so the DMA writes zeros: used for rows, columns and k beyond
+// the problem.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Upper bound on the polls of one wait: each poll is an LDS read plus a ~64-clock sleep,
+// so 2^20 polls last tens of milliseconds, far beyond any wait of a working pipeline
+// (microseconds).  A wait that gives up raises the workgroup's abort word, so that every
+// other wait of the workgroup returns at once, and records the event in g_watchdog for the
+// host; the kernel then finishes (with wrong results) instead of hanging.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// ---------------------------------------------------------------------------------------
+// Tile configuration
+// ---------------------------------------------------------------------------------------
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WM = WM_, WN = WN_;             // consumer waves along M and N
+  static constexpr int NCONS = WM * WN, NPROD = NPROD_;
+  static constexpr int NWAVES = NCONS + NPROD, NT = NWAVES * 64;
+  static constexpr bool B_KN = B_KN_;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;    // one consumer wave's sub-tile
+  static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
+  static constexpr int KSUB = BK / 16;                  // MFMA k-steps per ring slot
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // 1 KB per DMA
+  static constexpr int LOADS = (A_INSTR + B_INSTR) / NPROD;  // DMAs per producer per k-step
+  static constexpr int CPR_A = BK / 8;                  // 16-byte chunks per A row
+  static constexpr int CPR_B = B_KN ? BN / 8 : BK / 8;  // 16-byte chunks per B row
+  // Tile-metadata slots.  The producer rewrites slot j mod NINFO when it starts tile
+  // j + NINFO, which needs the release of k-step g(j + NINFO) - STAGES >= g(j) + n(j) + 1
+  // (each tile has at least one k-step): a step of tile j + 1.  So tile j's metadata stays
+  // in place until its epilogue is done.
+  static constexpr int NINFO = STAGES + 2;
+  static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "consumer sub-tile must be 32x32 blocks");
+  static_assert(BK % 16 == 0 && (BK == 32 || BK == 64), "BK must be 32 or 64");
+  static_assert((A_INSTR + B_INSTR) % NPROD == 0, "DMAs must split evenly over producers");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles must be whole KB");
+  static_assert(LOADS <= 31, "two k-steps of DMAs must fit the vector-memory counter");
+  static_assert(STAGES >= 2, "the producer signals a step after issuing the next one");
+  static_assert(NT <= 1024, "workgroup too large");
+};
+
+// Chunk swizzle for rows of BK bf16 (K contiguous), CPR chunks per row.  For 8 lanes
+// reading rows r..r+7 (and for 16 lanes reading r..r+15) at one logical chunk, the
+// physical chunks land in distinct 16-byte bank groups.
+template <int CPR>
+__host__ __device__ constexpr int swz_k(int r) {
+  if constexpr (CPR == 8) {
+    return ((r >> 1) ^ ((r & 1) << 2)) & 7;
+  } else {
+    static_assert(CPR == 4, "BK of 32 or 64");
+    return ((r >> 2) ^ (r >> 1)) & 3;
+  }
+}
+
+// Chunk swizzle for rows of BN bf16 (N contiguous, layout KN), CPR chunks per row.  A
+// transposing read takes 4 consecutive k-rows x 32 bytes per 16 lanes; the XOR values of
+// 4 consecutive rows differ in bits 1-2 and in bits 2-3 so that both 16- and 32-lane
+// service groups see distinct banks.
+template <int CPR>
+__host__ __device__ constexpr int swz_n(int k) {
+  if constexpr (CPR >= 16) {
+    const int m = k & 3;  // 0, 6, 10, 12 for m = 0..3
+    return ((m & 1) * 6) ^ ((m & 2) * 5);
+  } else {
+    static_assert(CPR == 8, "BN of 64 or more");
+    return (k & 3) << 1;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Tile metadata, published by the producer and read by the consumers
+// ---------------------------------------------------------------------------------------
+struct TileInfo {            // 16 dwords
+  uint32_t tag;              // tile_tag(j) for tile j, end_tag(j) when no tile j exists
+  int32_t K;                 // reduction length of this tile's problem
+  int32_t m_rows, n_cols;    // valid rows / columns of the tile (<= BM, BN)
+  uint64_t C;                // address of the tile's first output element
+  int64_t ldc;               // output row stride in elements
+  uint64_t bias;             // address of bias[n0] or 0
+  uint64_t gidx;             // address of idx[m0] (broadcast gather) or 0
+  uint64_t P;                // address of P[0][n0] (broadcast gather) or 0
+  int32_t ldp;               // row stride of P in elements
+  uint32_t p_bytes;          // bytes of P from P[0][n0] on (bounds of the gather)
+};
+static_assert(sizeof(TileInfo) == 64, "TileInfo is 16 dwords");
+
+// Tags of a metadata slot.  The consumer checks the tag of the slot it expects before it
+// uses any address from it: a slot that is not exactly what the producer published stops
+// the workgroup (abort word, watchdog bit 2) instead of steering stores.
+__host__ __device__ constexpr uint32_t tile_tag(int j) { return 0x50544700u ^ ((uint32_t)j * 2654435761u); }
+__host__ __device__ constexpr uint32_t end_tag(int j) { return 0x454e4400u ^ ((uint32_t)j * 2246822519u); }
+
+// What the producer needs to fetch a tile (never leaves the producer's registers).
+struct TileSrc {
+  const __bf16* A;   // first row of the tile
+  int64_t lda;
+  const __bf16* B;   // first row (NK) or first column (KN) of the tile
+  int64_t ldb;
+  TileInfo info;
+};
+
+// ---------------------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// A copy of x that the compiler cannot see through: index arithmetic derived from it is
+// recomputed where it is used instead of being hoisted out of loops and kept live.
+__device__ __forceinline__ int opaque(int x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The ring counters are touched with hand-issued LDS instructions.  Compiler-issued LDS
+// accesses after a DMA-to-LDS load make the compiler wait for every outstanding DMA
+// (it cannot tell the counters from the ring), which would serialise the producer; the
+// asm versions carry their own waits, and LDS executes one wave's accesses in order.
+__device__ __forceinline__ uint32_t lds_peek(const uint32_t* p) {
+  uint32_t v;
+  __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void lds_bump(uint32_t* p) {
+  __asm__ volatile("" ::: "memory");
+  if (lane_id() == 0) {
+    const uint32_t one = 1;
+    __asm__ volatile("ds_add_u32 %0, %1" : : "v"(lds_addr(p)), "v"(one) : "memory");
+  }
+}
+
+extern __device__ uint32_t g_watchdog;
+
+// Stop the workgroup: raise its abort word (every wait returns at once) and record `why`
+// in the device watchdog word (1: a wait timed out, 2: inconsistent tile metadata).
+__device__ __forceinline__ void raise_abort(uint32_t* abort, uint32_t why) {
+  if (lane_id() == 0) {
+    const uint32_t one = 1;
+    __asm__ volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(abort)), "v"(one) : "memory");
+    atomicOr(&g_watchdog, why);
+  }
+}
+
+// Wait until a monotone LDS counter reaches `target`; bounded (see kSpinLimit).
+__device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t target, uint32_t* abort) {
+  uint32_t polls = 0;
+  while ((uint32_t)__builtin_amdgcn_readfirstlane(lds_peek(p)) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if ((++polls & 63) == 0) {
+      if ((uint32_t)__builtin_amdgcn_readfirstlane(lds_peek(abort)) != 0) break;
+      if (polls >= kSpinLimit) {
+        raise_abort(abort, 1u);
+        break;
+      }
+    }
+  }
+  __asm__ volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  __builtin_amdgcn_s_waitcnt(imm);
+  __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Wave-uniform copies of a value.  The builtin returns a signed int: it is converted to
+// uint32_t before any widening, so that a low address word with bit 31 set is never
+// sign-extended into the high word.
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+  return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | (uint64_t)uni((uint32_t)x);
+}
+
+// Buffer descriptor over [base, base + nbytes).  Base and size are wave-uniform by
+// construction; reading them through readfirstlane keeps the descriptor in scalar registers
+// (a descriptor the compiler believes divergent costs a loop around every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t ub = uni64(reinterpret_cast<uint64_t>(base));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ub), (short)0, (int)uni(nbytes),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float v) {
+  // e^-v as 2^(-v log2 e) on the hardware exp2; v / (1 + e^-v) is then v * sigmoid(v).
+  const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);
+  return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// ---------------------------------------------------------------------------------------
+// Producer role
+// ---------------------------------------------------------------------------------------
+// Producer p owns DMA indices [p * LOADS, (p + 1) * LOADS) of every k-step: index i < A_INSTR
+// copies 1 KB of the A tile, the rest copy the B tile.  Lane l of DMA i fills LDS bytes
+// [1024 i + 16 l, +16) of the slot, i.e. physical chunk P = 64 i + l of the tile.
+template <class C>
+__device__ __forceinline__ void chunk_of(int i, int lane, int& row, int& chunk) {
+  if (i < C::A_INSTR) {
+    const int P = i * 64 + lane;
+    row = P / C::CPR_A;
+    chunk = (P % C::CPR_A) ^ swz_k<C::CPR_A>(row);
+  } else {
+    const int P = (i - C::A_INSTR) * 64 + lane;
+    row = P / C::CPR_B;  // n-row (NK) or k-row (KN)
+    if constexpr (C::B_KN) chunk = (P % C::CPR_B) ^ swz_n<C::CPR_B>(row);
+    else chunk = (P % C::CPR_B) ^ swz_k<C::CPR_B>(row);
+  }
+}
+
+template <class C, class S>
+__device__ __forceinline__ void producer_role(const typename S::Args& args, char* ring, TileInfo* info,
+                                              uint32_t* full, uint32_t* empty, uint32_t* abort, int pid,
+                                              char* sched_lds) {
+  static_assert(C::A_INSTR % C::LOADS == 0, "each producer copies either A or B chunks");
+  const int lane = lane_id();
+  const int i0 = pid * C::LOADS;
+  const bool opA = i0 < C::A_INSTR;                 // this producer's operand
+  const int lds_base = opA ? i0 * 1024 : C::A_BYTES + (i0 - C::A_INSTR) * 1024;
+  uint32_t g = 0;  // k-steps issued by this workgroup so far (all tiles)
+  for (int j = 0;; ++j) {
+    TileSrc t = {};
+    const bool has = S::template tile<C>(args, j, t, sched_lds);
+    // Per-lane byte offset of each of this producer's chunks; rows/columns outside the
+    // problem get an out-of-range offset, so the DMA writes zeros there.
+    uint32_t voff[C::LOADS];
+    const void* src = nullptr;
+    uint32_t src_bytes = 0;
+    int64_t k_stride = 2;   // bytes per unit of k along the operand (for the k-step offset)
+    int nsteps = 1;
+    if (has) {
+      const int K = t.info.K;
+      nsteps = (K + C::BK - 1) / C::BK;
+      if (opA) {
+        src = t.A;
+        src_bytes = (uint32_t)((int64_t)(t.info.m_rows - 1) * t.lda * 2 + (int64_t)K * 2);
+      } else {
+        src = t.B;
+        src_bytes = C::B_KN ? (uint32_t)((int64_t)(K - 1) * t.ldb * 2 + (int64_t)t.info.n_cols * 2)
+                            : (uint32_t)((int64_t)(t.info.n_cols - 1) * t.ldb * 2 + (int64_t)K * 2);
+        if (C::B_KN) k_stride = t.ldb * 2;
+      }
+#pragma unroll
+      for (int q = 0; q < C::LOADS; ++q) {
+        const int i = i0 + q;
+        int row, c;
+        chunk_of<C>(i, lane, row, c);
+        bool ok;
+        int64_t off;
+        if (opA) {
+          ok = row < t.info.m_rows;
+          off = row * t.lda * 2 + c * 16;
+        } else if (C::B_KN) {
+          ok = c * 8 < t.info.n_cols;
+          off = row * t.ldb * 2 + c * 16;
+        } else {
+          ok = row < t.info.n_cols;
+          off = row * t.ldb * 2 + c * 16;
+        }
+        voff[q] = ok ? (uint32_t)off : kOutOfRange;
+      }
+    }
+    for (int st = 0; st < nsteps; ++st, ++g) {
+      const int s = g % C::STAGES;
+      wait_at_least(&empty[s], (uint32_t)C::NCONS * (g / C::STAGES), abort);
+      if (st == 0 && pid == 0 && lane == 0) {
+        // publish this tile's metadata, or the end marker, in its info slot
+        TileInfo ti = t.info;
+        ti.tag = has ? tile_tag(j) : end_tag(j);
+        info[j % C::NINFO] = ti;
+      }
+      if (has) {
+        const int k0 = st * C::BK;
+        const bool tail = k0 + C::BK > t.info.K;
+        char* dst = ring + s * C::STAGE_BYTES + lds_base;
+        // The k-step offset moves the descriptor's base (scalar arithmetic); the scalar
+        // offset operand of the DMA stays 0: on gfx950 a nonzero one is not used with
+        // buffer-to-LDS loads (it does not only move the global address).
+        const int64_t kbytes = (int64_t)k0 * k_stride;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(static_cast<const char*>(src) + kbytes, src_bytes - (uint32_t)kbytes);
+        const uint32_t soff = 0;
+        if (!tail) {
+#pragma unroll
+          for (int q = 0; q < C::LOADS; ++q) dma16(rs, dst + q * 1024, voff[q], soff);
+        } else {
+          // the last, partial k-step: chunks past K are zero-filled
+#pragma unroll
+          for (int q = 0; q < C::LOADS; ++q) {
+            int row, c;
+            chunk_of<C>(i0 + q, lane, row, c);
+            const int kpos = (!opA && C::B_KN) ? row : c * 8;
+            dma16(rs, dst + q * 1024, k0 + kpos < t.info.K ? voff[q] : kOutOfRange, soff);
+          }
+        }
+        if (g > 0) {
+          wait_vmcnt<C::LOADS>();   // the previous k-step's copies have landed in LDS
+          lds_bump(&full[(g - 1) % C::STAGES]);
+        }
+      } else if (g > 0) {
+        wait_vmcnt<0>();
+        lds_bump(&full[(g - 1) % C::STAGES]);
+      }
+    }
+    if (!has) break;
+  }
+  // the end marker's step
+  wait_vmcnt<0>();
+  lds_bump(&full[(g - 1) % C::STAGES]);
+}
+
+// ---------------------------------------------------------------------------------------
+// Consumer role: MFMA on staged tiles, then the epilogue stage on the accumulators
+// ---------------------------------------------------------------------------------------
+
+// Epilogue stage of one consumer wave: out = silu?(acc + bias + P[idx[row]]), converted and
+// stored.  Every access goes through a buffer descriptor; elements outside the tile's valid
+// rows/columns get an out-of-range offset, so loads return 0 and stores are dropped.
+template <class C>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], int wm, int wn,
+                                         int m_rows, int n_cols, uint64_t Cp, int ldc,
+                                         uint64_t biasp, uint64_t gidxp, uint64_t Pp, int ldp,
+                                         uint32_t p_bytes, int epi, bool f32out) {
+  const int lane = opaque(lane_id());
+  const int osz = f32out ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)(((m_rows - 1) * ldc + n_cols) * osz));
+  const bool do_bias = (epi == EPI_BIAS || epi == EPI_BIAS_SILU) && biasp != 0;
+  const bool do_silu = (epi == EPI_SILU || epi == EPI_BIAS_SILU);
+  const bool gather = gidxp != 0;
+  float bcol[C::TN];
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const int col = wn * C::WTN + tn * 32 + (lane & 31);
+    bcol[tn] = 0.0f;
+    if (do_bias) {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<void*>(biasp), (uint32_t)(n_cols * 4));
+      bcol[tn] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, col < n_cols ? col * 4 : kOutOfRange, 0, 0));
+    }
+  }
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * C::WTM + tm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const bool row_ok = row < m_rows;
+      int prow = 0;
+      if (gather) {
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<void*>(gidxp), (uint32_t)(m_rows * 4));
+        prow = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, row_ok ? row * 4 : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const int col = wn * C::WTN + tn * 32 + (lane & 31);
+        const bool ok = row_ok && col < n_cols;
+        float v = acc[tm][tn][r] + bcol[tn];
+        if (gather) {
+          const __amdgpu_buffer_rsrc_t rp = make_rsrc(reinterpret_cast<void*>(Pp), p_bytes);
+          const uint32_t po = ok ? (uint32_t)(prow * ldp + col) * 4u : kOutOfRange;
+          v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, po, 0, 0));
+        }
+        if (do_silu) v = silu(v);
+        const uint32_t vo = ok ? (uint32_t)(row * ldc + col) * (uint32_t)osz : kOutOfRange;
+        if (f32out) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, vo, 0, 0);
+        } else {
+          const __bf16 h = (__bf16)v;
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), rc, vo, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, uint32_t* full, uint32_t* empty,
+                                              uint32_t* abort, int cw, int epi, bool f32out) {
+  const int lane = lane_id();
+  const int wm = cw / C::WN, wn = cw % C::WN;
+  // A-fragment addressing: lane l holds row (l % 32) of a 32-row block and k-chunk l / 32.
+  // Physical chunk = (2 kk + l/32) ^ swz(row) = (2 kk) ^ (l/32 ^ swz(row)) since bit 0 of
+  // 2 kk is clear; swz(row) depends only on row % 16, the same for every block of the wave.
+  const int ra = wm * C::WTM + (lane & 31);
+  const int a_chunk = (lane >> 5) ^ swz_k<C::CPR_A>(ra);
+  const int a_base = ra * C::BK * 2;
+  int b_base = 0, b_chunk = 0;
+  int b_kn[C::TN][2];  // KN: byte offset of each transposing read at sub-step 0
+  if constexpr (!C::B_KN) {
+    const int rb = wn * C::WTN + (lane & 31);
+    b_chunk = (lane >> 5) ^ swz_k<C::CPR_B>(rb);
+    b_base = rb * C::BK * 2;
+  } else {
+    // Transposing read: in each 16-lane block, lane i fetches 4 bf16 of k-row (i / 4) at
+    // columns 4 (i % 4) .. +3; the hardware hands lane i the 4 k-values of column i.
+    // Sub-step kk adds 16 k-rows, a multiple of 4, so the swizzle (a function of k mod 4)
+    // and hence the offset within a row do not change with kk.
+    const int blk = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = (blk >> 1) * 8 + h * 4 + (i >> 2);
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const int n = wn * C::WTN + tn * 32 + (blk & 1) * 16 + (i & 3) * 4;
+        b_kn[tn][h] = k * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(k)) << 4) + ((n >> 2) & 1) * 8;
+      }
+    }
+  }
+
+  uint32_t g = 0;
+  for (int j = 0;; ++j) {
+    // The first k-step of tile j carries its metadata.
+    const int s0 = g % C::STAGES;
+    wait_at_least(&full[s0], (uint32_t)C::NPROD * (g / C::STAGES + 1), abort);
+    const TileInfo* ti = &info[j % C::NINFO];
+    const uint32_t tag = uni(ti->tag);
+    if (tag != tile_tag(j)) {
+      // the end marker, or (never in a working pipeline) a slot that is not what was
+      // published: release the step so the counters stay consistent, and stop
+      if (tag != end_tag(j)) raise_abort(abort, 2u);
+      lds_bump(&empty[s0]);
+      break;
+    }
+    const int K = (int)uni((uint32_t)ti->K);
+    const int nsteps = (K + C::BK - 1) / C::BK;
+
+    f32x16 acc[C::TM][C::TN];
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = f32x16{};
+
+    for (int st = 0; st < nsteps; ++st, ++g) {
+      const int s = g % C::STAGES;
+      if (st > 0) wait_at_least(&full[s], (uint32_t)C::NPROD * (g / C::STAGES + 1), abort);
+      const char* slot = ring + s * C::STAGE_BYTES;
+      const char* slotB = slot + C::A_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < C::KSUB; ++kk) {
+        // Fragments of one 16-deep sub-step: B first, so the first MFMAs can start while
+        // the later A rows are still in flight.
+        bf16x8 a[C::TM], b[C::TN];
+        if constexpr (!C::B_KN) {
+          const char* pb = slotB + b_base + (((kk * 2) ^ b_chunk) << 4);
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn)
+            b[tn] = *reinterpret_cast<const bf16x8*>(pb + tn * 32 * C::BK * 2);
+        } else {
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) {
+            i16x4 hv[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(slotB + b_kn[tn][h] + kk * 16 * C::BN * 2));
+            typedef __attribute__((ext_vector_type(8))) short i16x8;
+            const i16x8 v = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            b[tn] = __builtin_bit_cast(bf16x8, v);
+          }
+        }
+        const char* pa = slot + a_base + (((kk * 2) ^ a_chunk) << 4);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+          a[tm] = *reinterpret_cast<const bf16x8*>(pa + tm * 32 * C::BK * 2);
+        if (kk == C::KSUB - 1) {
+          // every fragment of this k-step is in registers: hand the slot back
+          wait_lgkm0();
+          lds_bump(&empty[s]);
+        }
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+        // keep each sub-step's loads next to its MFMAs: the register budget has no room for
+        // a second set of fragments; the other consumer wave on the SIMD hides the latency
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- epilogue stage: bias, broadcast gather-add, SiLU, convert, store -------------
+    // The metadata is read again here (it is still in place, see NINFO), so that nothing
+    // of the epilogue stays live in registers across the MFMA loop.
+    const int m_rows = (int)uni((uint32_t)ti->m_rows);
+    const int n_cols = (int)uni((uint32_t)ti->n_cols);
+    const uint64_t Cp = uni64(ti->C);
+    const int ldc = (int)uni((uint32_t)ti->ldc);
+    const uint64_t biasp = uni64(ti->bias);
+    const uint64_t gidxp = uni64(ti->gidx);
+    const uint64_t Pp = uni64(ti->P);
+    const int ldp = (int)uni((uint32_t)ti->ldp);
+    const uint32_t p_bytes = uni(ti->p_bytes);
+    if (m_rows < 1 || m_rows > C::BM || n_cols < 1 || n_cols > C::BN || ldc < n_cols) {
+      raise_abort(abort, 2u);
+      break;
+    }
+    epilogue<C>(acc, wm, wn, m_rows, n_cols, Cp, ldc, biasp, gidxp, Pp, ldp, p_bytes, epi, f32out);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------------------
+template <class C, class S>
+__global__ __launch_bounds__(C::NT, 1) void ptg_kernel(typename S::Args args) {
+  constexpr int kFlags = 2 * C::STAGES + 1;  // full[], empty[], abort
+  __shared__ __attribute__((aligned(1024))) char smem[C::RING_BYTES + C::NINFO * sizeof(TileInfo) +
+                                                    kFlags * sizeof(uint32_t) + S::LDS_BYTES];
+  char* ring = smem;
+  TileInfo* info = reinterpret_cast<TileInfo*>(smem + C::RING_BYTES);
+  uint32_t* full = reinterpret_cast<uint32_t*>(smem + C::RING_BYTES + C::NINFO * sizeof(TileInfo));
+  uint32_t* empty = full + C::STAGES;
+  uint32_t* abort = empty + C::STAGES;
+  char* sched_lds = reinterpret_cast<char*>(full + kFlags);
+  if (threadIdx.x < kFlags) full[threadIdx.x] = 0;
+  S::template init<C>(args, sched_lds);  // cooperative; the barrier below publishes it
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  if (wave < C::NCONS) {
+    __builtin_amdgcn_s_setprio(1);
+    consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0);
+  } else {
+    producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds);
+  }
+}
+
+}  // namespace ptg

@@ -1,0 +1,428 @@
+// ptg_kernels.hip - tile schedulers, tile-configuration choice and kernel launches.
+//
+// Three schedulers feed the same pipelined kernel (ptg_device.hpp):
+//   Dense   - one problem; tiles visited in an XCD-aware, M-grouped order.
+//   Grouped - mixture-of-experts grouped GEMM: the expert row ranges come from int32 offsets
+//             in device memory (How We Built TLX, "Case Study 3: Distributed Grouped GEMM for
+//             LLM Pretraining"); the per-expert tile prefix is rebuilt in LDS by every
+//             workgroup, so the host never reads the offsets.
+//   Batch   - independent problems (pointer-array form) from a table in the caller's
+//             workspace, with the tile prefix staged in LDS; the persistent workgroups run
+//             across problem boundaries without draining the ring ("Case Study 2", final
+//             stage of the linear-compression kernel).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "ptg_device.hpp"
+#include "ptg_launch.h"
+
+namespace ptg {
+
+__device__ uint32_t g_watchdog = 0;
+
+// MI300-class parts hand workgroups of one dispatch to their XCDs round-robin (8 XCDs
+// on MI355X).  Renumbering so that consecutive tile indices land on one XCD lets tiles that
+// share A rows or B columns meet in that XCD's L2.
+__device__ __forceinline__ int64_t xcd_rank(int w, int grid) {
+  return (grid % 8 == 0) ? (int64_t)(w % 8) * (grid / 8) + w / 8 : (int64_t)w;
+}
+
+// ---------------------------------------------------------------------------------------
+// Dense scheduler
+// ---------------------------------------------------------------------------------------
+struct DenseSched {
+  struct Args {
+    const __bf16* A;
+    const __bf16* B;
+    char* C;
+    const float* bias;
+    const int32_t* gidx;
+    const float* P;
+    int64_t lda, ldb, ldc;
+    int32_t ldp, p_rows;
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n, group_m;
+    int32_t epi, out_f32, out_bytes;
+  };
+  static constexpr int LDS_BYTES = 16;
+
+  template <class C>
+  __device__ static void init(const Args&, char*) {}
+
+  template <class C>
+  __device__ static bool tile(const Args& a, int j, TileSrc& t, char*) {
+    const int64_t L = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
+    const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
+    if (L >= ntiles) return false;
+    // groups of `group_m` tile rows, walked column by column inside a group
+    const int64_t per_group = (int64_t)a.group_m * a.tiles_n;
+    const int64_t grp = L / per_group, in = L % per_group;
+    const int first_m = (int)(grp * a.group_m);
+    const int gm = min(a.tiles_m - first_m, a.group_m);
+    const int tm = first_m + (int)(in % gm), tn = (int)(in / gm);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    t.A = a.A + m0 * a.lda;
+    t.lda = a.lda;
+    t.B = C::B_KN ? a.B + n0 : a.B + n0 * a.ldb;
+    t.ldb = a.ldb;
+    t.info.tag = 0;  // set by the producer when it publishes the slot
+    t.info.K = a.K;
+    t.info.m_rows = (int)min((int64_t)C::BM, a.M - m0);
+    t.info.n_cols = (int)min((int64_t)C::BN, a.N - n0);
+    t.info.C = (uint64_t)(a.C + (m0 * a.ldc + n0) * a.out_bytes);
+    t.info.ldc = a.ldc;
+    t.info.bias = a.bias ? (uint64_t)(a.bias + n0) : 0;
+    t.info.gidx = a.gidx ? (uint64_t)(a.gidx + m0) : 0;
+    t.info.P = a.P ? (uint64_t)(a.P + n0) : 0;
+    t.info.ldp = a.ldp;
+    t.info.p_bytes = a.P ? (uint32_t)(((int64_t)a.p_rows * a.ldp - n0) * 4) : 0u;
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Exclusive prefix sum over n <= NT * IPT values held one per index, in LDS, by the whole
+// workgroup.  `val(i)` gives value i; the result goes to out[0..n] (out[n] = total).
+// ---------------------------------------------------------------------------------------
+template <int NT, class F>
+__device__ __forceinline__ void block_exclusive_scan(int n, F val, int32_t* out, int32_t* wave_sums) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWAVE = NT / 64;
+  const int per = (n + NT - 1) / NT;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int32_t local = 0;
+  for (int i = lo; i < hi; ++i) local += val(i);
+  // inclusive scan of `local` across the wave
+  int32_t inc = local;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wave_sums[wave] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int w = 0; w < NWAVE; ++w) {
+      const int32_t x = wave_sums[w];
+      wave_sums[w] = run;
+      run += x;
+    }
+    wave_sums[NWAVE] = run;
+  }
+  __syncthreads();
+  int32_t run = wave_sums[wave] + inc - local;
+  for (int i = lo; i < hi; ++i) {
+    out[i] = run;
+    run += val(i);
+  }
+  if (tid == 0) out[n] = wave_sums[NWAVE];
+  __syncthreads();
+}
+
+// Largest index g in [0, n) with pre[g] <= x (pre nondecreasing, pre[0] <= x < pre[n]).
+__device__ __forceinline__ int upper_index(const int32_t* pre, int n, int64_t x) {
+  int lo = 0, hi = n;  // invariant: pre[lo] <= x < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)pre[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------------------
+// Grouped (mixture-of-experts) scheduler
+// ---------------------------------------------------------------------------------------
+struct GroupedSched {
+  struct Args {
+    const __bf16* X;
+    const __bf16* W;
+    char* Y;
+    const float* bias;
+    const int32_t* offsets;
+    int64_t M_total;
+    int32_t G, N, K, tiles_n;
+    int32_t epi, out_f32, out_bytes;
+  };
+  // offsets[G + 1], tile prefix[G + 1], scan scratch
+  static constexpr int LDS_BYTES = 2 * (kMaxGroups + 1) * 4 + 20 * 4;
+
+  template <class C>
+  __device__ static void init(const Args& a, char* lds) {
+    int32_t* off = reinterpret_cast<int32_t*>(lds);
+    int32_t* pre = off + kMaxGroups + 1;
+    int32_t* scratch = pre + kMaxGroups + 1;
+    // Offsets are clamped to [0, M_total]: the precondition says they already are, and the
+    // clamp keeps every access inside X and Y even when a caller breaks it.
+    for (int i = threadIdx.x; i <= a.G; i += C::NT) {
+      const int64_t o = a.offsets[i];
+      off[i] = (int32_t)(o < 0 ? 0 : (o > a.M_total ? a.M_total : o));
+    }
+    __syncthreads();
+    const int tn = a.tiles_n;
+    block_exclusive_scan<C::NT>(a.G, [&](int g) {
+      const int cnt = off[g + 1] - off[g];
+      return cnt > 0 ? ((cnt + C::BM - 1) / C::BM) * tn : 0;
+    }, pre, scratch);
+  }
+
+  template <class C>
+  __device__ static bool tile(const Args& a, int j, TileSrc& t, char* lds) {
+    const int32_t* off = reinterpret_cast<const int32_t*>(lds);
+    const int32_t* pre = off + kMaxGroups + 1;
+    const int64_t L = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
+    if (L >= pre[a.G]) return false;
+    const int g = upper_index(pre, a.G, L);
+    const int local = (int)(L - pre[g]);
+    const int row0 = off[g], cnt = off[g + 1] - off[g];  // cnt > 0: the group has tiles
+    const int mtiles = (cnt + C::BM - 1) / C::BM;
+    const int mt = local % mtiles, nt = local / mtiles;  // the m-tiles of one W_g strip are adjacent
+    const int64_t m0 = (int64_t)row0 + (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
+    const int64_t wsize = (int64_t)a.K * a.N;
+    t.A = a.X + m0 * a.K;
+    t.lda = a.K;
+    t.B = a.W + g * wsize + (C::B_KN ? n0 : n0 * a.K);
+    t.ldb = C::B_KN ? a.N : a.K;
+    t.info.tag = 0;  // set by the producer when it publishes the slot
+    t.info.K = a.K;
+    t.info.m_rows = min(C::BM, cnt - mt * C::BM);
+    t.info.n_cols = (int)min((int64_t)C::BN, (int64_t)a.N - n0);
+    t.info.C = (uint64_t)(a.Y + (m0 * a.N + n0) * a.out_bytes);
+    t.info.ldc = a.N;
+    t.info.bias = a.bias ? (uint64_t)(a.bias + (int64_t)g * a.N + n0) : 0;
+    t.info.gidx = 0;
+    t.info.P = 0;
+    t.info.ldp = 0;
+    t.info.p_bytes = 0;
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Batch (pointer-array) scheduler
+// ---------------------------------------------------------------------------------------
+struct BatchSched {
+  struct Args {
+    const int32_t* prefix;        // [count + 1] tile prefix (workspace)
+    const BatchProblem* probs;    // [count]
+    int32_t count;
+    int32_t epi, out_f32, out_bytes;
+  };
+  static constexpr int LDS_BYTES = (kMaxBatch + 1) * 4 + 16;
+
+  template <class C>
+  __device__ static void init(const Args& a, char* lds) {
+    int32_t* pre = reinterpret_cast<int32_t*>(lds);
+    for (int i = threadIdx.x; i <= a.count; i += C::NT) pre[i] = a.prefix[i];
+  }
+
+  template <class C>
+  __device__ static bool tile(const Args& a, int j, TileSrc& t, char* lds) {
+    const int32_t* pre = reinterpret_cast<const int32_t*>(lds);
+    const int64_t L = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
+    if (L >= pre[a.count]) return false;
+    const int p = upper_index(pre, a.count, L);
+    const int local = (int)(L - pre[p]);
+    const BatchProblem& q = a.probs[p];
+    const int mt = local % q.tiles_m, nt = local / q.tiles_m;
+    const int64_t m0 = (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
+    t.A = reinterpret_cast<const __bf16*>(q.A) + m0 * q.lda;
+    t.lda = q.lda;
+    t.B = reinterpret_cast<const __bf16*>(q.B) + n0;
+    t.ldb = q.ldb;
+    t.info.tag = 0;  // set by the producer when it publishes the slot
+    t.info.K = q.K;
+    t.info.m_rows = (int)min((int64_t)C::BM, (int64_t)q.M - m0);
+    t.info.n_cols = (int)min((int64_t)C::BN, (int64_t)q.N - n0);
+    t.info.C = (uint64_t)(reinterpret_cast<char*>(q.C) + (m0 * q.ldc + n0) * a.out_bytes);
+    t.info.ldc = q.ldc;
+    t.info.bias = q.bias ? (uint64_t)(q.bias + n0) : 0;
+    t.info.gidx = 0;
+    t.info.P = 0;
+    t.info.ldp = 0;
+    t.info.p_bytes = 0;
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Tile configurations
+// ---------------------------------------------------------------------------------------
+// Large problems: 256 x 256 tiles, 8 consumer waves (2 x 4, 128 x 64 each), 4 producers,
+// two 64 KB ring slots.  Medium/small: 128 x 128 tiles, 4 consumers (64 x 64 each), 2
+// producers, four 32 KB slots.
+template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN>;
+template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN>;
+
+struct DeviceInfo {
+  int cus = 0;
+};
+
+static int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <class C, class S>
+static hipError_t launch_persistent(const typename S::Args& a, int64_t max_tiles, hipStream_t stream) {
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorNoDevice;
+  const int64_t grid = max_tiles < cus ? max_tiles : cus;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((ptg_kernel<C, S>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class C>
+static void describe(int32_t cfg[6]) {
+  cfg[0] = C::BM; cfg[1] = C::BN; cfg[2] = C::BK; cfg[3] = C::STAGES; cfg[4] = C::NCONS; cfg[5] = C::NPROD;
+}
+
+static bool use_large(int64_t M, int64_t N) {
+  // enough 256 x 256 tiles to fill the chip at least once
+  const int64_t t = ((M + 255) / 256) * ((N + 255) / 256);
+  return t >= 128;
+}
+
+void dense_config(int64_t M, int64_t N, int64_t K, int b_kn, int32_t cfg[6]) {
+  (void)K;
+  if (use_large(M, N)) {
+    if (b_kn) describe<CfgLarge<true>>(cfg); else describe<CfgLarge<false>>(cfg);
+  } else {
+    if (b_kn) describe<CfgMedium<true>>(cfg); else describe<CfgMedium<false>>(cfg);
+  }
+}
+
+template <class C>
+static hipError_t launch_dense_cfg(const DenseLaunch& d, hipStream_t stream) {
+  DenseSched::Args a;
+  a.A = reinterpret_cast<const __bf16*>(d.A);
+  a.B = reinterpret_cast<const __bf16*>(d.B);
+  a.C = reinterpret_cast<char*>(d.C);
+  a.bias = d.bias;
+  a.gidx = d.gidx;
+  a.P = d.P;
+  a.lda = d.lda; a.ldb = d.ldb; a.ldc = d.ldc; a.ldp = (int32_t)d.ldp; a.p_rows = (int32_t)d.p_rows;
+  a.M = (int32_t)d.M; a.N = (int32_t)d.N; a.K = (int32_t)d.K;
+  a.tiles_m = (int32_t)((d.M + C::BM - 1) / C::BM);
+  a.tiles_n = (int32_t)((d.N + C::BN - 1) / C::BN);
+  a.group_m = 4;
+  a.epi = d.epi; a.out_f32 = d.out_f32; a.out_bytes = d.out_f32 ? 4 : 2;
+  return launch_persistent<C, DenseSched>(a, (int64_t)a.tiles_m * a.tiles_n, stream);
+}
+
+hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream) {
+  if (d.M == 0 || d.N == 0) return hipSuccess;
+  if (use_large(d.M, d.N)) {
+    return d.b_kn ? launch_dense_cfg<CfgLarge<true>>(d, stream) : launch_dense_cfg<CfgLarge<false>>(d, stream);
+  }
+  return d.b_kn ? launch_dense_cfg<CfgMedium<true>>(d, stream) : launch_dense_cfg<CfgMedium<false>>(d, stream);
+}
+
+template <class C>
+static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream) {
+  GroupedSched::Args a;
+  a.X = reinterpret_cast<const __bf16*>(g.X);
+  a.W = reinterpret_cast<const __bf16*>(g.W);
+  a.Y = reinterpret_cast<char*>(g.Y);
+  a.bias = g.bias;
+  a.offsets = g.offsets;
+  a.M_total = g.M_total;
+  a.G = g.G; a.N = (int32_t)g.N; a.K = (int32_t)g.K;
+  a.tiles_n = (int32_t)((g.N + C::BN - 1) / C::BN);
+  a.epi = g.epi; a.out_f32 = g.out_f32; a.out_bytes = g.out_f32 ? 4 : 2;
+  // every group adds at most one partial m-tile
+  const int64_t max_tiles = ((g.M_total + C::BM - 1) / C::BM + g.G) * a.tiles_n;
+  return launch_persistent<C, GroupedSched>(a, max_tiles, stream);
+}
+
+hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream) {
+  if (g.M_total == 0 || g.N == 0) return hipSuccess;
+  return g.b_kn ? launch_grouped_cfg<CfgMedium<true>>(g, stream) : launch_grouped_cfg<CfgMedium<false>>(g, stream);
+}
+
+hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream) {
+  using C = CfgMedium<true>;
+  static_assert(C::BM == kBatchBM && C::BN == kBatchBN, "batch prefix tile shape");
+  const char* ws = reinterpret_cast<const char*>(b.workspace);
+  BatchSched::Args a;
+  a.prefix = reinterpret_cast<const int32_t*>(ws + sizeof(BatchHeader));
+  a.probs = reinterpret_cast<const BatchProblem*>(ws + sizeof(BatchHeader) + batch_prefix_bytes(b.count));
+  a.count = b.count;
+  a.epi = b.epi; a.out_f32 = b.out_f32; a.out_bytes = b.out_f32 ? 4 : 2;
+  // the tile count lives on the device: launch one workgroup per CU, idle ones exit at once
+  return launch_persistent<C, BatchSched>(a, (int64_t)1 << 30, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// Validation kernels for device-resident preconditions
+// ---------------------------------------------------------------------------------------
+// Flag word of the check kernels (one per device, no allocation).
+__device__ int32_t g_check_flag = 0;
+
+__global__ void check_offsets_kernel(const int32_t* off, int32_t G, int64_t M_total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i > G) return;
+  bool bad = false;
+  if (i == 0 && off[0] != 0) bad = true;
+  if (i == G && (int64_t)off[G] != M_total) bad = true;
+  if (i < G && off[i + 1] < off[i]) bad = true;
+  if (bad) atomicOr(&g_check_flag, 1);
+}
+
+__global__ void check_index_kernel(const int32_t* idx, int64_t n, int64_t U) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t v = idx[i];
+  if (v < 0 || (int64_t)v >= U) atomicOr(&g_check_flag, 1);
+}
+
+template <class Launch>
+static hipError_t run_check(hipStream_t stream, int* bad, Launch launch) {
+  int32_t h = 0;
+  hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_check_flag), &h, sizeof h, 0, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipMemcpyFromSymbolAsync(&h, HIP_SYMBOL(g_check_flag), sizeof h, 0, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  *bad = (e == hipSuccess && h != 0) ? 1 : 0;
+  return e;
+}
+
+hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hipStream_t stream, int* bad) {
+  return run_check(stream, bad, [&]() {
+    const int64_t n = (int64_t)G + 1;
+    hipLaunchKernelGGL(check_offsets_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       offsets, G, M_total);
+    return hipGetLastError();
+  });
+}
+
+hipError_t check_index(const int32_t* idx, int64_t n, int64_t U, hipStream_t stream, int* bad) {
+  return run_check(stream, bad, [&]() {
+    hipLaunchKernelGGL(check_index_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       idx, n, U);
+    return hipGetLastError();
+  });
+}
+
+hipError_t read_watchdog(uint32_t* value, int clear) {
+  hipError_t e = hipMemcpyFromSymbol(value, HIP_SYMBOL(g_watchdog), sizeof(uint32_t), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !clear) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_watchdog), &zero, sizeof(uint32_t), 0, hipMemcpyHostToDevice);
+}
+
+}  // namespace ptg

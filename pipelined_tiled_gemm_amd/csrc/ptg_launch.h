@@ -1,0 +1,95 @@
+// ptg_launch.h - host-side launch descriptions shared by the C ABI layer and the kernels.
+// Plain structs (no device code): the ABI layer fills them after validation, the launchers
+// in ptg_kernels.hip pick a tile configuration and enqueue one persistent kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptg {
+
+// One dense problem C = epi(A.B + bias [+ P[gidx[m]]]).
+struct DenseLaunch {
+  const void* A;
+  const void* B;
+  void* C;
+  const float* bias;          // [N] or null
+  const int32_t* gidx;        // [M] row -> row of P, or null (broadcast gather)
+  const float* P;             // [p_rows x ldp] fp32, or null
+  int64_t lda, ldb, ldc, ldp, p_rows;
+  int64_t M, N, K;
+  int b_kn;                   // 1: B is K x N; 0: B is N x K
+  int epi;                    // ptg_epilogue value
+  int out_f32;                // 1: float32 output; 0: bfloat16
+};
+
+struct GroupedLaunch {
+  const void* X;
+  const void* W;
+  void* Y;
+  const float* bias;          // [G x N] or null
+  const int32_t* offsets;     // device [G + 1]
+  int64_t M_total, N, K;
+  int32_t G;
+  int b_kn, epi, out_f32;
+};
+
+// Device-side record of one problem of a batch (written by ptg_gemm_batch_prepare).
+struct BatchProblem {
+  const void* A;
+  const void* B;
+  void* C;
+  const float* bias;
+  int64_t lda, ldb, ldc;
+  int32_t M, N, K;
+  int32_t tiles_m, tiles_n;
+  int32_t pad;
+};
+static_assert(sizeof(BatchProblem) == 80, "BatchProblem layout");
+
+// Workspace layout of a batch: [header 256 B][prefix int32 (count + 1), padded to 256 B][problems].
+struct BatchHeader {
+  int32_t magic;
+  int32_t count;
+  int32_t total_tiles;
+  int32_t bm, bn;
+  int32_t epi;
+  int32_t reserved[58];
+};
+static_assert(sizeof(BatchHeader) == 256, "BatchHeader layout");
+constexpr int32_t kBatchMagic = 0x50544742;  // "PTGB"
+
+inline size_t batch_prefix_bytes(int32_t count) {
+  return ((size_t)(count + 1) * 4 + 255) / 256 * 256;
+}
+inline size_t batch_workspace_bytes(int32_t count) {
+  return sizeof(BatchHeader) + batch_prefix_bytes(count) + (size_t)count * sizeof(BatchProblem);
+}
+
+struct BatchLaunch {
+  const void* workspace;
+  int32_t count;
+  int epi, out_f32;
+};
+
+// Limits enforced by the ABI layer.
+constexpr int32_t kMaxGroups = 1024;       // group offsets and tile prefix live in LDS
+constexpr int32_t kMaxBatch = 2048;        // batch tile prefix lives in LDS
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Tile shape used by the batch path (the prefix written by prepare depends on it).
+constexpr int kBatchBM = 128, kBatchBN = 128;
+
+hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream);
+hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream);
+hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream);
+// Validation of device-resident preconditions: runs a check kernel on `stream`, waits for
+// it, and sets *bad to 1 if the data violates the precondition (0 otherwise).
+hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hipStream_t stream,
+                         int* bad);
+hipError_t check_index(const int32_t* idx, int64_t n, int64_t U, hipStream_t stream, int* bad);
+// The dense path's tile configuration for a problem: BM, BN, BK, stages, consumers, producers.
+void dense_config(int64_t M, int64_t N, int64_t K, int b_kn, int32_t cfg[6]);
+// Watchdog word of the bounded waits (nonzero if a wait ever gave up).
+hipError_t read_watchdog(uint32_t* value, int clear);
+
+}  // namespace ptg

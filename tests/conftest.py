@@ -9,3 +9,15 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size case, minutes of CPU work")
+
+
+def pytest_sessionstart(session):
+    """Build what is missing (never rebuild what is there): the oracle's shared library and,
+    when the HIP toolchain is present, libptg.so."""
+    import importlib
+    oracle = importlib.import_module("oracle")
+    oracle.build(force=False)
+    lib = os.path.join(ROOT, "pipelined_tiled_gemm_amd", "libptg.so")
+    if not os.path.exists(lib):
+        from pipelined_tiled_gemm_amd import build
+        build.build()

@@ -1,0 +1,144 @@
+"""The C ABI on the CPU: the library loads, exports every entry point include/ptg.h declares,
+and rejects invalid calls with the documented status before touching any device.
+
+Pointers passed here are never dereferenced: every call below fails host-side validation
+(or is a documented no-op) before a HIP call would be made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from pipelined_tiled_gemm_amd import _ffi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+P = 0x10000  # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _ffi.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ptg.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ptg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    decl = declared_functions()
+    assert len(decl) >= 15
+    assert set(decl) == set(_ffi.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_exports_are_c_symbols():
+    out = os.popen(f"nm -D --defined-only {_ffi.LIB_PATH}").read()
+    syms = set(re.findall(r"\bT (ptg_\w+)", out))
+    assert set(declared_functions()) <= syms
+
+
+def test_status_strings(L):
+    for code, name in _ffi.STATUS_NAMES.items():
+        assert L.ptg_status_string(code).decode() == name
+    assert L.ptg_version() >= 1
+
+
+def gemm(L, M=64, N=64, K=64, A=P, lda=None, B=P, ldb=None, layout=0, C=P, ldc=None, dtype=0,
+         bias=None, epi=0):
+    lda = K if lda is None else lda
+    ldb = (N if layout == 0 else K) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return L.ptg_gemm(M, N, K, A, lda, B, ldb, layout, C, ldc, dtype, bias, epi, None)
+
+
+def test_gemm_validation(L):
+    assert gemm(L, M=-1) == INVALID
+    assert gemm(L, K=0) == UNSUPPORTED
+    assert gemm(L, N=12) == UNSUPPORTED
+    assert gemm(L, K=20) == UNSUPPORTED
+    assert gemm(L, A=None) == INVALID
+    assert gemm(L, C=None) == INVALID
+    assert gemm(L, A=P + 2) == UNSUPPORTED
+    assert gemm(L, lda=32) == INVALID
+    assert gemm(L, ldb=8) == INVALID
+    assert gemm(L, ldc=72 + 4) == UNSUPPORTED      # bf16 rows must stay 16-byte aligned
+    assert gemm(L, layout=7) == UNSUPPORTED
+    assert gemm(L, dtype=9) == UNSUPPORTED
+    assert gemm(L, epi=4) == UNSUPPORTED
+    assert gemm(L, epi=1, bias=None) == INVALID      # BIAS needs a bias vector
+    assert gemm(L, M=1 << 31) == UNSUPPORTED
+    assert "ptg_gemm" in L.ptg_last_error().decode()
+    # empty problems are valid no-ops that never reach the device
+    assert gemm(L, M=0, A=None, B=None, C=None) == OK
+    assert gemm(L, N=0, A=None, B=None, C=None) == OK
+
+
+def test_grouped_validation(L):
+    def g(G=4, M=64, N=64, K=64, X=P, W=P, layout=0, off=P, Y=P, dtype=0, bias=None, epi=0):
+        return L.ptg_grouped_gemm(G, M, N, K, X, W, layout, off, Y, dtype, bias, epi, None)
+    assert g(G=0) == INVALID
+    assert g(G=1025) == UNSUPPORTED
+    assert g(K=0) == UNSUPPORTED
+    assert g(off=None) == INVALID
+    assert g(off=P + 2) == UNSUPPORTED
+    assert g(X=P + 8) == UNSUPPORTED
+    assert g(epi=3, bias=None) == INVALID
+    assert g(M=0, X=None, W=None, Y=None, off=None) == OK
+
+
+def test_batch_validation(L):
+    n = 3
+    need = L.ptg_gemm_batch_workspace(n)
+    assert need >= 256 + 16 + n * 80
+    arr = (_ffi.ProblemStruct * n)()
+    for i in range(n):
+        s = arr[i]
+        s.M, s.N, s.K = 64, 64, 64
+        s.A = s.B = s.C = P
+        s.lda = s.ldb = s.ldc = 64
+    assert L.ptg_gemm_batch_prepare(0, arr, 0, P, need, None) == INVALID
+    assert L.ptg_gemm_batch_prepare(n, arr, 0, P, need - 1, None) == WORKSPACE
+    assert L.ptg_gemm_batch_prepare(n, arr, 0, None, need, None) == WORKSPACE
+    arr[1].K = 12
+    assert L.ptg_gemm_batch_prepare(n, arr, 0, P, need, None) == UNSUPPORTED
+    arr[1].K = 64
+    arr[2].lda = 8
+    assert L.ptg_gemm_batch_prepare(n, arr, 0, P, need, None) == INVALID
+    arr[2].lda = 64
+    assert L.ptg_gemm_batch_prepare(n, arr, 1, P, need, None) == INVALID   # bias missing
+    assert L.ptg_gemm_batch_run(n, P, need - 1, 0, 0, None) == WORKSPACE
+    assert L.ptg_gemm_batch_run(n, P, need, 5, 0, None) == UNSUPPORTED
+    assert L.ptg_gemm_batch_run(2049, P, 1 << 30, 0, 0, None) == UNSUPPORTED
+
+
+def test_broadcast_validation(L):
+    U, N = 4, 64
+    need = L.ptg_broadcast_gemm_workspace(U, N)
+    assert need == U * N * 4
+
+    def b(U=U, Mc=100, Ku=64, Kc=32, N=N, Xu=P, Xc=P, idx=P, W=P, layout=0, Y=P, dtype=0,
+          bias=None, epi=0, ws=P, wsb=need):
+        return L.ptg_broadcast_gemm(U, Mc, Ku, Kc, N, Xu, Xc, idx, W, layout, Y, dtype, bias, epi,
+                                    ws, wsb, None)
+    assert b(U=0) == INVALID
+    assert b(Kc=0) == UNSUPPORTED
+    assert b(Ku=12) == UNSUPPORTED
+    assert b(idx=None) == INVALID
+    assert b(wsb=need - 4) == WORKSPACE
+    assert b(ws=None) == WORKSPACE
+    assert b(Mc=0, Xu=None, Xc=None, idx=None, W=None, Y=None, ws=None, wsb=0) == OK
+
+
+def test_describe_config(L):
+    cfg = (ctypes.c_int32 * 6)()
+    assert L.ptg_describe_config(8192, 8192, 8192, 1, cfg) == OK
+    big = list(cfg)
+    assert big[:2] == [256, 256] and big[4] + big[5] <= 16
+    assert L.ptg_describe_config(256, 256, 256, 0, cfg) == OK
+    assert list(cfg)[:2] == [128, 128]
+    assert L.ptg_describe_config(1, 1, 1, 0, None) == INVALID

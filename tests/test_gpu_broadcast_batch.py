@@ -1,0 +1,170 @@
+"""GPU parity of the in-kernel broadcast GEMM and of the batched (pointer-array) GEMM."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pipelined_tiled_gemm_amd as ptg
+import workloads as wl
+from parity import check, dev, dev_bf16, exact, host_f32, int_bf16, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _no_watchdog():
+    ptg.watchdog(clear=True)
+    yield
+    torch.cuda.synchronize()
+    assert ptg.watchdog(clear=True) == 0, "a pipeline wait timed out"
+
+
+def run_broadcast(w: wl.Broadcast, out_dtype, epi, rows=None):
+    out = ptg.broadcast_gemm(dev_bf16(w.Xu), dev_bf16(w.Xc), dev(w.idx), dev_bf16(w.W),
+                             w_layout=w.w_layout, out_dtype=out_dtype,
+                             bias=dev(w.bias) if w.bias is not None else None, epi=epi)
+    v = oracle.broadcast_gemm(w.Xu, w.Xc, w.idx, w.W, w.w_layout, w.bias, epi, rows=rows)
+    return out, v
+
+
+# ------------------------------------------------------------------------------------------
+# broadcast
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+@pytest.mark.parametrize("epi", [wl.EPI_NONE, wl.EPI_BIAS_SILU])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_broadcast_small(layout, epi, out_dtype, shuffle):
+    w = wl.broadcast(41, 5, 264, 136, 200, cmin=1, cmax=300, w_layout=layout, with_bias=True,
+                     shuffle=shuffle)
+    out, v = run_broadcast(w, out_dtype, epi)
+    check(out, v, w.Ku + w.Kc, f"broadcast layout={layout} epi={epi} shuffle={shuffle}")
+
+
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+def test_broadcast_block_identities(layout):
+    """W = [I; 0] returns Xu[idx] exactly (pins the gather); W = [0; I] returns Xc."""
+    rng = np.random.default_rng(3)
+    U, Ku, Kc, Mc = 7, 128, 128, 555
+    Xu = wl.f32_to_bf16_bits(rng.uniform(-1, 1, (U, Ku)).astype(np.float32))
+    Xc = wl.f32_to_bf16_bits(rng.uniform(-1, 1, (Mc, Kc)).astype(np.float32))
+    idx = rng.integers(0, U, Mc).astype(np.int32)
+    top = wl.f32_to_bf16_bits(np.concatenate([np.eye(Ku), np.zeros((Kc, Ku))]).astype(np.float32))
+    bot = wl.f32_to_bf16_bits(np.concatenate([np.zeros((Ku, Kc)), np.eye(Kc)]).astype(np.float32))
+    for W, want in ((top, wl.bf16_bits_to_f32(Xu).astype(np.float64)[idx]),
+                    (bot, wl.bf16_bits_to_f32(Xc).astype(np.float64))):
+        Wl = W if layout == wl.B_KN else np.ascontiguousarray(W.T)
+        for out_dtype in (torch.float32, torch.bfloat16):
+            out = ptg.broadcast_gemm(dev_bf16(Xu), dev_bf16(Xc), dev(idx), dev_bf16(Wl),
+                                     w_layout=layout, out_dtype=out_dtype)
+            exact(out, want, "block identity")
+
+
+def test_broadcast_equals_materialised_gemm():
+    """Invariant: broadcast equals a plain GEMM on the explicitly materialised input."""
+    rng = np.random.default_rng(12)
+    U, Ku, Kc, N, Mc = 6, 192, 64, 136, 901
+    Xu, Xc = int_bf16(rng, (U, Ku)), int_bf16(rng, (Mc, Kc))
+    W = int_bf16(rng, (Ku + Kc, N))
+    idx = rng.integers(0, U, Mc).astype(np.int32)
+    out = ptg.broadcast_gemm(dev_bf16(Xu), dev_bf16(Xc), dev(idx), dev_bf16(W), out_dtype=torch.float32)
+    Z = np.concatenate([Xu[idx], Xc], axis=1)
+    ref = ptg.gemm(dev_bf16(Z), dev_bf16(W), out_dtype=torch.float32)
+    assert torch.equal(out, ref)
+
+
+def test_broadcast_check_helper():
+    idx = torch.tensor([0, 1, 4, 2], dtype=torch.int32, device="cuda")
+    with pytest.raises(ptg.PtgError) as e:
+        ptg.broadcast_gemm_check(4, idx)
+    assert e.value.status == 5
+    ptg.broadcast_gemm_check(5, idx)
+
+
+def test_config4_ikbo_sampled():
+    """64 users (Xu 64 x 2048), 81403 candidates (Xc x 512), W 2560 x 1024, bf16 output and
+    its fp32 twin, on sampled rows including the first and last candidate of every user."""
+    w = wl.config4()
+    starts = np.concatenate([[0], np.cumsum(w.counts)])
+    rows = set(sample_rows(w.Mc, 64, 9).tolist()) | set(starts[:-1].tolist()) | set((starts[1:] - 1).tolist())
+    rows = np.array(sorted(rows), dtype=np.int64)
+    v = oracle.broadcast_gemm(w.Xu, w.Xc, w.idx, w.W, w.w_layout, rows=rows)
+    args = (dev_bf16(w.Xu), dev_bf16(w.Xc), dev(w.idx), dev_bf16(w.W))
+    idx = torch.from_numpy(rows).cuda()
+    for out_dtype in (torch.bfloat16, torch.float32):
+        out = ptg.broadcast_gemm(*args, out_dtype=out_dtype)
+        check(out[idx], v, w.Ku + w.Kc, f"config4 {out_dtype}")
+
+
+# ------------------------------------------------------------------------------------------
+# batch of independent problems
+# ------------------------------------------------------------------------------------------
+def run_batch(pl: wl.ProblemList, out_dtype, rows_per=None):
+    probs, outs = [], []
+    for p in pl.problems:
+        C = torch.empty((p.M, p.N), dtype=out_dtype, device="cuda")
+        probs.append((dev_bf16(p.A), dev_bf16(p.B), C, dev(p.bias)))
+        outs.append(C)
+    ptg.gemm_batch(probs, pl.epi)
+    vs = oracle.problem_list(pl.problems, pl.epi, rows_per)
+    return outs, vs
+
+
+@pytest.mark.parametrize("epi", [wl.EPI_NONE, wl.EPI_BIAS_SILU])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_batch_small(epi, out_dtype):
+    pl = wl.problem_list(51, 9, mmin=1, mmax=300, nk_choices=(8, 136, 256), epi=epi)
+    outs, vs = run_batch(pl, out_dtype)
+    for i, (o, v) in enumerate(zip(outs, vs)):
+        check(o, v, pl.problems[i].K, f"batch problem {i}")
+
+
+def test_batch_prepare_once_run_twice():
+    """The recorded batch can be re-run without re-preparing (no host work on run)."""
+    pl = wl.problem_list(52, 5, mmin=64, mmax=200)
+    probs, outs = [], []
+    for p in pl.problems:
+        C = torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
+        probs.append((dev_bf16(p.A), dev_bf16(p.B), C, dev(p.bias)))
+        outs.append(C)
+    ws = torch.empty(ptg.gemm_batch_workspace(len(probs)), dtype=torch.uint8, device="cuda")
+    ptg.gemm_batch_prepare(probs, pl.epi, ws)
+    ptg.gemm_batch_run(len(probs), ws, torch.float32, pl.epi)
+    first = [o.clone() for o in outs]
+    for o in outs:
+        o.zero_()
+    ptg.gemm_batch_run(len(probs), ws, torch.float32, pl.epi)
+    for a, b in zip(first, outs):
+        assert torch.equal(a, b)
+    vs = oracle.problem_list(pl.problems, pl.epi)
+    for i, (o, v) in enumerate(zip(outs, vs)):
+        check(o, v, pl.problems[i].K, f"problem {i}")
+
+
+def test_batch_each_equals_standalone_gemm():
+    pl = wl.problem_list(53, 6, mmin=1, mmax=700)
+    probs = []
+    for p in pl.problems:
+        probs.append((dev_bf16(p.A), dev_bf16(p.B), torch.empty((p.M, p.N), dtype=torch.float32,
+                      device="cuda"), dev(p.bias)))
+    ptg.gemm_batch(probs, pl.epi)
+    for A, B, C, bias in probs:
+        one = ptg.gemm(A, B, out_dtype=torch.float32, bias=bias, epi=pl.epi)
+        assert torch.allclose(C, one, rtol=0, atol=0) or torch.equal(C, one)
+
+
+def test_config5_recsys_batch_sampled():
+    """1024 problems (M ~ U{64..1024}, N, K in {128, 256, 512}) in one persistent launch with
+    the fused bias + SiLU epilogue; bf16 output and fp32 twin, sampled rows of every problem."""
+    pl = wl.config5()
+    rows_per = [sample_rows(p.M, 3, 100 + i) for i, p in enumerate(pl.problems)]
+    vs = oracle.problem_list(pl.problems, pl.epi, rows_per)
+    for out_dtype in (torch.bfloat16, torch.float32):
+        probs, outs = [], []
+        for p in pl.problems:
+            C = torch.empty((p.M, p.N), dtype=out_dtype, device="cuda")
+            probs.append((dev_bf16(p.A), dev_bf16(p.B), C, dev(p.bias)))
+            outs.append(C)
+        ptg.gemm_batch(probs, pl.epi)
+        for i, (o, v) in enumerate(zip(outs, vs)):
+            check(o[torch.from_numpy(rows_per[i]).cuda()], v, pl.problems[i].K, f"config5 problem {i}")

@@ -1,0 +1,117 @@
+"""GPU parity of the grouped (mixture-of-experts) GEMM against the fp64 CPU oracle.
+
+Expert row ranges come from device-resident int32 offsets with empty groups, groups
+smaller than a tile, and (at full size) the 64-expert Zipf(1.1) routing of the workload.
+Group bookkeeping is pinned bit-exactly with W_g = (g + 1) I.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pipelined_tiled_gemm_amd as ptg
+import workloads as wl
+from parity import check, dev, dev_bf16, exact, int_bf16, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _no_watchdog():
+    ptg.watchdog(clear=True)
+    yield
+    torch.cuda.synchronize()
+    assert ptg.watchdog(clear=True) == 0, "a pipeline wait timed out"
+
+
+def run_grouped(w: wl.Grouped, out_dtype, epi, rows=None):
+    out = ptg.grouped_gemm(dev_bf16(w.X), dev_bf16(w.W), dev(w.offsets), w_layout=w.w_layout,
+                           out_dtype=out_dtype, bias=dev(w.bias) if w.bias is not None else None,
+                           epi=epi)
+    v = oracle.grouped_gemm(w.X, w.W, w.w_layout, w.offsets, w.bias, epi, rows=rows)
+    return out, v
+
+
+COUNTS = np.array([300, 0, 1, 129, 0, 0, 64, 511, 2, 0])
+
+
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+@pytest.mark.parametrize("epi", [wl.EPI_NONE, wl.EPI_BIAS_SILU])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_grouped_small(layout, epi, out_dtype):
+    w = wl.grouped(31, len(COUNTS), int(COUNTS.sum()), 200, 136, w_layout=layout,
+                   with_bias=True, counts=COUNTS)
+    out, v = run_grouped(w, out_dtype, epi)
+    check(out, v, w.K, f"grouped layout={layout} epi={epi}")
+
+
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+def test_grouped_scaled_identity_pins_groups(layout):
+    """W_g = (g+1) I with integer X: row r must equal (g(r)+1) X[r] exactly."""
+    counts = np.array([5, 0, 130, 1, 0, 257, 3, 0])
+    G, K = len(counts), 128
+    M = int(counts.sum())
+    rng = np.random.default_rng(4)
+    X = int_bf16(rng, (M, K))
+    W = np.stack([wl.f32_to_bf16_bits((g + 1) * np.eye(K, dtype=np.float32)) for g in range(G)])
+    if layout == wl.B_NK:
+        W = np.ascontiguousarray(W.transpose(0, 2, 1))
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = ptg.grouped_gemm(dev_bf16(X), dev_bf16(W), dev(off), w_layout=layout, out_dtype=out_dtype)
+        grp = np.repeat(np.arange(G), counts)
+        exact(out, (grp[:, None] + 1) * wl.bf16_bits_to_f32(X).astype(np.float64), "scaled identity")
+
+
+def test_grouped_equals_per_group_gemm():
+    """Invariant: the grouped result equals a plain GEMM per expert (GPU against GPU)."""
+    rng = np.random.default_rng(6)
+    counts = np.array([77, 0, 256, 3, 190])
+    G, K, N = len(counts), 192, 264
+    M = int(counts.sum())
+    X = int_bf16(rng, (M, K))
+    W = int_bf16(rng, (G, K, N))
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    Xd, Wd = dev_bf16(X), dev_bf16(W)
+    out = ptg.grouped_gemm(Xd, Wd, dev(off), out_dtype=torch.float32)
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            one = ptg.gemm(Xd[lo:hi], Wd[g], out_dtype=torch.float32)
+            assert torch.equal(out[lo:hi], one)
+
+
+def test_grouped_single_group_is_dense():
+    w = wl.grouped(8, 1, 333, 136, 200, counts=np.array([333]))
+    out, v = run_grouped(w, torch.float32, wl.EPI_NONE)
+    dense = ptg.gemm(dev_bf16(w.X), dev_bf16(w.W[0]), out_dtype=torch.float32)
+    check(out, v, w.K, "single group")
+    assert torch.equal(out, dense)
+
+
+def test_grouped_check_helper():
+    off = torch.tensor([0, 3, 2, 5], dtype=torch.int32, device="cuda")
+    with pytest.raises(ptg.PtgError) as e:
+        ptg.grouped_gemm_check(off, 5)
+    assert e.value.status == 5
+    ptg.grouped_gemm_check(torch.tensor([0, 2, 2, 5], dtype=torch.int32, device="cuda"), 5)
+
+
+@pytest.mark.parametrize("reading", ["rank", "sampled"])
+def test_config3_moe_sampled(reading):
+    """64 experts, 16384 rows (Zipf(1.1) routing), K = 4096, N = 1536; bf16 output and the
+    fp32 twin on sampled rows: first and last row of every live group plus random rows."""
+    w = wl.config3(reading)
+    rows = set(sample_rows(w.M_total, 64, 7).tolist())
+    for g in range(w.G):
+        if w.counts[g] > 0:
+            rows |= {int(w.offsets[g]), int(w.offsets[g + 1]) - 1}
+    rows = np.array(sorted(rows), dtype=np.int64)
+    v = oracle.grouped_gemm(w.X, w.W, w.w_layout, w.offsets, rows=rows)
+    X, W, off = dev_bf16(w.X), dev_bf16(w.W), dev(w.offsets)
+    idx = torch.from_numpy(rows).cuda()
+    for out_dtype in (torch.bfloat16, torch.float32):
+        out = ptg.grouped_gemm(X, W, off, out_dtype=out_dtype)
+        check(out[idx], v, w.K, f"config3 {reading} {out_dtype}")

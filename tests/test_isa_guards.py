@@ -1,0 +1,80 @@
+"""Checks on the gfx950 assembly of the kernels (CPU only: hipcc cross-compiles).
+
+- Every buffer-to-LDS DMA takes a zero scalar offset.  The k-step offset is carried by the
+  descriptor base: gfx950 buffer-to-LDS loads are not used with a nonzero scalar offset,
+  and a kernel that used one faulted (its DMAs wrote outside their ring slots and reached
+  the tile metadata that holds the output pointer).
+- No kernel spills to scratch, and none needs a waterfall loop around a DMA (a descriptor
+  or offset the compiler believes divergent).
+- No scalar sign-extension of a 32-bit word into 64 bits (s_bfe_i64 with width 32).  A
+  buffer-descriptor helper once rebuilt a pointer from two readfirstlane results, whose
+  signed int type sign-extended the low word into the high word whenever bit 31 of the
+  address was set: the descriptor base became 0xffff'xxxx'xxxx and the first access faulted.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from pipelined_tiled_gemm_amd import build
+
+hipcc_missing = shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "k.s"
+    cmd = [build.hipcc(), *build.compile_flags(), "-S", "--cuda-device-only",
+           os.path.join(build.CSRC, "ptg_kernels.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def kernels(asm_text):
+    for m in re.finditer(r"\n(_ZN3ptg10ptg_kernel\S+):", asm_text):
+        start = m.start()
+        end = asm_text.index(".Lfunc_end", start)
+        yield m.group(1), asm_text[start:end].split("\n")
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_lds_dma_scalar_offset_is_zero(asm):
+    n = 0
+    for name, body in kernels(asm):
+        for line in body:
+            if "buffer_load_dword" in line and " lds" in line:
+                ops = line.split(None, 1)[1].split(",")
+                assert ops[2].strip().split()[0] == "0", f"{name}: {line.strip()}"
+                n += 1
+    assert n > 0
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_no_scratch_and_no_waterfall(asm):
+    for name, body in kernels(asm):
+        assert not any("scratch_" in l for l in body), f"{name} spills to scratch"
+        for k, line in enumerate(body):
+            if "buffer_load_dword" in line and " lds" in line:
+                assert "saveexec" not in body[k - 1], f"{name}: waterfall loop around a DMA"
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_no_sign_extended_address_words(asm):
+    for name, body in kernels(asm):
+        for line in body:
+            if line.strip().startswith("s_bfe_i64") and line.strip().endswith("0x200000"):
+                raise AssertionError(f"{name}: sign-extends a 32-bit word: {line.strip()}")
+
+
+def test_promotion_rule_behind_the_guard():
+    """The C rule the guard is about: an int OR-ed into a uint64_t is sign-extended, so a
+    low address word with bit 31 set turns the high word into 0xffffffff."""
+    lo_bits, hi = 0x9ABC0000, 0x00007F12
+    as_int = lo_bits - (1 << 32) if lo_bits & (1 << 31) else lo_bits   # readfirstlane's int
+    sign_extended = as_int & ((1 << 64) - 1)                              # int -> uint64_t
+    wrong = (hi << 32) | sign_extended
+    right = (hi << 32) | (as_int & 0xFFFFFFFF)                           # via uint32_t
+    assert wrong >> 32 == 0xFFFFFFFF
+    assert right == 0x00007F12_9ABC0000
