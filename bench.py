@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Throughput of the pipelined tiled GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+
+A step is one call of the pipelined GEMM on the headline workload: C = A.B with
+M = N = K = 8192, A row-major bf16, B stored transposed (N x K) bf16, entries N(0,1)/sqrt(K),
+fp32 accumulation, bf16 output (seeded synthetic data, resident in HBM before timing).
+W untimed steps, then exactly K timed steps between two device synchronisations; one JSON
+line is printed.
+
+value            whole-job TFLOP/s over the timed steps (algorithmic 2 M N K flops per step)
+roofline         the GEMM kernel against MI355X's dense bf16 MFMA peak (2500 TFLOP/s); its
+                 duration comes from HIP events recorded on the stream the library launches
+                 on; `traffic` is the HBM bytes per launch measured by rocprofv3 counters when
+                 a summary for the current kernel sources exists under profiles/, else null
+cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload (some output
+                 rows), on all host cores it uses, in the same unit
+secondary        grouped (mixture-of-experts), broadcast and batched workloads, timed the
+                 same way (TFLOP/s, % of peak, GB/s of compulsory traffic)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % of MI355X bf16 MFMA peak (dense, grouped, broadcast GEMM)"
+PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_8192_nk_bf16.txt")
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "pipelined_tiled_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches the sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_dev(bits, torch, np):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Untimed warmup, then `steps` calls between device synchronisations.
+    Returns (wall seconds per call, event milliseconds per call on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, e0.elapsed_time(e1) / steps
+
+
+def secondary(torch, np, ptg, wl, steps):
+    out = {}
+    # grouped: 64 experts, 16384 rows, K=4096, N=1536, rank-Zipf(1.1) routing
+    w = wl.config3("rank")
+    X, W, off = to_dev(w.X, torch, np), to_dev(w.W, torch, np), torch.from_numpy(w.offsets).cuda()
+    Y = torch.empty((w.M_total, w.N), dtype=torch.bfloat16, device="cuda")
+    _, ms = time_calls(lambda: ptg.grouped_gemm(X, W, off, out=Y), steps, 3, torch)
+    f, b = wl.grouped_flops(w), wl.grouped_bytes(w)
+    out["grouped_moe_64x16384x4096x1536"] = {
+        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS}
+    del X, W, off, Y, w
+    # broadcast: 64 users, sum C_u = 81403 candidates, [2048 | 512] -> 1024
+    w = wl.config4()
+    Xu, Xc, idx, W = (to_dev(w.Xu, torch, np), to_dev(w.Xc, torch, np),
+                      torch.from_numpy(w.idx).cuda(), to_dev(w.W, torch, np))
+    Y = torch.empty((w.Mc, w.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ptg.broadcast_gemm_workspace(w.U, w.N), dtype=torch.uint8, device="cuda")
+    _, ms = time_calls(lambda: ptg.broadcast_gemm(Xu, Xc, idx, W, out=Y, workspace=ws), steps, 3, torch)
+    f, fm, b = wl.broadcast_flops(w), wl.broadcast_flops_materialised(w), wl.broadcast_bytes(w)
+    out["broadcast_ikbo_64users_81403cand"] = {
+        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
+        "effective_tflops_materialised_equivalent": fm / ms / 1e9,
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS}
+    del Xu, Xc, idx, W, Y, ws, w
+    # batch: 1024 independent GEMMs with fused bias + SiLU, one persistent launch
+    pl = wl.config5()
+    probs = []
+    for p in pl.problems:
+        probs.append((to_dev(p.A, torch, np), to_dev(p.B, torch, np),
+                      torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda"),
+                      torch.from_numpy(p.bias).cuda()))
+    ws = torch.empty(ptg.gemm_batch_workspace(len(probs)), dtype=torch.uint8, device="cuda")
+    ptg.gemm_batch_prepare(probs, pl.epi, ws)
+    _, ms = time_calls(lambda: ptg.gemm_batch_run(len(probs), ws, torch.bfloat16, pl.epi), steps, 3, torch)
+    f, b = wl.problem_list_flops(pl), wl.problem_list_bytes(pl)
+    out["batch_recsys_1024_bias_silu"] = {
+        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS}
+    return out
+
+
+def cpu_baseline(w, np, budget_s=15.0):
+    """The oracle, untuned, on a bounded sample of output rows of the headline GEMM."""
+    import oracle
+    oracle.build(force=False)
+    M, N, K = w.M, w.N, w.K
+    t0 = time.perf_counter()
+    oracle.gemm(w.A, w.B, w.b_layout, rows=np.arange(8))
+    dt = time.perf_counter() - t0
+    rows = int(max(8, min(M, 8 * budget_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm(w.A, w.B, w.b_layout, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of {M} output rows (all {N} columns) of the {M}x{N}x{K} GEMM, "
+                      f"fp64 on the same bf16 inputs, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import pipelined_tiled_gemm_amd as ptg
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.config2()
+    A, B = to_dev(w.A, torch, np), to_dev(w.B, torch, np)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    flops = wl.dense_flops(w.M, w.N, w.K)
+    ptg.watchdog(clear=True)
+    step = lambda: ptg.gemm(A, B, b_layout=wl.B_NK, out=C)  # noqa: E731
+    wall_s, ev_ms = time_calls(step, args.steps, args.warmup, torch)
+    if ptg.watchdog(clear=True) != 0:
+        raise RuntimeError("a pipeline wait timed out during the benchmark")
+    value = flops / wall_s / 1e12
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    cfg = ptg.describe_config(w.M, w.N, w.K, wl.B_NK)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense GEMM M=N=K=8192, A row-major, B stored N x K, bf16 inputs "
+                               "N(0,1)/sqrt(K), fp32 accumulation, bf16 output",
+                   "M": w.M, "N": w.N, "K": w.K, "tile": cfg, "pct_peak": round(100 * value / PEAK_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(), "kernel_ms": round(ev_ms, 4)},
+    }
+    del A, B, C
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        line["secondary"] = secondary(torch, np, ptg, wl, max(5, args.steps // 2))
+        if ptg.watchdog(clear=True) != 0:
+            raise RuntimeError("a pipeline wait timed out during the secondary workloads")
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, np)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -221,6 +221,14 @@ ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, pt
     auto* rec = reinterpret_cast<ptg::BatchProblem*>(host.data() + sizeof(ptg::BatchHeader) +
                                                      ptg::batch_prefix_bytes(count));
     int64_t total = 0;
+    ptg::Guards& gu = hdr->guard;
+    gu.a_lo = gu.b_lo = gu.c_lo = gu.bias_lo = UINT64_MAX;
+    gu.a_hi = gu.b_hi = gu.c_hi = gu.bias_hi = 0;
+    auto widen = [](uint64_t& lo, uint64_t& hi, const void* p, uint64_t bytes) {
+      const uint64_t a = reinterpret_cast<uint64_t>(p);
+      if (a < lo) lo = a;
+      if (a + bytes > hi) hi = a + bytes;
+    };
     for (int32_t p = 0; p < count; ++p) {
       const ptg_problem& q = problems[p];
       ptg_status st = validate_problem(fn, p, q, epi);
@@ -232,11 +240,21 @@ ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, pt
       const bool empty = q.M == 0 || q.N == 0;
       r.tiles_m = empty ? 0 : (int32_t)((q.M + ptg::kBatchBM - 1) / ptg::kBatchBM);
       r.tiles_n = empty ? 0 : (int32_t)((q.N + ptg::kBatchBN - 1) / ptg::kBatchBN);
+      if (!empty) {
+        widen(gu.a_lo, gu.a_hi, q.A, (uint64_t)(((q.M - 1) * q.lda + q.K) * 2));
+        widen(gu.b_lo, gu.b_hi, q.B, (uint64_t)(((q.K - 1) * q.ldb + q.N) * 2));
+        widen(gu.c_lo, gu.c_hi, q.C, (uint64_t)(((q.M - 1) * q.ldc + q.N) * 4));
+        if (r.bias) widen(gu.bias_lo, gu.bias_hi, r.bias, (uint64_t)q.N * 4);
+      }
       pre[p] = (int32_t)total;
       total += (int64_t)r.tiles_m * r.tiles_n;
       if (total >= ((int64_t)1 << 31)) return fail(PTG_ERR_UNSUPPORTED, "%s: too many tiles", fn);
     }
     pre[count] = (int32_t)total;
+    if (gu.a_lo > gu.a_hi) gu.a_lo = gu.a_hi = 0;
+    if (gu.b_lo > gu.b_hi) gu.b_lo = gu.b_hi = 0;
+    if (gu.c_lo > gu.c_hi) gu.c_lo = gu.c_hi = 0;
+    if (gu.bias_lo > gu.bias_hi) gu.bias_lo = gu.bias_hi = 0;
     hdr->magic = ptg::kBatchMagic;
     hdr->count = count;
     hdr->total_tiles = (int32_t)total;

@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ptg_launch.h"
+
 namespace ptg {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -149,6 +151,13 @@ struct TileSrc {
   TileInfo info;
 };
 
+// Every descriptor a workgroup builds must lie inside the range (Guards, ptg_launch.h) of
+// its operand; one that does not (never the case in a working pipeline) aborts the
+// workgroup before any access.
+__device__ __forceinline__ bool inside(uint64_t p, uint64_t bytes, uint64_t lo, uint64_t hi) {
+  return p >= lo && p <= hi && bytes <= hi - p;
+}
+
 // ---------------------------------------------------------------------------------------
 // Small device helpers
 // ---------------------------------------------------------------------------------------
@@ -187,7 +196,8 @@ __device__ __forceinline__ void lds_bump(uint32_t* p) {
 extern __device__ uint32_t g_watchdog;
 
 // Stop the workgroup: raise its abort word (every wait returns at once) and record `why`
-// in the device watchdog word (1: a wait timed out, 2: inconsistent tile metadata).
+// in the device watchdog word (1: a wait timed out, 2: inconsistent tile metadata, 4: a DMA
+// source outside its operand, 8: an epilogue access outside its operand).
 __device__ __forceinline__ void raise_abort(uint32_t* abort, uint32_t why) {
   if (lane_id() == 0) {
     const uint32_t one = 1;
@@ -276,7 +286,7 @@ __device__ __forceinline__ void chunk_of(int i, int lane, int& row, int& chunk) 
 template <class C, class S>
 __device__ __forceinline__ void producer_role(const typename S::Args& args, char* ring, TileInfo* info,
                                               uint32_t* full, uint32_t* empty, uint32_t* abort, int pid,
-                                              char* sched_lds) {
+                                              char* sched_lds, const Guards& gd) {
   static_assert(C::A_INSTR % C::LOADS == 0, "each producer copies either A or B chunks");
   const int lane = lane_id();
   const int i0 = pid * C::LOADS;
@@ -304,6 +314,11 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
         src_bytes = C::B_KN ? (uint32_t)((int64_t)(K - 1) * t.ldb * 2 + (int64_t)t.info.n_cols * 2)
                             : (uint32_t)((int64_t)(t.info.n_cols - 1) * t.ldb * 2 + (int64_t)K * 2);
         if (C::B_KN) k_stride = t.ldb * 2;
+      }
+      if (!inside(reinterpret_cast<uint64_t>(src), src_bytes, opA ? gd.a_lo : gd.b_lo,
+                  opA ? gd.a_hi : gd.b_hi)) {
+        raise_abort(abort, 4u);
+        src_bytes = 0;  // every copy of this tile is out of range: nothing is read
       }
 #pragma unroll
       for (int q = 0; q < C::LOADS; ++q) {
@@ -439,7 +454,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], int 
 
 template <class C>
 __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, uint32_t* full, uint32_t* empty,
-                                              uint32_t* abort, int cw, int epi, bool f32out) {
+                                              uint32_t* abort, int cw, int epi, bool f32out,
+                                              const Guards& gd) {
   const int lane = lane_id();
   const int wm = cw / C::WN, wn = cw % C::WN;
   // A-fragment addressing: lane l holds row (l % 32) of a 32-row block and k-chunk l / 32.
@@ -558,6 +574,15 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
       raise_abort(abort, 2u);
       break;
     }
+    const uint64_t c_bytes = (uint64_t)((m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
+    const bool do_bias = (epi == EPI_BIAS || epi == EPI_BIAS_SILU) && biasp != 0;
+    if (!inside(Cp, c_bytes, gd.c_lo, gd.c_hi) ||
+        (do_bias && !inside(biasp, (uint64_t)n_cols * 4, gd.bias_lo, gd.bias_hi)) ||
+        (gidxp != 0 && (!inside(gidxp, (uint64_t)m_rows * 4, gd.gidx_lo, gd.gidx_hi) ||
+                        !inside(Pp, p_bytes, gd.p_lo, gd.p_hi)))) {
+      raise_abort(abort, 8u);
+      break;
+    }
     epilogue<C>(acc, wm, wn, m_rows, n_cols, Cp, ldc, biasp, gidxp, Pp, ldp, p_bytes, epi, f32out);
   }
 }
@@ -580,11 +605,12 @@ __global__ __launch_bounds__(C::NT, 1) void ptg_kernel(typename S::Args args) {
   S::template init<C>(args, sched_lds);  // cooperative; the barrier below publishes it
   __syncthreads();
   const int wave = threadIdx.x >> 6;
+  const Guards gd = S::guards(args);
   if (wave < C::NCONS) {
     __builtin_amdgcn_s_setprio(1);
-    consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0);
+    consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, gd);
   } else {
-    producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds);
+    producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, gd);
   }
 }
 

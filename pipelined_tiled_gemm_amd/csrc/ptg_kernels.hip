@@ -12,6 +12,7 @@
 //             stage of the linear-compression kernel).
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <mutex>
 #include <vector>
 
@@ -45,7 +46,9 @@ struct DenseSched {
     int32_t M, N, K;
     int32_t tiles_m, tiles_n, group_m;
     int32_t epi, out_f32, out_bytes;
+    Guards guard;
   };
+  __device__ static Guards guards(const Args& a) { return a.guard; }
   static constexpr int LDS_BYTES = 16;
 
   template <class C>
@@ -145,7 +148,9 @@ struct GroupedSched {
     int64_t M_total;
     int32_t G, N, K, tiles_n;
     int32_t epi, out_f32, out_bytes;
+    Guards guard;
   };
+  __device__ static Guards guards(const Args& a) { return a.guard; }
   // offsets[G + 1], tile prefix[G + 1], scan scratch
   static constexpr int LDS_BYTES = 2 * (kMaxGroups + 1) * 4 + 20 * 4;
 
@@ -209,7 +214,9 @@ struct BatchSched {
     const BatchProblem* probs;    // [count]
     int32_t count;
     int32_t epi, out_f32, out_bytes;
+    const Guards* guard_ptr;
   };
+  __device__ static Guards guards(const Args& a) { return *a.guard_ptr; }
   static constexpr int LDS_BYTES = (kMaxBatch + 1) * 4 + 16;
 
   template <class C>
@@ -275,6 +282,19 @@ static int device_cus() {
   return cache[dev];
 }
 
+static uint64_t addr(const void* p) { return reinterpret_cast<uint64_t>(p); }
+
+// [p, p + bytes), or the empty range [0, 0) when p is null.
+static void span(const void* p, uint64_t bytes, uint64_t& lo, uint64_t& hi) {
+  lo = p ? addr(p) : 0;
+  hi = p ? addr(p) + bytes : 0;
+}
+
+// Bytes of a row-major [rows x cols] matrix with row stride ld (elements of `esize` bytes).
+static uint64_t mat_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+  return rows > 0 ? (uint64_t)(((rows - 1) * ld + cols) * esize) : 0;
+}
+
 template <class C, class S>
 static hipError_t launch_persistent(const typename S::Args& a, int64_t max_tiles, hipStream_t stream) {
   const int cus = device_cus();
@@ -320,6 +340,13 @@ static hipError_t launch_dense_cfg(const DenseLaunch& d, hipStream_t stream) {
   a.tiles_n = (int32_t)((d.N + C::BN - 1) / C::BN);
   a.group_m = 4;
   a.epi = d.epi; a.out_f32 = d.out_f32; a.out_bytes = d.out_f32 ? 4 : 2;
+  Guards& g = a.guard;
+  span(d.A, mat_bytes(d.M, d.K, d.lda, 2), g.a_lo, g.a_hi);
+  span(d.B, d.b_kn ? mat_bytes(d.K, d.N, d.ldb, 2) : mat_bytes(d.N, d.K, d.ldb, 2), g.b_lo, g.b_hi);
+  span(d.C, mat_bytes(d.M, d.N, d.ldc, a.out_bytes), g.c_lo, g.c_hi);
+  span(d.bias, (uint64_t)d.N * 4, g.bias_lo, g.bias_hi);
+  span(d.gidx, (uint64_t)d.M * 4, g.gidx_lo, g.gidx_hi);
+  span(d.P, mat_bytes(d.p_rows, d.ldp, d.ldp, 4), g.p_lo, g.p_hi);
   return launch_persistent<C, DenseSched>(a, (int64_t)a.tiles_m * a.tiles_n, stream);
 }
 
@@ -343,6 +370,12 @@ static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream)
   a.G = g.G; a.N = (int32_t)g.N; a.K = (int32_t)g.K;
   a.tiles_n = (int32_t)((g.N + C::BN - 1) / C::BN);
   a.epi = g.epi; a.out_f32 = g.out_f32; a.out_bytes = g.out_f32 ? 4 : 2;
+  Guards& gd = a.guard;
+  gd = Guards{};
+  span(g.X, (uint64_t)g.M_total * g.K * 2, gd.a_lo, gd.a_hi);
+  span(g.W, (uint64_t)g.G * g.K * g.N * 2, gd.b_lo, gd.b_hi);
+  span(g.Y, (uint64_t)g.M_total * g.N * a.out_bytes, gd.c_lo, gd.c_hi);
+  span(g.bias, (uint64_t)g.G * g.N * 4, gd.bias_lo, gd.bias_hi);
   // every group adds at most one partial m-tile
   const int64_t max_tiles = ((g.M_total + C::BM - 1) / C::BM + g.G) * a.tiles_n;
   return launch_persistent<C, GroupedSched>(a, max_tiles, stream);
@@ -362,6 +395,9 @@ hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream) {
   a.probs = reinterpret_cast<const BatchProblem*>(ws + sizeof(BatchHeader) + batch_prefix_bytes(b.count));
   a.count = b.count;
   a.epi = b.epi; a.out_f32 = b.out_f32; a.out_bytes = b.out_f32 ? 4 : 2;
+  // The problems' pointers come from the host-validated table that prepare wrote, together
+  // with the union of their address ranges (read by the kernel from the header).
+  a.guard_ptr = reinterpret_cast<const Guards*>(ws + offsetof(BatchHeader, guard));
   // the tile count lives on the device: launch one workgroup per CU, idle ones exit at once
   return launch_persistent<C, BatchSched>(a, (int64_t)1 << 30, stream);
 }

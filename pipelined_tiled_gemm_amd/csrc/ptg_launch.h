@@ -46,6 +46,14 @@ struct BatchProblem {
 };
 static_assert(sizeof(BatchProblem) == 80, "BatchProblem layout");
 
+// Address ranges [lo, hi) a kernel may touch, derived by the host from validated arguments
+// (see the kernel's range checks).
+struct Guards {
+  uint64_t a_lo, a_hi, b_lo, b_hi;      // DMA sources
+  uint64_t c_lo, c_hi;                  // output
+  uint64_t bias_lo, bias_hi, gidx_lo, gidx_hi, p_lo, p_hi;  // epilogue operands
+};
+
 // Workspace layout of a batch: [header 256 B][prefix int32 (count + 1), padded to 256 B][problems].
 struct BatchHeader {
   int32_t magic;
@@ -53,7 +61,9 @@ struct BatchHeader {
   int32_t total_tiles;
   int32_t bm, bn;
   int32_t epi;
-  int32_t reserved[58];
+  int32_t reserved0[2];
+  Guards guard;                 // union of the problems' operand ranges
+  int32_t reserved[32];
 };
 static_assert(sizeof(BatchHeader) == 256, "BatchHeader layout");
 constexpr int32_t kBatchMagic = 0x50544742;  // "PTGB"
