@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -200,6 +202,15 @@ def main():
     }
     del A, B, C
     torch.cuda.empty_cache()
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = 1 << 30
+        del src, dst
+        torch.cuda.empty_cache()
     if not args.no_secondary:
         line["secondary"] = secondary(torch, np, ptg, wl, max(5, args.steps // 2))
         if ptg.watchdog(clear=True) != 0:
