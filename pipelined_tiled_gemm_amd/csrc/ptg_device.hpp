@@ -13,8 +13,9 @@
 //     s = g mod STAGES holds k-step g; "full[s]" counts producer arrivals and "empty[s]"
 //     counts consumer releases.  A producer never refills a slot before every consumer has
 //     released it, and a consumer never reads a slot before every producer has filled it
-//     (the page's multistage-buffer rule; "TLX in Production" reading notes on the same
-//     listing).  Counters only grow, so no phase bit is needed.
+//     (the multistage-buffer rule; the yuxiaoba.github.io reading notes on the post, section
+//     "Tensor expressions with explicit handoffs").  Counters only grow, so no phase bit is
+//     needed.
 //   - Consumer waves read operand fragments with ds_read_b128 (K-contiguous tiles) or the
 //     transposing ds_read_b64_tr_b16 (N-contiguous tiles), issue v_mfma_f32_32x32x16_bf16
 //     into fp32 accumulators held in registers, release the slot as soon as the last
