@@ -9,7 +9,7 @@
 #include <exception>
 #include <vector>
 
-#include "../../include/ptg.h"
+#include "ptg.h"
 #include "ptg_launch.h"
 
 namespace {

@@ -75,6 +75,9 @@ struct Cfg {
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // 1 KB per DMA
   static constexpr int LOADS = (A_INSTR + B_INSTR) / NPROD;  // DMAs per producer per k-step
+  // k-steps a producer keeps in flight before it waits for the oldest to land (bounded by
+  // the ring and by the 6-bit vector-memory counter)
+  static constexpr int INFLIGHT = (STAGES < 63 / LOADS) ? STAGES : 63 / LOADS;
   static constexpr int CPR_A = BK / 8;                  // 16-byte chunks per A row
   static constexpr int CPR_B = B_KN ? BN / 8 : BK / 8;  // 16-byte chunks per B row
   // Tile-metadata slots.  The producer rewrites slot j mod NINFO when it starts tile
@@ -87,8 +90,9 @@ struct Cfg {
   static_assert(BK % 16 == 0 && (BK == 32 || BK == 64), "BK must be 32 or 64");
   static_assert((A_INSTR + B_INSTR) % NPROD == 0, "DMAs must split evenly over producers");
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles must be whole KB");
-  static_assert(LOADS <= 31, "two k-steps of DMAs must fit the vector-memory counter");
-  static_assert(STAGES >= 2, "the producer signals a step after issuing the next one");
+  static_assert(LOADS <= 63, "one k-step of DMAs must fit the vector-memory counter");
+  static_assert(STAGES >= 2, "the ring needs at least two slots");
+  static_assert(INFLIGHT >= 1 && INFLIGHT <= STAGES, "in-flight steps are bounded by the ring");
   static_assert(NT <= 1024, "workgroup too large");
 };
 
@@ -287,13 +291,14 @@ __device__ __forceinline__ void chunk_of(int i, int lane, int& row, int& chunk) 
 template <class C, class S>
 __device__ __forceinline__ void producer_role(const typename S::Args& args, char* ring, TileInfo* info,
                                               uint32_t* full, uint32_t* empty, uint32_t* abort, int pid,
-                                              char* sched_lds, const Guards& gd) {
+                                              char* sched_lds, const Guards* guards) {
   static_assert(C::A_INSTR % C::LOADS == 0, "each producer copies either A or B chunks");
   const int lane = lane_id();
   const int i0 = pid * C::LOADS;
   const bool opA = i0 < C::A_INSTR;                 // this producer's operand
   const int lds_base = opA ? i0 * 1024 : C::A_BYTES + (i0 - C::A_INSTR) * 1024;
-  uint32_t g = 0;  // k-steps issued by this workgroup so far (all tiles)
+  uint32_t g = 0;         // k-steps issued by this workgroup so far (all tiles)
+  uint32_t next_sig = 0;  // oldest k-step whose "full" has not been signalled
   for (int j = 0;; ++j) {
     TileSrc t = {};
     const bool has = S::template tile<C>(args, j, t, sched_lds);
@@ -316,8 +321,9 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
                             : (uint32_t)((int64_t)(t.info.n_cols - 1) * t.ldb * 2 + (int64_t)K * 2);
         if (C::B_KN) k_stride = t.ldb * 2;
       }
-      if (!inside(reinterpret_cast<uint64_t>(src), src_bytes, opA ? gd.a_lo : gd.b_lo,
-                  opA ? gd.a_hi : gd.b_hi)) {
+      const uint64_t lo = uni64(opA ? guards->a_lo : guards->b_lo);
+      const uint64_t hi = uni64(opA ? guards->a_hi : guards->b_hi);
+      if (!inside(reinterpret_cast<uint64_t>(src), src_bytes, lo, hi)) {
         raise_abort(abort, 4u);
         src_bytes = 0;  // every copy of this tile is out of range: nothing is read
       }
@@ -343,7 +349,14 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
     }
     for (int st = 0; st < nsteps; ++st, ++g) {
       const int s = g % C::STAGES;
-      wait_at_least(&empty[s], (uint32_t)C::NCONS * (g / C::STAGES), abort);
+      const uint32_t released = (uint32_t)C::NCONS * (g / C::STAGES);
+      if ((uint32_t)__builtin_amdgcn_readfirstlane(lds_peek(&empty[s])) < released) {
+        // The slot is still in use: before sleeping on it, hand every step in flight to the
+        // consumers as soon as it has landed, so that no step waits on a later issue.
+        wait_vmcnt<0>();
+        for (; next_sig < g; ++next_sig) lds_bump(&full[next_sig % C::STAGES]);
+        wait_at_least(&empty[s], released, abort);
+      }
       if (st == 0 && pid == 0 && lane == 0) {
         // publish this tile's metadata, or the end marker, in its info slot
         TileInfo ti = t.info;
@@ -374,19 +387,23 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
             dma16(rs, dst + q * 1024, k0 + kpos < t.info.K ? voff[q] : kOutOfRange, soff);
           }
         }
-        if (g > 0) {
-          wait_vmcnt<C::LOADS>();   // the previous k-step's copies have landed in LDS
-          lds_bump(&full[(g - 1) % C::STAGES]);
+        // Steps next_sig .. g are in flight.  With INFLIGHT of them outstanding, wait until the
+        // oldest has landed (the later ones may still be in flight: the vector-memory counter
+        // retires loads in order) and hand it to the consumers.
+        if (g + 1 - next_sig == (uint32_t)C::INFLIGHT) {
+          wait_vmcnt<(C::INFLIGHT - 1) * C::LOADS>();
+          lds_bump(&full[next_sig % C::STAGES]);
+          ++next_sig;
         }
-      } else if (g > 0) {
+      } else {
+        // the end marker: every step issued so far has landed, hand them all over
         wait_vmcnt<0>();
-        lds_bump(&full[(g - 1) % C::STAGES]);
+        for (; next_sig < g; ++next_sig) lds_bump(&full[next_sig % C::STAGES]);
       }
     }
     if (!has) break;
   }
-  // the end marker's step
-  wait_vmcnt<0>();
+  // the end marker's own step (it carries no data)
   lds_bump(&full[(g - 1) % C::STAGES]);
 }
 
@@ -456,7 +473,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], int 
 template <class C>
 __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, uint32_t* full, uint32_t* empty,
                                               uint32_t* abort, int cw, int epi, bool f32out,
-                                              const Guards& gd) {
+                                              const Guards* guards) {
   const int lane = lane_id();
   const int wm = cw / C::WN, wn = cw % C::WN;
   // A-fragment addressing: lane l holds row (l % 32) of a 32-row block and k-chunk l / 32.
@@ -466,25 +483,23 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
   const int a_chunk = (lane >> 5) ^ swz_k<C::CPR_A>(ra);
   const int a_base = ra * C::BK * 2;
   int b_base = 0, b_chunk = 0;
-  int b_kn[C::TN][2];  // KN: byte offset of each transposing read at sub-step 0
+  int b_kn[C::TN];  // KN: byte offset of the first transposing read of block tn at sub-step 0
   if constexpr (!C::B_KN) {
     const int rb = wn * C::WTN + (lane & 31);
     b_chunk = (lane >> 5) ^ swz_k<C::CPR_B>(rb);
     b_base = rb * C::BK * 2;
   } else {
     // Transposing read: in each 16-lane block, lane i fetches 4 bf16 of k-row (i / 4) at
-    // columns 4 (i % 4) .. +3; the hardware hands lane i the 4 k-values of column i.
-    // Sub-step kk adds 16 k-rows, a multiple of 4, so the swizzle (a function of k mod 4)
-    // and hence the offset within a row do not change with kk.
+    // columns 4 (i % 4) .. +3; the hardware hands lane i the 4 k-values of column i.  The
+    // second read of a fragment is 4 k-rows further down, and sub-step kk adds 16 k-rows:
+    // both multiples of 4, so the swizzle (a function of k mod 4), hence the offset within
+    // a row, is unchanged and both become immediate offsets.
     const int blk = lane >> 4, i = lane & 15;
+    const int k = (blk >> 1) * 8 + (i >> 2);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = (blk >> 1) * 8 + h * 4 + (i >> 2);
-#pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) {
-        const int n = wn * C::WTN + tn * 32 + (blk & 1) * 16 + (i & 3) * 4;
-        b_kn[tn][h] = k * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(k)) << 4) + ((n >> 2) & 1) * 8;
-      }
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int n = wn * C::WTN + tn * 32 + (blk & 1) * 16 + (i & 3) * 4;
+      b_kn[tn] = k * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(k)) << 4) + ((n >> 2) & 1) * 8;
     }
   }
 
@@ -511,51 +526,80 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
 #pragma unroll
       for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = f32x16{};
 
+    // Fragment loads of one 16-deep sub-step kk of a staged slot.
+    auto load_a = [&](const char* slot, int kk, int tm) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(slot + a_base + (((kk * 2) ^ a_chunk) << 4) +
+                                              tm * 32 * C::BK * 2);
+    };
+    auto load_b = [&](const char* slot, int kk, int tn) -> bf16x8 {
+      const char* slotB = slot + C::A_BYTES;
+      if constexpr (!C::B_KN) {
+        return *reinterpret_cast<const bf16x8*>(slotB + b_base + (((kk * 2) ^ b_chunk) << 4) +
+                                                tn * 32 * C::BK * 2);
+      } else {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(slotB + b_kn[tn] + kk * 16 * C::BN * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(slotB + b_kn[tn] + (kk * 16 + 4) * C::BN * 2));
+        typedef __attribute__((ext_vector_type(8))) short i16x8;
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+
+    // Rolling prefetch: each fragment register is refilled with the next sub-step's
+    // fragment right after its last MFMA of the current sub-step, so LDS latency hides
+    // behind the remaining MFMAs.  MFMAs run B-column-major: b[tn] is free after TM MFMAs,
+    // every a[tm] after the last column.
+    bf16x8 a[C::TM], b[C::TN];
+    {
+      const char* slot0 = ring + s0 * C::STAGE_BYTES;
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) b[tn] = load_b(slot0, 0, tn);
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm) a[tm] = load_a(slot0, 0, tm);
+    }
     for (int st = 0; st < nsteps; ++st, ++g) {
       const int s = g % C::STAGES;
-      if (st > 0) wait_at_least(&full[s], (uint32_t)C::NPROD * (g / C::STAGES + 1), abort);
       const char* slot = ring + s * C::STAGE_BYTES;
-      const char* slotB = slot + C::A_BYTES;
+      const bool more_steps = st + 1 < nsteps;
+      const int sn = (g + 1) % C::STAGES;
+      const char* next_slot = ring + sn * C::STAGE_BYTES;
 #pragma unroll
       for (int kk = 0; kk < C::KSUB; ++kk) {
-        // Fragments of one 16-deep sub-step: B first, so the first MFMAs can start while
-        // the later A rows are still in flight.
-        bf16x8 a[C::TM], b[C::TN];
-        if constexpr (!C::B_KN) {
-          const char* pb = slotB + b_base + (((kk * 2) ^ b_chunk) << 4);
-#pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn)
-            b[tn] = *reinterpret_cast<const bf16x8*>(pb + tn * 32 * C::BK * 2);
-        } else {
-#pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn) {
-            i16x4 hv[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_i16x4*)(slotB + b_kn[tn][h] + kk * 16 * C::BN * 2));
-            typedef __attribute__((ext_vector_type(8))) short i16x8;
-            const i16x8 v = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            b[tn] = __builtin_bit_cast(bf16x8, v);
-          }
-        }
-        const char* pa = slot + a_base + (((kk * 2) ^ a_chunk) << 4);
-#pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm)
-          a[tm] = *reinterpret_cast<const bf16x8*>(pa + tm * 32 * C::BK * 2);
-        if (kk == C::KSUB - 1) {
-          // every fragment of this k-step is in registers: hand the slot back
+        const bool last_kk = kk == C::KSUB - 1;
+        const bool more = !last_kk || more_steps;     // a sub-step follows in this tile
+        const char* nslot = last_kk ? next_slot : slot;
+        const int nkk = last_kk ? 0 : kk + 1;
+        bool ready = !last_kk;                        // the next slot's data is known present
+        if (last_kk) {
+          // this sub-step's fragments (the last reads of slot s) are in registers
           wait_lgkm0();
           lds_bump(&empty[s]);
         }
-#pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
-        // keep each sub-step's loads next to its MFMAs: the register budget has no room for
-        // a second set of fragments; the other consumer wave on the SIMD hides the latency
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm) {
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+            if (tn == C::TN - 1 && more) {
+              if (!ready) {
+                wait_at_least(&full[sn], (uint32_t)C::NPROD * ((g + 1) / C::STAGES + 1), abort);
+                ready = true;
+              }
+              a[tm] = load_a(nslot, nkk, tm);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (more) {
+            if (!ready) {
+              wait_at_least(&full[sn], (uint32_t)C::NPROD * ((g + 1) / C::STAGES + 1), abort);
+              ready = true;
+            }
+            b[tn] = load_b(nslot, nkk, tn);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
 
@@ -577,10 +621,11 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
     }
     const uint64_t c_bytes = (uint64_t)((m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
     const bool do_bias = (epi == EPI_BIAS || epi == EPI_BIAS_SILU) && biasp != 0;
-    if (!inside(Cp, c_bytes, gd.c_lo, gd.c_hi) ||
-        (do_bias && !inside(biasp, (uint64_t)n_cols * 4, gd.bias_lo, gd.bias_hi)) ||
-        (gidxp != 0 && (!inside(gidxp, (uint64_t)m_rows * 4, gd.gidx_lo, gd.gidx_hi) ||
-                        !inside(Pp, p_bytes, gd.p_lo, gd.p_hi)))) {
+    const Guards& gd = *guards;
+    if (!inside(Cp, c_bytes, uni64(gd.c_lo), uni64(gd.c_hi)) ||
+        (do_bias && !inside(biasp, (uint64_t)n_cols * 4, uni64(gd.bias_lo), uni64(gd.bias_hi))) ||
+        (gidxp != 0 && (!inside(gidxp, (uint64_t)m_rows * 4, uni64(gd.gidx_lo), uni64(gd.gidx_hi)) ||
+                        !inside(Pp, p_bytes, uni64(gd.p_lo), uni64(gd.p_hi))))) {
       raise_abort(abort, 8u);
       break;
     }
@@ -595,23 +640,27 @@ template <class C, class S>
 __global__ __launch_bounds__(C::NT, 1) void ptg_kernel(typename S::Args args) {
   constexpr int kFlags = 2 * C::STAGES + 1;  // full[], empty[], abort
   __shared__ __attribute__((aligned(1024))) char smem[C::RING_BYTES + C::NINFO * sizeof(TileInfo) +
-                                                    kFlags * sizeof(uint32_t) + S::LDS_BYTES];
+                                                    sizeof(Guards) + kFlags * sizeof(uint32_t) +
+                                                    S::LDS_BYTES];
   char* ring = smem;
   TileInfo* info = reinterpret_cast<TileInfo*>(smem + C::RING_BYTES);
-  uint32_t* full = reinterpret_cast<uint32_t*>(smem + C::RING_BYTES + C::NINFO * sizeof(TileInfo));
+  Guards* guards = reinterpret_cast<Guards*>(smem + C::RING_BYTES + C::NINFO * sizeof(TileInfo));
+  uint32_t* full = reinterpret_cast<uint32_t*>(guards + 1);
   uint32_t* empty = full + C::STAGES;
   uint32_t* abort = empty + C::STAGES;
   char* sched_lds = reinterpret_cast<char*>(full + kFlags);
   if (threadIdx.x < kFlags) full[threadIdx.x] = 0;
+  // The operand ranges wait in LDS until a check needs them (kept in registers they would
+  // occupy two dozen scalar registers for the whole kernel).
+  if (threadIdx.x == 0) *guards = S::guards(args);
   S::template init<C>(args, sched_lds);  // cooperative; the barrier below publishes it
   __syncthreads();
   const int wave = threadIdx.x >> 6;
-  const Guards gd = S::guards(args);
   if (wave < C::NCONS) {
     __builtin_amdgcn_s_setprio(1);
-    consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, gd);
+    consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
   } else {
-    producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, gd);
+    producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, guards);
   }
 }
 
