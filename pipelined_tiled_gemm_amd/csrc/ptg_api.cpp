@@ -336,20 +336,22 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
     u.B = W; u.ldb = kn ? N : Kt;
     u.C = P; u.ldc = N;
     u.M = U; u.N = N; u.K = Ku;
-    u.b_kn = kn; u.epi = PTG_EPI_NONE; u.out_f32 = 1;
+    u.bias = needs_bias(epi) ? bias : nullptr;  // the bias rides along with the user part
+    u.b_kn = kn; u.epi = needs_bias(epi) ? PTG_EPI_BIAS : PTG_EPI_NONE; u.out_f32 = 1;
     hipError_t e = ptg::launch_dense(u, s);
     if (e != hipSuccess) return hip_fail(e, fn);
-    // ... and the candidate half runs per candidate, adding P[user_idx[r]] in the epilogue.
+    // ... and the candidate half runs per candidate, starting from P[user_idx[r]].
     ptg::DenseLaunch c{};
     c.A = Xc; c.lda = Kc;
     c.B = kn ? static_cast<const void*>(static_cast<const char*>(W) + Ku * N * 2)
              : static_cast<const void*>(static_cast<const char*>(W) + Ku * 2);
     c.ldb = kn ? N : Kt;
     c.C = Y; c.ldc = N;
-    c.bias = needs_bias(epi) ? bias : nullptr;
+    c.bias = nullptr;
     c.gidx = user_idx; c.P = P; c.ldp = N; c.p_rows = U;
     c.M = Mc; c.N = N; c.K = Kc;
-    c.b_kn = kn; c.epi = epi; c.out_f32 = y_dtype == PTG_F32;
+    c.b_kn = kn; c.out_f32 = y_dtype == PTG_F32;
+    c.epi = (epi == PTG_EPI_SILU || epi == PTG_EPI_BIAS_SILU) ? PTG_EPI_SILU : PTG_EPI_NONE;
     e = ptg::launch_dense(c, s);
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;

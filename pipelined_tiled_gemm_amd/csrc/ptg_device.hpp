@@ -41,6 +41,9 @@ namespace ptg {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+// (Vectors are reinterpreted whole: this compiler's __builtin_bit_cast of a subscripted vector
+// element reads element 0 whatever the subscript.)
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -61,9 +64,12 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // ---------------------------------------------------------------------------------------
 // Tile configuration
 // ---------------------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_>
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_, int PREG_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  // k-steps a producer holds in registers ahead of the LDS ring (0: tiles go straight from
+  // memory into LDS)
+  static constexpr int PREG = PREG_;
   static constexpr int WM = WM_, WN = WN_;             // consumer waves along M and N
   static constexpr int NCONS = WM * WN, NPROD = NPROD_;
   static constexpr int NWAVES = NCONS + NPROD, NT = NWAVES * 64;
@@ -80,11 +86,16 @@ struct Cfg {
   static constexpr int INFLIGHT = (STAGES < 63 / LOADS) ? STAGES : 63 / LOADS;
   static constexpr int CPR_A = BK / 8;                  // 16-byte chunks per A row
   static constexpr int CPR_B = B_KN ? BN / 8 : BK / 8;  // 16-byte chunks per B row
-  // Tile-metadata slots.  The producer rewrites slot j mod NINFO when it starts tile
-  // j + NINFO, which needs the release of k-step g(j + NINFO) - STAGES >= g(j) + n(j) + 1
-  // (each tile has at least one k-step): a step of tile j + 1.  So tile j's metadata stays
-  // in place until its epilogue is done.
-  static constexpr int NINFO = STAGES + 2;
+  // rows covered by two consecutive 1 KB loads (one load covers 64 chunks)
+  static constexpr int ROWS_A = 128 / CPR_A, ROWS_B = 128 / CPR_B;
+  // Tile-metadata slots.  Slot j mod NINFO holds tile j's metadata from the moment the
+  // producer starts fetching the tile until its epilogue is done.  The producer writes the
+  // slot for tile j + NINFO while it fetches a step at most PREG + 1 steps ahead of the ring
+  // slot it fills last, and it fills that slot only after the release of the step STAGES
+  // earlier; with NINFO = STAGES + PREG + 3, that released step belongs to tile j + 1 or a
+  // later one (every tile has at least one step), so the consumers have finished tile j,
+  // epilogue included.
+  static constexpr int NINFO = STAGES + PREG + 3;
   static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "consumer sub-tile must be 32x32 blocks");
   static_assert(BK % 16 == 0 && (BK == 32 || BK == 64), "BK must be 32 or 64");
@@ -93,6 +104,8 @@ struct Cfg {
   static_assert(LOADS <= 63, "one k-step of DMAs must fit the vector-memory counter");
   static_assert(STAGES >= 2, "the ring needs at least two slots");
   static_assert(INFLIGHT >= 1 && INFLIGHT <= STAGES, "in-flight steps are bounded by the ring");
+  static_assert(PREG == 0 || PREG == 1, "register staging holds one step");
+  static_assert(PREG == 0 || LOADS * 4 <= 96, "a register-staged step must fit the producer's registers");
   static_assert(NT <= 1024, "workgroup too large");
 };
 
@@ -268,6 +281,13 @@ __device__ __forceinline__ float silu(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Two floats to two bf16 (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------------------------------
 // Producer role
 // ---------------------------------------------------------------------------------------
@@ -275,7 +295,7 @@ __device__ __forceinline__ float silu(float v) {
 // copies 1 KB of the A tile, the rest copy the B tile.  Lane l of DMA i fills LDS bytes
 // [1024 i + 16 l, +16) of the slot, i.e. physical chunk P = 64 i + l of the tile.
 template <class C>
-__device__ __forceinline__ void chunk_of(int i, int lane, int& row, int& chunk) {
+__host__ __device__ constexpr void chunk_of(int i, int lane, int& row, int& chunk) {
   if (i < C::A_INSTR) {
     const int P = i * 64 + lane;
     row = P / C::CPR_A;
@@ -286,6 +306,23 @@ __device__ __forceinline__ void chunk_of(int i, int lane, int& row, int& chunk) 
     if constexpr (C::B_KN) chunk = (P % C::CPR_B) ^ swz_n<C::CPR_B>(row);
     else chunk = (P % C::CPR_B) ^ swz_k<C::CPR_B>(row);
   }
+}
+
+// The chunk pattern of load index i repeats every two loads, shifted by ROWS rows: for every
+// lane, load i + 2 fetches the same chunk as load i, ROWS_A (A) or ROWS_B (B) rows further on.
+// Checked at compile time for each configuration that stages through registers.
+template <class C>
+constexpr bool chunk_period2() {
+  for (int i = 0; i + 2 < C::A_INSTR + C::B_INSTR; ++i) {
+    if ((i < C::A_INSTR) != (i + 2 < C::A_INSTR)) continue;
+    for (int lane = 0; lane < 64; ++lane) {
+      int r0 = 0, c0 = 0, r2 = 0, c2 = 0;
+      chunk_of<C>(i, lane, r0, c0);
+      chunk_of<C>(i + 2, lane, r2, c2);
+      if (c2 != c0 || r2 != r0 + (i < C::A_INSTR ? C::ROWS_A : C::ROWS_B)) return false;
+    }
+  }
+  return true;
 }
 
 template <class C, class S>
@@ -407,63 +444,277 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
   lds_bump(&full[(g - 1) % C::STAGES]);
 }
 
+// Producer role with register staging (PREG = 1).  Each producer keeps its share of the
+// next k-step in registers (buffer loads into VGPRs), ahead of the LDS ring: when a ring
+// slot is released it writes the staged step into it with ds_write_b128, hands it over and
+// at once issues the loads of the following step into the same registers.  A step's loads
+// are thus issued one ring step earlier than a direct memory-to-LDS copy could issue them
+// (that needs the slot already free), and memory latency hides behind one more step of the
+// consumers' work.  The loads pick the same swizzled chunks as the DMA path, so the LDS
+// image is identical.
+//
+// The fetch side runs one step ahead of the ring, across tile boundaries: it starts a tile
+// (asks the scheduler, publishes the tile's metadata or the end marker) when it has fetched
+// the previous tile's last step.
+
+// What the fetch side keeps of the tile it fetches (every member is wave-uniform except the
+// per-lane bases).
+struct FetchTile {
+  uint64_t src;         // operand base of the tile (A rows or B rows/columns)
+  uint32_t bytes;       // bytes of the operand from src on, 0 when out of range
+  uint32_t rstep;       // bytes between loads q and q + 2
+  int64_t kstride;      // bytes per unit of k along the operand
+  int K, nsteps;
+  bool has;             // false: no tile, the end marker was published
+  uint32_t vbase0, vbase1;  // per-lane offsets of this producer's loads 0 and 1
+  int kbase0, kbase1;       // k (within a step) of loads 0 and 1; load q + 2 adds ROWS_B
+                            // k-rows in layout KN, nothing otherwise
+};
+
+template <class C, class S>
+__device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, int j, int pid, bool opA,
+                                                int i0, char* sched_lds, TileInfo* info,
+                                                const Guards* guards, uint32_t* abort) {
+  const int lane = lane_id();
+  TileSrc t = {};
+  FetchTile f = {};
+  // Every value is the same across the wave; saying so keeps the fetch state in scalar
+  // registers (a scheduler may read LDS, whose loads the compiler treats as per-lane).
+  f.has = uni(S::template tile<C>(args, j, t, sched_lds) ? 1u : 0u) != 0;
+  if (pid == 0 && lane == 0) {
+    TileInfo ti = t.info;
+    ti.tag = f.has ? tile_tag(j) : end_tag(j);
+    info[j % C::NINFO] = ti;
+  }
+  if (!f.has) return f;
+  f.K = (int)uni((uint32_t)t.info.K);
+  f.nsteps = (f.K + C::BK - 1) / C::BK;
+  const int64_t ld = (int64_t)uni64((uint64_t)(opA ? t.lda : t.ldb));
+  const int extent = (int)uni((uint32_t)(opA ? t.info.m_rows : t.info.n_cols));
+  f.src = uni64(reinterpret_cast<uint64_t>(opA ? (const void*)t.A : (const void*)t.B));
+  if (opA || !C::B_KN) {
+    f.bytes = (uint32_t)((int64_t)(extent - 1) * ld * 2 + (int64_t)f.K * 2);
+    f.kstride = 2;
+  } else {
+    f.bytes = (uint32_t)((int64_t)(f.K - 1) * ld * 2 + (int64_t)extent * 2);
+    f.kstride = ld * 2;
+  }
+  if (!inside(f.src, f.bytes, uni64(opA ? guards->a_lo : guards->b_lo), uni64(opA ? guards->a_hi : guards->b_hi))) {
+    raise_abort(abort, 4u);
+    f.bytes = 0;  // every load of this tile is out of range: nothing is read
+  }
+  // Rows and columns beyond the tile lie beyond the descriptor (a row past the last valid
+  // one starts past its end) or in columns the epilogue never stores, so only the k tail
+  // needs masking.  Chunk offsets repeat with period 2 in the load index (chunk_period2),
+  // so two per-lane bases and a row step describe all of them.
+  int row0 = 0, c0 = 0, row1 = 0, c1 = 0;
+  chunk_of<C>(i0, lane, row0, c0);
+  chunk_of<C>(i0 + 1, lane, row1, c1);
+  f.vbase0 = (uint32_t)(row0 * ld * 2 + c0 * 16);
+  f.vbase1 = (uint32_t)(row1 * ld * 2 + c1 * 16);
+  f.kbase0 = (!opA && C::B_KN) ? row0 : c0 * 8;  // k of the chunk's first element
+  f.kbase1 = (!opA && C::B_KN) ? row1 : c1 * 8;
+  f.rstep = (uint32_t)(ld * 2 * (opA ? C::ROWS_A : C::ROWS_B));
+  return f;
+}
+
+template <class C, class S>
+__device__ __forceinline__ void producer_role_regs(const typename S::Args& args, char* ring, TileInfo* info,
+                                                   uint32_t* full, uint32_t* empty, uint32_t* abort, int pid,
+                                                   char* sched_lds, const Guards* guards) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  static_assert(C::A_INSTR % C::LOADS == 0, "each producer copies either A or B chunks");
+  static_assert(C::LOADS % 2 == 0 && chunk_period2<C>(), "load offsets must repeat every two loads");
+  const int lane = lane_id();
+  const int i0 = pid * C::LOADS;
+  const bool opA = i0 < C::A_INSTR;  // this producer's operand
+  const int lds_base = (opA ? i0 * 1024 : C::A_BYTES + (i0 - C::A_INSTR) * 1024) + lane * 16;
+  const int kq = (!opA && C::B_KN) ? C::ROWS_B : 0;
+
+  u32x4 R[C::LOADS];
+  int fj = 0, fst = 0;  // tile and step the registers hold (or will hold)
+  FetchTile f = fetch_tile<C, S>(args, 0, pid, opA, i0, sched_lds, info, guards, abort);
+  for (uint32_t g = 0;; ++g) {
+    // ---- fetch: issue the loads of step fst of tile fj into R (zeros past K) -----------
+    if (f.has) {
+      const int k0 = fst * C::BK;
+      const int64_t kbytes = (int64_t)k0 * f.kstride;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(reinterpret_cast<const void*>(f.src + kbytes), f.bytes - (uint32_t)kbytes);
+      if (k0 + C::BK <= f.K) {
+#pragma unroll
+        for (int q = 0; q < C::LOADS; ++q)
+          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((q & 1) ? f.vbase1 : f.vbase0) + (uint32_t)(q >> 1) * f.rstep, 0, 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < C::LOADS; ++q) {
+          const int kpos = ((q & 1) ? f.kbase1 : f.kbase0) + (q >> 1) * kq;
+          const uint32_t vo = ((q & 1) ? f.vbase1 : f.vbase0) + (uint32_t)(q >> 1) * f.rstep;
+          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, k0 + kpos < f.K ? vo : kOutOfRange, 0, 0);
+        }
+      }
+    }
+    // ---- ring: step g goes to slot s once the consumers have released it ---------------
+    const int s = g % C::STAGES;
+    wait_at_least(&empty[s], (uint32_t)C::NCONS * (g / C::STAGES), abort);
+    if (!f.has) {
+      lds_bump(&full[s]);  // the end marker's step carries no data
+      break;
+    }
+    char* dst = ring + s * C::STAGE_BYTES + lds_base;
+#pragma unroll
+    for (int q = 0; q < C::LOADS; ++q) *reinterpret_cast<u32x4*>(dst + q * 1024) = R[q];
+    // LDS runs one wave's accesses in order: the writes land before the count moves
+    lds_bump(&full[s]);
+    // ---- advance the fetch side -------------------------------------------------------
+    if (++fst == f.nsteps) {
+      fst = 0;
+      f = fetch_tile<C, S>(args, ++fj, pid, opA, i0, sched_lds, info, guards, abort);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Consumer role: MFMA on staged tiles, then the epilogue stage on the accumulators
 // ---------------------------------------------------------------------------------------
 
-// Epilogue stage of one consumer wave: out = silu?(acc + bias + P[idx[row]]), converted and
-// stored.  Every access goes through a buffer descriptor; elements outside the tile's valid
-// rows/columns get an out-of-range offset, so loads return 0 and stores are dropped.
+// Start value of one consumer wave's accumulators: bias[col], or P[idx[row]][col] for a
+// gathered (broadcast) launch, else zero; a gathered launch carries no bias (the host adds
+// it to P).  The MFMAs then add the products on top, so the epilogue needs no loads and
+// nothing extra stays live next to the accumulators (the loads land in the accumulator
+// registers themselves).  Layout as in the epilogue below: register 4q + t of acc[tm][tn],
+// lane l, is row 32 tm + l % 32, column 32 tn + 8q + 4 (l / 32) + t of the wave's sub-tile,
+// so each lane loads runs of 4 columns.  Returns false (workgroup aborted) when the tile's
+// metadata or an operand range is wrong.
 template <class C>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], int wm, int wn,
-                                         int m_rows, int n_cols, uint64_t Cp, int ldc,
-                                         uint64_t biasp, uint64_t gidxp, uint64_t Pp, int ldp,
-                                         uint32_t p_bytes, int epi, bool f32out) {
+__device__ __forceinline__ bool init_acc(f32x16 (&acc)[C::TM][C::TN], const TileInfo* ti,
+                                         const Guards* guards, int epi, int wm, int wn,
+                                         uint32_t* abort) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = f32x16{};
+  const uint64_t biasp = uni64(ti->bias);
+  const uint64_t gidxp = uni64(ti->gidx);
+  const bool gather = gidxp != 0;
+  const bool do_bias = (epi == EPI_BIAS || epi == EPI_BIAS_SILU) && biasp != 0 && !gather;
+  if (!do_bias && !gather) return true;
+  const int m_rows = (int)uni((uint32_t)ti->m_rows);
+  const int n_cols = (int)uni((uint32_t)ti->n_cols);
+  const uint64_t Pp = uni64(ti->P);
+  const int ldp = (int)uni((uint32_t)ti->ldp);
+  const uint32_t p_bytes = uni(ti->p_bytes);
+  if (m_rows < 1 || m_rows > C::BM || n_cols < 1 || n_cols > C::BN) {
+    raise_abort(abort, 2u);
+    return false;
+  }
+  const Guards& gd = *guards;
+  if ((do_bias && !inside(biasp, (uint64_t)n_cols * 4, uni64(gd.bias_lo), uni64(gd.bias_hi))) ||
+      (gather && (!inside(gidxp, (uint64_t)m_rows * 4, uni64(gd.gidx_lo), uni64(gd.gidx_hi)) ||
+                  !inside(Pp, p_bytes, uni64(gd.p_lo), uni64(gd.p_hi))))) {
+    raise_abort(abort, 8u);
+    return false;
+  }
   const int lane = opaque(lane_id());
+  const int half = lane >> 5;
+  if (do_bias) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<void*>(biasp), (uint32_t)(n_cols * 4));
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * C::WTN + tn * 32 + q * 8 + half * 4;
+        const f32x4 b4 = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col < n_cols ? col * 4 : kOutOfRange, 0, 0));
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[tm][tn][4 * q + t] = b4[t];
+      }
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<void*>(gidxp), (uint32_t)(m_rows * 4));
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(reinterpret_cast<void*>(Pp), p_bytes);
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      const int row = wm * C::WTM + tm * 32 + (lane & 31);
+      const bool row_ok = row < m_rows;
+      const int prow = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, row_ok ? row * 4 : kOutOfRange, 0, 0);
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * C::WTN + tn * 32 + q * 8 + half * 4;
+          const uint32_t po = (row_ok && col < n_cols) ? (uint32_t)(prow * ldp + col) * 4u : kOutOfRange;
+          const f32x4 p4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, po, 0, 0));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[tm][tn][4 * q + t] = p4[t];
+        }
+      }
+    }
+  }
+  return true;
+}
+
+// Epilogue stage of one consumer wave: SiLU if asked, conversion, stores.  The MFMAs run with
+// B as the first operand, so acc[tm][tn] holds the transpose of its 32 x 32 block (layout
+// above): each lane owns runs of 4 consecutive columns of one row.  fp32 output leaves in
+// 16-byte stores; bf16 output is packed to 8-byte runs, and lanes l and l + 32 (same row)
+// trade halves so that each holds 8 consecutive columns, again one 16-byte store.  N is a
+// multiple of 8 and rows are 16-byte aligned, so a run is wholly inside the valid columns
+// or wholly outside; rows and runs outside the tile get an out-of-range offset (the store
+// is dropped).
+template <class C>
+__device__ __forceinline__ void epilogue(f32x16 (&acc)[C::TM][C::TN], int wm, int wn, int m_rows,
+                                         int n_cols, uint64_t Cp, int ldc, bool do_silu, bool f32out) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const int lane = opaque(lane_id());
+  const int half = lane >> 5;
   const int osz = f32out ? 4 : 2;
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)(((m_rows - 1) * ldc + n_cols) * osz));
-  const bool do_bias = (epi == EPI_BIAS || epi == EPI_BIAS_SILU) && biasp != 0;
-  const bool do_silu = (epi == EPI_SILU || epi == EPI_BIAS_SILU);
-  const bool gather = gidxp != 0;
-  float bcol[C::TN];
-#pragma unroll
-  for (int tn = 0; tn < C::TN; ++tn) {
-    const int col = wn * C::WTN + tn * 32 + (lane & 31);
-    bcol[tn] = 0.0f;
-    if (do_bias) {
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<void*>(biasp), (uint32_t)(n_cols * 4));
-      bcol[tn] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, col < n_cols ? col * 4 : kOutOfRange, 0, 0));
-    }
-  }
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
+    const int row = wm * C::WTM + tm * 32 + (lane & 31);
+    const bool row_ok = row < m_rows;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * C::WTM + tm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const bool row_ok = row < m_rows;
-      int prow = 0;
-      if (gather) {
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<void*>(gidxp), (uint32_t)(m_rows * 4));
-        prow = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, row_ok ? row * 4 : kOutOfRange, 0, 0);
+    for (int tn = 0; tn < C::TN; ++tn) {
+      f32x16& v = acc[tm][tn];
+      if (do_silu) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = silu(v[r]);
       }
+      if (f32out) {
 #pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) {
-        const int col = wn * C::WTN + tn * 32 + (lane & 31);
-        const bool ok = row_ok && col < n_cols;
-        float v = acc[tm][tn][r] + bcol[tn];
-        if (gather) {
-          const __amdgpu_buffer_rsrc_t rp = make_rsrc(reinterpret_cast<void*>(Pp), p_bytes);
-          const uint32_t po = ok ? (uint32_t)(prow * ldp + col) * 4u : kOutOfRange;
-          v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, po, 0, 0));
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * C::WTN + tn * 32 + q * 8 + half * 4;
+          const uint32_t vo = (row_ok && col < n_cols) ? (uint32_t)(row * ldc + col) * 4u : kOutOfRange;
+          const f32x4 o = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rc, vo, 0, 0);
         }
-        if (do_silu) v = silu(v);
-        const uint32_t vo = ok ? (uint32_t)(row * ldc + col) * (uint32_t)osz : kOutOfRange;
-        if (f32out) {
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, vo, 0, 0);
-        } else {
-          const __bf16 h = (__bf16)v;
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), rc, vo, 0, 0);
+      } else {
+        // pack each run of 4 to bf16 (round to nearest even); then, for the run pairs (0, 1)
+        // and (2, 3), the low lanes' second run trades places with the high lanes' first run
+        uint32_t w[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[q][0] = pack_bf16(v[4 * q], v[4 * q + 1]);
+          w[q][1] = pack_bf16(v[4 * q + 2], v[4 * q + 3]);
+        }
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(w[2 * pr][h], w[2 * pr + 1][h], false, false);
+            w[2 * pr][h] = sw[0];
+            w[2 * pr + 1][h] = sw[1];
+          }
+          // low lanes now hold columns 16 pr + 0..7 of the block, high lanes 16 pr + 8..15
+          const int col = wn * C::WTN + tn * 32 + pr * 16 + half * 8;
+          const uint32_t vo = (row_ok && col < n_cols) ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
+          const u32x4 d = {w[2 * pr][0], w[2 * pr][1], w[2 * pr + 1][0], w[2 * pr + 1][1]};
+          __builtin_amdgcn_raw_buffer_store_b128(d, rc, vo, 0, 0);
         }
       }
     }
@@ -521,10 +772,7 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
     const int nsteps = (K + C::BK - 1) / C::BK;
 
     f32x16 acc[C::TM][C::TN];
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = f32x16{};
+    if (!init_acc<C>(acc, ti, guards, epi, wm, wn, abort)) break;
 
     // Fragment loads of one 16-deep sub-step kk of a staged slot.
     auto load_a = [&](const char* slot, int kk, int tm) -> bf16x8 {
@@ -581,7 +829,7 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
         for (int tn = 0; tn < C::TN; ++tn) {
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm) {
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[tn], a[tm], acc[tm][tn], 0, 0, 0);
             if (tn == C::TN - 1 && more) {
               if (!ready) {
                 wait_at_least(&full[sn], (uint32_t)C::NPROD * ((g + 1) / C::STAGES + 1), abort);
@@ -603,33 +851,23 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
       }
     }
 
-    // ---- epilogue stage: bias, broadcast gather-add, SiLU, convert, store -------------
+    // ---- epilogue stage: SiLU, convert, store ------------------------------------------
     // The metadata is read again here (it is still in place, see NINFO), so that nothing
     // of the epilogue stays live in registers across the MFMA loop.
     const int m_rows = (int)uni((uint32_t)ti->m_rows);
     const int n_cols = (int)uni((uint32_t)ti->n_cols);
     const uint64_t Cp = uni64(ti->C);
     const int ldc = (int)uni((uint32_t)ti->ldc);
-    const uint64_t biasp = uni64(ti->bias);
-    const uint64_t gidxp = uni64(ti->gidx);
-    const uint64_t Pp = uni64(ti->P);
-    const int ldp = (int)uni((uint32_t)ti->ldp);
-    const uint32_t p_bytes = uni(ti->p_bytes);
     if (m_rows < 1 || m_rows > C::BM || n_cols < 1 || n_cols > C::BN || ldc < n_cols) {
       raise_abort(abort, 2u);
       break;
     }
     const uint64_t c_bytes = (uint64_t)((m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
-    const bool do_bias = (epi == EPI_BIAS || epi == EPI_BIAS_SILU) && biasp != 0;
-    const Guards& gd = *guards;
-    if (!inside(Cp, c_bytes, uni64(gd.c_lo), uni64(gd.c_hi)) ||
-        (do_bias && !inside(biasp, (uint64_t)n_cols * 4, uni64(gd.bias_lo), uni64(gd.bias_hi))) ||
-        (gidxp != 0 && (!inside(gidxp, (uint64_t)m_rows * 4, uni64(gd.gidx_lo), uni64(gd.gidx_hi)) ||
-                        !inside(Pp, p_bytes, uni64(gd.p_lo), uni64(gd.p_hi))))) {
+    if (!inside(Cp, c_bytes, uni64(guards->c_lo), uni64(guards->c_hi))) {
       raise_abort(abort, 8u);
       break;
     }
-    epilogue<C>(acc, wm, wn, m_rows, n_cols, Cp, ldc, biasp, gidxp, Pp, ldp, p_bytes, epi, f32out);
+    epilogue<C>(acc, wm, wn, m_rows, n_cols, Cp, ldc, epi == EPI_SILU || epi == EPI_BIAS_SILU, f32out);
   }
 }
 
@@ -655,12 +893,15 @@ __global__ __launch_bounds__(C::NT, 1) void ptg_kernel(typename S::Args args) {
   if (threadIdx.x == 0) *guards = S::guards(args);
   S::template init<C>(args, sched_lds);  // cooperative; the barrier below publishes it
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
+  const int wave = (int)uni(threadIdx.x >> 6);  // the same for every lane of a wave
   if (wave < C::NCONS) {
     __builtin_amdgcn_s_setprio(1);
     consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
   } else {
-    producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, guards);
+    if constexpr (C::PREG > 0)
+      producer_role_regs<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, guards);
+    else
+      producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, guards);
   }
 }
 

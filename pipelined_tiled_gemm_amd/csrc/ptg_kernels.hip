@@ -260,7 +260,7 @@ struct BatchSched {
 // Large problems: 256 x 256 tiles, 8 consumer waves (2 x 4, 128 x 64 each), 4 producers,
 // two 64 KB ring slots.  Medium/small: 128 x 128 tiles, 4 consumers (64 x 64 each), 2
 // producers, four 32 KB slots.
-template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN>;
+template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN, 1>;
 template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN>;
 
 struct DeviceInfo {

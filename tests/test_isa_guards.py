@@ -10,6 +10,10 @@
   buffer-descriptor helper once rebuilt a pointer from two readfirstlane results, whose
   signed int type sign-extended the low word into the high word whenever bit 31 of the
   address was set: the descriptor base became 0xffff'xxxx'xxxx and the first access faulted.
+- No __builtin_bit_cast of a subscripted vector element in the kernel sources: this hipcc
+  reads element 0 whatever the subscript (an fp32 epilogue built that way stored column 0
+  of every 4-column run four times).  The compiler behaviour itself is pinned too.
+- Every 16-byte output store takes four distinct registers (no broadcast of one value).
 """
 import os
 import re
@@ -78,3 +82,51 @@ def test_promotion_rule_behind_the_guard():
     right = (hi << 32) | (as_int & 0xFFFFFFFF)                           # via uint32_t
     assert wrong >> 32 == 0xFFFFFFFF
     assert right == 0x00007F12_9ABC0000
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_no_bit_cast_of_vector_elements():
+    pat = re.compile(r"__builtin_bit_cast\(\s*[\w:]+\s*,\s*[\w.]+\s*\[")
+    for name in os.listdir(build.CSRC):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            text = open(os.path.join(build.CSRC, name)).read()
+            assert not pat.search(text), f"{name}: __builtin_bit_cast of a vector element"
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_compiler_bit_cast_of_element_reads_element_zero(tmp_path):
+    """Why the rule above exists: bit_cast(float, x[2]) compiles to element 0."""
+    src = tmp_path / "bc.hip"
+    src.write_text(
+        "#include <hip/hip_runtime.h>\n"
+        "typedef __attribute__((ext_vector_type(4))) unsigned u32x4;\n"
+        "__global__ void k(const u32x4* in, float* out) {\n"
+        "  u32x4 x = in[threadIdx.x];\n"
+        "  out[threadIdx.x] = __builtin_bit_cast(float, x[2]);\n"
+        "}\n")
+    out = tmp_path / "bc.ll"
+    subprocess.run([build.hipcc(), "--offload-arch=gfx950", "-O3", "--cuda-device-only", "-S",
+                    "-emit-llvm", str(src), "-o", str(out)], check=True, capture_output=True)
+    ir = out.read_text()
+    # if a fixed compiler extracts element 2, this test fails and the rule can be relaxed
+    assert "extractelement <4 x float> %6, i64 0" in ir or re.search(r"extractelement <4 x \w+> %\d+, i64 0", ir)
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_wide_output_stores_take_distinct_registers(asm):
+    n = 0
+    for name, body in kernels(asm):
+        for k, line in enumerate(body):
+            if "buffer_store_dwordx4" not in line:
+                continue
+            n += 1
+            reg = line.split()[1].rstrip(",")          # v[a:b]
+            a = int(reg[2:reg.index(":")])
+            movs = [l for l in body[max(0, k - 8):k] if "v_mov_b32" in l]
+            srcs = {}
+            for l in movs:
+                dst, src = [x.strip() for x in l.split(None, 1)[1].split(",")[:2]]
+                if dst.startswith("v") and dst[1:].isdigit() and a <= int(dst[1:]) <= a + 3:
+                    srcs[dst] = src
+            assert len(srcs) < 4 or len(set(srcs.values())) > 1, f"{name}: broadcast store {line.strip()}"
+    assert n > 0
