@@ -80,7 +80,7 @@ struct Cfg {
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // 1 KB per DMA
-  static constexpr int LOADS = (A_INSTR + B_INSTR) / NPROD;  // DMAs per producer per k-step
+  static constexpr int LOADS = (A_INSTR + B_INSTR) / NPROD;  // 1 KB loads per producer per k-step
   // k-steps a producer keeps in flight before it waits for the oldest to land (bounded by
   // the ring and by the 6-bit vector-memory counter)
   static constexpr int INFLIGHT = (STAGES < 63 / LOADS) ? STAGES : 63 / LOADS;
@@ -104,8 +104,8 @@ struct Cfg {
   static_assert(LOADS <= 63, "one k-step of DMAs must fit the vector-memory counter");
   static_assert(STAGES >= 2, "the ring needs at least two slots");
   static_assert(INFLIGHT >= 1 && INFLIGHT <= STAGES, "in-flight steps are bounded by the ring");
-  static_assert(PREG == 0 || PREG == 1, "register staging holds one step");
-  static_assert(PREG == 0 || LOADS * 4 <= 96, "a register-staged step must fit the producer's registers");
+  static_assert(PREG == 0 || PREG == 1, "0: memory to LDS; 1: one step staged in registers");
+  static_assert(PREG == 0 || LOADS * 4 <= 128, "a register-staged step must fit the producer's registers");
   static_assert(NT <= 1024, "workgroup too large");
 };
 
@@ -179,12 +179,23 @@ __device__ __forceinline__ bool inside(uint64_t p, uint64_t bytes, uint64_t lo, 
 // ---------------------------------------------------------------------------------------
 // Small device helpers
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// Lane index from the lane-mask counter (a function of the lane alone, so the compiler can
+// recompute it where needed instead of keeping the thread index live).
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
 
 // A copy of x that the compiler cannot see through: index arithmetic derived from it is
 // recomputed where it is used instead of being hoisted out of loops and kept live.
 __device__ __forceinline__ int opaque(int x) {
   __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
+// The lane index, computed afresh where it is used (nothing stays live before that point).
+__device__ __forceinline__ int opaque_lane() {
+  int x;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
   return x;
 }
 
@@ -616,7 +627,7 @@ __device__ __forceinline__ bool init_acc(f32x16 (&acc)[C::TM][C::TN], const Tile
     raise_abort(abort, 8u);
     return false;
   }
-  const int lane = opaque(lane_id());
+  const int lane = opaque_lane();
   const int half = lane >> 5;
   if (do_bias) {
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<void*>(biasp), (uint32_t)(n_cols * 4));
@@ -669,7 +680,7 @@ template <class C>
 __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::TM][C::TN], int wm, int wn, int m_rows,
                                          int n_cols, uint64_t Cp, int ldc, bool do_silu, bool f32out) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-  const int lane = opaque(lane_id());
+  const int lane = opaque_lane();
   const int half = lane >> 5;
   const int osz = f32out ? 4 : 2;
   const __amdgpu_buffer_rsrc_t rc =
@@ -734,7 +745,7 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
   const int a_chunk = (lane >> 5) ^ swz_k<C::CPR_A>(ra);
   const int a_base = ra * C::BK * 2;
   int b_base = 0, b_chunk = 0;
-  int b_kn[C::TN];  // KN: byte offset of the first transposing read of block tn at sub-step 0
+  int b_kn0 = 0;  // KN: byte offset of the first transposing read of block 0 at sub-step 0
   if constexpr (!C::B_KN) {
     const int rb = wn * C::WTN + (lane & 31);
     b_chunk = (lane >> 5) ^ swz_k<C::CPR_B>(rb);
@@ -744,14 +755,15 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
     // columns 4 (i % 4) .. +3; the hardware hands lane i the 4 k-values of column i.  The
     // second read of a fragment is 4 k-rows further down, and sub-step kk adds 16 k-rows:
     // both multiples of 4, so the swizzle (a function of k mod 4), hence the offset within
-    // a row, is unchanged and both become immediate offsets.
+    // a row, is unchanged and both become immediate offsets.  Block tn sits 4 tn chunks
+    // further along the row; the wave's first chunk index is a multiple of 4 TN, so that
+    // is an XOR of the chunk index (TN a power of two), and the swizzle XOR commutes with
+    // it: block tn reads at b_kn0 ^ (tn << 6).
+    static_assert((C::TN & (C::TN - 1)) == 0, "TN must be a power of two");
     const int blk = lane >> 4, i = lane & 15;
     const int k = (blk >> 1) * 8 + (i >> 2);
-#pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-      const int n = wn * C::WTN + tn * 32 + (blk & 1) * 16 + (i & 3) * 4;
-      b_kn[tn] = k * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(k)) << 4) + ((n >> 2) & 1) * 8;
-    }
+    const int n = wn * C::WTN + (blk & 1) * 16 + (i & 3) * 4;
+    b_kn0 = k * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(k)) << 4) + ((n >> 2) & 1) * 8;
   }
 
   uint32_t g = 0;
@@ -785,10 +797,11 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
         return *reinterpret_cast<const bf16x8*>(slotB + b_base + (((kk * 2) ^ b_chunk) << 4) +
                                                 tn * 32 * C::BK * 2);
       } else {
+        const int off = b_kn0 ^ (tn << 6);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(slotB + b_kn[tn] + kk * 16 * C::BN * 2));
+            (lds_i16x4*)(slotB + off + kk * 16 * C::BN * 2));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(slotB + b_kn[tn] + (kk * 16 + 4) * C::BN * 2));
+            (lds_i16x4*)(slotB + off + (kk * 16 + 4) * C::BN * 2));
         typedef __attribute__((ext_vector_type(8))) short i16x8;
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
@@ -898,7 +911,7 @@ __global__ __launch_bounds__(C::NT, 1) void ptg_kernel(typename S::Args args) {
     __builtin_amdgcn_s_setprio(1);
     consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
   } else {
-    if constexpr (C::PREG > 0)
+    if constexpr (C::PREG == 1)
       producer_role_regs<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, guards);
     else
       producer_role<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, guards);
