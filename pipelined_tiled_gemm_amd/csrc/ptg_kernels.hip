@@ -146,7 +146,7 @@ struct GroupedSched {
     const float* bias;
     const int32_t* offsets;
     int64_t M_total;
-    int32_t G, N, K, tiles_n;
+    int32_t G, N, K, tiles_n, group_m;
     int32_t epi, out_f32, out_bytes;
     Guards guard;
   };
@@ -183,7 +183,14 @@ struct GroupedSched {
     const int local = (int)(L - pre[g]);
     const int row0 = off[g], cnt = off[g + 1] - off[g];  // cnt > 0: the group has tiles
     const int mtiles = (cnt + C::BM - 1) / C::BM;
-    const int mt = local % mtiles, nt = local / mtiles;  // the m-tiles of one W_g strip are adjacent
+    // Within a group, tiles come in bands of group_m m-tiles walked column by column: the
+    // workgroups of one XCD, which take consecutive tiles, then share both the band's rows
+    // of X and a few column strips of W_g in their L2.
+    const int per_band = a.group_m * a.tiles_n;
+    const int band = local / per_band, in = local % per_band;
+    const int first_m = band * a.group_m;
+    const int bm = min(mtiles - first_m, a.group_m);
+    const int mt = first_m + in % bm, nt = in / bm;
     const int64_t m0 = (int64_t)row0 + (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
     const int64_t wsize = (int64_t)a.K * a.N;
     t.A = a.X + m0 * a.K;
@@ -257,11 +264,14 @@ struct BatchSched {
 // ---------------------------------------------------------------------------------------
 // Tile configurations
 // ---------------------------------------------------------------------------------------
-// Large problems: 256 x 256 tiles, 8 consumer waves (2 x 4, 128 x 64 each), 4 producers,
-// two 64 KB ring slots.  Medium/small: 128 x 128 tiles, 4 consumers (64 x 64 each), 2
-// producers, four 32 KB slots.
+// Large problems: 256 x 256 tiles, 8 consumer waves (2 x 4, 128 x 64 each), 4 producers
+// staging one k-step in registers, two 64 KB ring slots.  Medium/small: 128 x 128 tiles, 4
+// consumers (64 x 64 each), 2 producers, four 32 KB slots.  Grouped (mixture-of-experts):
+// 128 x 256 tiles (128-row tiles waste less on each expert's last partial tile), 4
+// consumers (one row of 128 x 64 sub-tiles, one per SIMD), 3 producers, three 48 KB slots.
 template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN, 1>;
 template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN>;
+template <bool KN> using CfgTall = Cfg<128, 256, 64, 3, 1, 4, 3, KN>;
 
 struct DeviceInfo {
   int cus = 0;
@@ -358,6 +368,9 @@ hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream) {
   return d.b_kn ? launch_dense_cfg<CfgMedium<true>>(d, stream) : launch_dense_cfg<CfgMedium<false>>(d, stream);
 }
 
+// m-tiles per band of the grouped tile order
+constexpr int kGroupedBandM = 8;
+
 template <class C>
 static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream) {
   GroupedSched::Args a;
@@ -369,6 +382,7 @@ static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream)
   a.M_total = g.M_total;
   a.G = g.G; a.N = (int32_t)g.N; a.K = (int32_t)g.K;
   a.tiles_n = (int32_t)((g.N + C::BN - 1) / C::BN);
+  a.group_m = kGroupedBandM;
   a.epi = g.epi; a.out_f32 = g.out_f32; a.out_bytes = g.out_f32 ? 4 : 2;
   Guards& gd = a.guard;
   gd = Guards{};
@@ -383,7 +397,7 @@ static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream)
 
 hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream) {
   if (g.M_total == 0 || g.N == 0) return hipSuccess;
-  return g.b_kn ? launch_grouped_cfg<CfgMedium<true>>(g, stream) : launch_grouped_cfg<CfgMedium<false>>(g, stream);
+  return g.b_kn ? launch_grouped_cfg<CfgTall<true>>(g, stream) : launch_grouped_cfg<CfgTall<false>>(g, stream);
 }
 
 hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream) {
