@@ -783,6 +783,22 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
     const int K = (int)uni((uint32_t)ti->K);
     const int nsteps = (K + C::BK - 1) / C::BK;
 
+    // A wave whose sub-tile lies wholly outside the tile's valid rows or columns has nothing
+    // to compute or store: it only takes part in the handoff, releasing each step as it
+    // arrives (a release never runs ahead of the step's arrival, so the counts stay exact).
+    // On a tile with at most half its rows valid, half the consumer waves idle and each
+    // SIMD's matrix core serves the other half alone.
+    if (wm * C::WTM >= (int)uni((uint32_t)ti->m_rows) || wn * C::WTN >= (int)uni((uint32_t)ti->n_cols)) {
+      lds_bump(&empty[s0]);
+      ++g;
+      for (int st = 1; st < nsteps; ++st, ++g) {
+        const int s = g % C::STAGES;
+        wait_at_least(&full[s], (uint32_t)C::NPROD * (g / C::STAGES + 1), abort);
+        lds_bump(&empty[s]);
+      }
+      continue;
+    }
+
     f32x16 acc[C::TM][C::TN];
     if (!init_acc<C>(acc, ti, guards, epi, wm, wn, abort)) break;
 

@@ -138,6 +138,15 @@ __device__ __forceinline__ int upper_index(const int32_t* pre, int n, int64_t x)
 // ---------------------------------------------------------------------------------------
 // Grouped (mixture-of-experts) scheduler
 // ---------------------------------------------------------------------------------------
+// Each group g owns rows [off[g], off[g+1]) and is cut into BM-row tiles.  A tile with more
+// than BM/2 valid rows costs a full tile; one with at most BM/2 (a group's last partial tile)
+// costs about half, since the consumer waves of its empty half idle (consumer_role).  The
+// full tiles of all groups come first and the half tiles after them, so the persistent
+// workgroups meet the heavy work early; rounds alternate direction over the workgroups
+// (snake order), so that the workgroups that took a full tile late take a half tile or
+// none at the end.  Within a group, full tiles come in bands of group_m m-tiles walked column
+// by column: the workgroups of one XCD, which take consecutive tiles, then share both the
+// band's rows of X and a few column strips of W_g in their L2.
 struct GroupedSched {
   struct Args {
     const __bf16* X;
@@ -151,14 +160,21 @@ struct GroupedSched {
     Guards guard;
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
-  // offsets[G + 1], tile prefix[G + 1], scan scratch
-  static constexpr int LDS_BYTES = 2 * (kMaxGroups + 1) * 4 + 20 * 4;
+  // offsets[G + 1], full-tile prefix[G + 1], half-tile prefix[G + 1], scan scratch
+  static constexpr int LDS_BYTES = 3 * (kMaxGroups + 1) * 4 + 20 * 4;
+
+  // full (more than BM/2 valid rows) and half m-tiles of a group of cnt rows
+  template <class C>
+  __device__ static int full_mtiles(int cnt) { return cnt / C::BM + (cnt % C::BM > C::BM / 2 ? 1 : 0); }
+  template <class C>
+  __device__ static int half_mtiles(int cnt) { return (cnt % C::BM > 0 && cnt % C::BM <= C::BM / 2) ? 1 : 0; }
 
   template <class C>
   __device__ static void init(const Args& a, char* lds) {
     int32_t* off = reinterpret_cast<int32_t*>(lds);
-    int32_t* pre = off + kMaxGroups + 1;
-    int32_t* scratch = pre + kMaxGroups + 1;
+    int32_t* pre_full = off + kMaxGroups + 1;
+    int32_t* pre_half = pre_full + kMaxGroups + 1;
+    int32_t* scratch = pre_half + kMaxGroups + 1;
     // Offsets are clamped to [0, M_total]: the precondition says they already are, and the
     // clamp keeps every access inside X and Y even when a caller breaks it.
     for (int i = threadIdx.x; i <= a.G; i += C::NT) {
@@ -169,28 +185,41 @@ struct GroupedSched {
     const int tn = a.tiles_n;
     block_exclusive_scan<C::NT>(a.G, [&](int g) {
       const int cnt = off[g + 1] - off[g];
-      return cnt > 0 ? ((cnt + C::BM - 1) / C::BM) * tn : 0;
-    }, pre, scratch);
+      return cnt > 0 ? full_mtiles<C>(cnt) * tn : 0;
+    }, pre_full, scratch);
+    block_exclusive_scan<C::NT>(a.G, [&](int g) {
+      const int cnt = off[g + 1] - off[g];
+      return cnt > 0 ? half_mtiles<C>(cnt) * tn : 0;
+    }, pre_half, scratch);
   }
 
   template <class C>
   __device__ static bool tile(const Args& a, int j, TileSrc& t, char* lds) {
     const int32_t* off = reinterpret_cast<const int32_t*>(lds);
-    const int32_t* pre = off + kMaxGroups + 1;
-    const int64_t L = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
-    if (L >= pre[a.G]) return false;
-    const int g = upper_index(pre, a.G, L);
-    const int local = (int)(L - pre[g]);
+    const int32_t* pre_full = off + kMaxGroups + 1;
+    const int32_t* pre_half = pre_full + kMaxGroups + 1;
+    const int r = (int)xcd_rank(blockIdx.x, gridDim.x);
+    const int64_t L = (int64_t)j * gridDim.x + ((j & 1) ? (int64_t)gridDim.x - 1 - r : r);
+    const int64_t n_full = pre_full[a.G];
+    int g, mt, nt;
+    if (L < n_full) {
+      g = upper_index(pre_full, a.G, L);
+      const int local = (int)(L - pre_full[g]);
+      const int mtiles = full_mtiles<C>(off[g + 1] - off[g]);
+      const int per_band = a.group_m * a.tiles_n;
+      const int band = local / per_band, in = local % per_band;
+      const int first_m = band * a.group_m;
+      const int bm = min(mtiles - first_m, a.group_m);
+      mt = first_m + in % bm;
+      nt = in / bm;
+    } else {
+      const int64_t L2 = L - n_full;
+      if (L2 >= pre_half[a.G]) return false;
+      g = upper_index(pre_half, a.G, L2);
+      mt = (off[g + 1] - off[g]) / C::BM;  // the group's last, partial m-tile
+      nt = (int)(L2 - pre_half[g]);
+    }
     const int row0 = off[g], cnt = off[g + 1] - off[g];  // cnt > 0: the group has tiles
-    const int mtiles = (cnt + C::BM - 1) / C::BM;
-    // Within a group, tiles come in bands of group_m m-tiles walked column by column: the
-    // workgroups of one XCD, which take consecutive tiles, then share both the band's rows
-    // of X and a few column strips of W_g in their L2.
-    const int per_band = a.group_m * a.tiles_n;
-    const int band = local / per_band, in = local % per_band;
-    const int first_m = band * a.group_m;
-    const int bm = min(mtiles - first_m, a.group_m);
-    const int mt = first_m + in % bm, nt = in / bm;
     const int64_t m0 = (int64_t)row0 + (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
     const int64_t wsize = (int64_t)a.K * a.N;
     t.A = a.X + m0 * a.K;
@@ -266,12 +295,12 @@ struct BatchSched {
 // ---------------------------------------------------------------------------------------
 // Large problems: 256 x 256 tiles, 8 consumer waves (2 x 4, 128 x 64 each), 4 producers
 // staging one k-step in registers, two 64 KB ring slots.  Medium/small: 128 x 128 tiles, 4
-// consumers (64 x 64 each), 2 producers, four 32 KB slots.  Grouped (mixture-of-experts):
-// 128 x 256 tiles (128-row tiles waste less on each expert's last partial tile), 4
-// consumers (one row of 128 x 64 sub-tiles, one per SIMD), 3 producers, three 48 KB slots.
+// consumers (64 x 64 each), 2 producers, four 32 KB slots.  Grouped (mixture-of-experts)
+// problems use the large tiles too: a group's last partial tile with at most 128 valid rows
+// runs on half the consumer waves at about half the cost.
 template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN, 1>;
 template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN>;
-template <bool KN> using CfgTall = Cfg<128, 256, 64, 3, 1, 4, 3, KN>;
+template <bool KN> using CfgGrouped = CfgLarge<KN>;
 
 struct DeviceInfo {
   int cus = 0;
@@ -397,7 +426,7 @@ static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream)
 
 hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream) {
   if (g.M_total == 0 || g.N == 0) return hipSuccess;
-  return g.b_kn ? launch_grouped_cfg<CfgTall<true>>(g, stream) : launch_grouped_cfg<CfgTall<false>>(g, stream);
+  return g.b_kn ? launch_grouped_cfg<CfgGrouped<true>>(g, stream) : launch_grouped_cfg<CfgGrouped<false>>(g, stream);
 }
 
 hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream) {
