@@ -148,6 +148,11 @@ ptg_status ptg_gemm_batch(int32_t count, const ptg_problem* problems, ptg_dtype 
  *   Y             [Mc x N] of y_dtype, dense
  *   bias          float32 [N] for the BIAS epilogues
  *   workspace     DEVICE scratch of at least ptg_broadcast_gemm_workspace(U, N) bytes
+ * The user product is small (U rows), so it is split along Ku into up to 32 slices that run
+ * side by side; their fp32 partial products go to the workspace after P and are summed in
+ * slice order (results do not depend on timing).  The workspace query returns
+ * U * N * 4 * (1 + S) bytes, S the slice count for U x N (a function of U and N only, at most
+ * 32; S = 1 needs no partials: U * N * 4 bytes).
  */
 size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N);
 ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N,

@@ -297,7 +297,9 @@ ptg_status ptg_gemm_batch(int32_t count, const ptg_problem* problems, ptg_dtype 
 
 size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N) {
   if (U <= 0 || N <= 0) return 0;
-  return (size_t)U * (size_t)N * sizeof(float);
+  const int32_t splits = ptg::broadcast_user_splits(U, N);
+  // P, then one partial product per split when the user phase splits K
+  return (size_t)U * (size_t)N * sizeof(float) * (splits > 1 ? 1 + (size_t)splits : 1);
 }
 
 ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
@@ -336,9 +338,26 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
     u.B = W; u.ldb = kn ? N : Kt;
     u.C = P; u.ldc = N;
     u.M = U; u.N = N; u.K = Ku;
-    u.bias = needs_bias(epi) ? bias : nullptr;  // the bias rides along with the user part
-    u.b_kn = kn; u.epi = needs_bias(epi) ? PTG_EPI_BIAS : PTG_EPI_NONE; u.out_f32 = 1;
-    hipError_t e = ptg::launch_dense(u, s);
+    u.b_kn = kn; u.out_f32 = 1;
+    // The user product is small (U rows): split K so that it spreads over the chip, each
+    // split writing a partial product after P, then sum the partials in split order (the
+    // result does not depend on timing) and add the bias, which rides along with P.
+    const int32_t max_splits = ptg::broadcast_user_splits(U, N);
+    const int64_t chunk = ((Ku + max_splits - 1) / max_splits + 63) / 64 * 64;  // whole k-steps
+    const int32_t splits = (int32_t)((Ku + chunk - 1) / chunk);
+    hipError_t e;
+    if (splits > 1) {
+      u.C = P + U * N;
+      u.splits = splits; u.k_chunk = chunk; u.c_split = U * N;
+      u.epi = PTG_EPI_NONE;
+      e = ptg::launch_dense(u, s);
+      if (e != hipSuccess) return hip_fail(e, fn);
+      e = ptg::launch_reduce_splits(P, P + U * N, U * N, splits, needs_bias(epi) ? bias : nullptr, N, s);
+    } else {
+      u.bias = needs_bias(epi) ? bias : nullptr;
+      u.epi = needs_bias(epi) ? PTG_EPI_BIAS : PTG_EPI_NONE;
+      e = ptg::launch_dense(u, s);
+    }
     if (e != hipSuccess) return hip_fail(e, fn);
     // ... and the candidate half runs per candidate, starting from P[user_idx[r]].
     ptg::DenseLaunch c{};

@@ -46,6 +46,8 @@ struct DenseSched {
     int32_t M, N, K;
     int32_t tiles_m, tiles_n, group_m;
     int32_t epi, out_f32, out_bytes;
+    int32_t splits;              // split-K: splits of k_chunk each, outputs c_split apart
+    int64_t k_chunk, c_split;
     Guards guard;
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
@@ -56,9 +58,11 @@ struct DenseSched {
 
   template <class C>
   __device__ static bool tile(const Args& a, int j, TileSrc& t, char*) {
-    const int64_t L = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
+    const int64_t L0 = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
     const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
-    if (L >= ntiles) return false;
+    if (L0 >= ntiles * a.splits) return false;
+    const int64_t split = L0 / ntiles, L = L0 % ntiles;
+    const int64_t k0 = split * a.k_chunk;
     // groups of `group_m` tile rows, walked column by column inside a group
     const int64_t per_group = (int64_t)a.group_m * a.tiles_n;
     const int64_t grp = L / per_group, in = L % per_group;
@@ -66,15 +70,15 @@ struct DenseSched {
     const int gm = min(a.tiles_m - first_m, a.group_m);
     const int tm = first_m + (int)(in % gm), tn = (int)(in / gm);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-    t.A = a.A + m0 * a.lda;
+    t.A = a.A + m0 * a.lda + k0;
     t.lda = a.lda;
-    t.B = C::B_KN ? a.B + n0 : a.B + n0 * a.ldb;
+    t.B = C::B_KN ? a.B + k0 * a.ldb + n0 : a.B + n0 * a.ldb + k0;
     t.ldb = a.ldb;
     t.info.tag = 0;  // set by the producer when it publishes the slot
-    t.info.K = a.K;
+    t.info.K = (int)min(a.k_chunk, (int64_t)a.K - k0);
     t.info.m_rows = (int)min((int64_t)C::BM, a.M - m0);
     t.info.n_cols = (int)min((int64_t)C::BN, a.N - n0);
-    t.info.C = (uint64_t)(a.C + (m0 * a.ldc + n0) * a.out_bytes);
+    t.info.C = (uint64_t)(a.C + (split * a.c_split + m0 * a.ldc + n0) * a.out_bytes);
     t.info.ldc = a.ldc;
     t.info.bias = a.bias ? (uint64_t)(a.bias + n0) : 0;
     t.info.gidx = a.gidx ? (uint64_t)(a.gidx + m0) : 0;
@@ -379,14 +383,18 @@ static hipError_t launch_dense_cfg(const DenseLaunch& d, hipStream_t stream) {
   a.tiles_n = (int32_t)((d.N + C::BN - 1) / C::BN);
   a.group_m = 4;
   a.epi = d.epi; a.out_f32 = d.out_f32; a.out_bytes = d.out_f32 ? 4 : 2;
+  a.splits = d.splits > 1 ? d.splits : 1;
+  a.k_chunk = d.splits > 1 ? d.k_chunk : d.K;
+  a.c_split = d.splits > 1 ? d.c_split : 0;
   Guards& g = a.guard;
   span(d.A, mat_bytes(d.M, d.K, d.lda, 2), g.a_lo, g.a_hi);
   span(d.B, d.b_kn ? mat_bytes(d.K, d.N, d.ldb, 2) : mat_bytes(d.N, d.K, d.ldb, 2), g.b_lo, g.b_hi);
-  span(d.C, mat_bytes(d.M, d.N, d.ldc, a.out_bytes), g.c_lo, g.c_hi);
+  span(d.C, (uint64_t)(a.splits - 1) * a.c_split * a.out_bytes + mat_bytes(d.M, d.N, d.ldc, a.out_bytes),
+       g.c_lo, g.c_hi);
   span(d.bias, (uint64_t)d.N * 4, g.bias_lo, g.bias_hi);
   span(d.gidx, (uint64_t)d.M * 4, g.gidx_lo, g.gidx_hi);
   span(d.P, mat_bytes(d.p_rows, d.ldp, d.ldp, 4), g.p_lo, g.p_hi);
-  return launch_persistent<C, DenseSched>(a, (int64_t)a.tiles_m * a.tiles_n, stream);
+  return launch_persistent<C, DenseSched>(a, (int64_t)a.tiles_m * a.tiles_n * a.splits, stream);
 }
 
 hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream) {
@@ -395,6 +403,50 @@ hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream) {
     return d.b_kn ? launch_dense_cfg<CfgLarge<true>>(d, stream) : launch_dense_cfg<CfgLarge<false>>(d, stream);
   }
   return d.b_kn ? launch_dense_cfg<CfgMedium<true>>(d, stream) : launch_dense_cfg<CfgMedium<false>>(d, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// Split-K reduction (broadcast user phase): out = sum of the partials in split order, plus
+// the bias; memory-bound, 16 bytes per lane per access.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void reduce_splits_kernel(float* out, const float* parts, int64_t count,
+                                                            int32_t splits, const float* bias, int64_t n) {
+  typedef __attribute__((ext_vector_type(4))) float f4;
+  const int64_t quads = count / 4;  // count and n are multiples of 8
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (int64_t)gridDim.x * blockDim.x) {
+    f4 acc = reinterpret_cast<const f4*>(parts)[q];
+    // eight partials in flight at a time, added in split order
+    for (int32_t s0 = 1; s0 < splits; s0 += 8) {
+      f4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = s0 + i < splits ? reinterpret_cast<const f4*>(parts + (s0 + i) * count)[q] : f4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < splits) acc += v[i];
+    }
+    if (bias) acc += reinterpret_cast<const f4*>(bias)[(q * 4 % n) / 4];
+    reinterpret_cast<f4*>(out)[q] = acc;
+  }
+}
+
+hipError_t launch_reduce_splits(float* out, const float* parts, int64_t count, int32_t splits,
+                                const float* bias, int64_t n, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  // 64-thread blocks: a small P still spreads over many CUs
+  const int64_t quads = count / 4;
+  const int64_t blocks = (quads + 63) / 64;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(64), 0, stream,
+                     out, parts, count, splits, bias, n);
+  return hipGetLastError();
+}
+
+// Splits of the broadcast user phase: enough to give the 256 CUs of an MI355X one tile each
+// when the U x N product alone has few tiles (it is small: U users), at most 32.
+int32_t broadcast_user_splits(int64_t U, int64_t N) {
+  const int64_t tiles = use_large(U, N) ? ((U + 255) / 256) * ((N + 255) / 256) : ((U + 127) / 128) * ((N + 127) / 128);
+  const int64_t s = 256 / (tiles > 0 ? tiles : 1);
+  return (int32_t)(s < 1 ? 1 : (s > 32 ? 32 : s));
 }
 
 // m-tiles per band of the grouped tile order

@@ -20,6 +20,11 @@ struct DenseLaunch {
   int b_kn;                   // 1: B is K x N; 0: B is N x K
   int epi;                    // ptg_epilogue value
   int out_f32;                // 1: float32 output; 0: bfloat16
+  // Split-K (fp32 output only): split s covers k in [s * k_chunk, (s + 1) * k_chunk) and
+  // writes its partial product to C + s * c_split elements.  splits = 1: the whole K.
+  int32_t splits = 1;
+  int64_t k_chunk = 0;
+  int64_t c_split = 0;
 };
 
 struct GroupedLaunch {
@@ -90,6 +95,12 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int kBatchBM = 128, kBatchBN = 128;
 
 hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream);
+// out[i] = sum over s of parts[s * count + i] (s ascending), plus bias[i % n] if bias.
+hipError_t launch_reduce_splits(float* out, const float* parts, int64_t count, int32_t splits,
+                                const float* bias, int64_t n, hipStream_t stream);
+// Split count of the broadcast path's user phase for a U x N product (a function of the
+// shape only, so that the workspace query and the call agree), and the maximum over K.
+int32_t broadcast_user_splits(int64_t U, int64_t N);
 hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream);
 hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream);
 // Validation of device-resident preconditions: runs a check kernel on `stream`, waits for

@@ -119,7 +119,10 @@ def test_batch_validation(L):
 def test_broadcast_validation(L):
     U, N = 4, 64
     need = L.ptg_broadcast_gemm_workspace(U, N)
-    assert need == U * N * 4
+    # P plus one partial per slice of the split user phase (one 128 x 128 tile -> 32 slices)
+    assert need == U * N * 4 * (1 + 32)
+    # a user product with 256 or more tiles runs unsplit: P alone
+    assert L.ptg_broadcast_gemm_workspace(16 * 256, 16 * 256) == 16 * 256 * 16 * 256 * 4
 
     def b(U=U, Mc=100, Ku=64, Kc=32, N=N, Xu=P, Xc=P, idx=P, W=P, layout=0, Y=P, dtype=0,
           bias=None, epi=0, ws=P, wsb=need):

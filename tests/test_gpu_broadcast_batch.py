@@ -73,6 +73,18 @@ def test_broadcast_equals_materialised_gemm():
     assert torch.equal(out, ref)
 
 
+@pytest.mark.parametrize("Ku", [8, 72, 2048, 2056])
+def test_broadcast_split_user_phase(Ku):
+    """The user product is split along Ku (up to 32 slices of whole 64-deep k-steps, the last
+    possibly short) and the partials summed in slice order: against the oracle, and
+    bit-identical from call to call (the sum does not depend on timing)."""
+    w = wl.broadcast(61 + Ku, 3, Ku, 40, 136, cmin=1, cmax=90, w_layout=wl.B_NK, with_bias=True)
+    out, v = run_broadcast(w, torch.float32, wl.EPI_BIAS)
+    check(out, v, w.Ku + w.Kc, f"broadcast split user phase Ku={Ku}")
+    again, _ = run_broadcast(w, torch.float32, wl.EPI_BIAS)
+    assert torch.equal(out, again)
+
+
 def test_broadcast_check_helper():
     idx = torch.tensor([0, 1, 4, 2], dtype=torch.int32, device="cuda")
     with pytest.raises(ptg.PtgError) as e:
