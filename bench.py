@@ -134,10 +134,11 @@ def cpu_baseline(w, np, budget_s=15.0):
     import oracle
     oracle.build(force=False)
     M, N, K = w.M, w.N, w.K
+    oracle.gemm(w.A, w.B, w.b_layout, rows=np.arange(8))  # thread pool and page-in
     t0 = time.perf_counter()
-    oracle.gemm(w.A, w.B, w.b_layout, rows=np.arange(8))
+    oracle.gemm(w.A, w.B, w.b_layout, rows=np.arange(64))
     dt = time.perf_counter() - t0
-    rows = int(max(8, min(M, 8 * budget_s / max(dt, 1e-3))))
+    rows = int(max(64, min(M, 64 * budget_s / max(dt, 1e-3))))
     t0 = time.perf_counter()
     oracle.gemm(w.A, w.B, w.b_layout, rows=np.arange(rows))
     dt = time.perf_counter() - t0
