@@ -64,12 +64,18 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // ---------------------------------------------------------------------------------------
 // Tile configuration
 // ---------------------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_, int PREG_ = 0>
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_, int PREG_ = 0,
+          bool M16_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   // k-steps a producer holds in registers ahead of the LDS ring (0: tiles go straight from
   // memory into LDS)
   static constexpr int PREG = PREG_;
+  // Matrix instruction: v_mfma_f32_16x16x32_bf16 (true) or v_mfma_f32_32x32x16_bf16 (false).
+  // Same flops per cycle; the 16x16 form moves a quarter of the accumulator registers per
+  // MFMA (a third less register traffic per flop), which on random data lets the part hold a
+  // higher clock under the same power.
+  static constexpr bool M16 = M16_;
   static constexpr int WM = WM_, WN = WN_;             // consumer waves along M and N
   static constexpr int NCONS = WM * WN, NPROD = NPROD_;
   static constexpr int NWAVES = NCONS + NPROD, NT = NWAVES * 64;
@@ -77,6 +83,8 @@ struct Cfg {
   static constexpr int WTM = BM / WM, WTN = BN / WN;    // one consumer wave's sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
   static constexpr int KSUB = BK / 16;                  // MFMA k-steps per ring slot
+  static constexpr int TM16 = WTM / 16, TN16 = WTN / 16;  // 16x16 blocks per wave (M16)
+  static constexpr int KS = BK / 32;                     // 32-deep k-slices per ring slot (M16)
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // 1 KB per DMA
@@ -98,6 +106,7 @@ struct Cfg {
   static constexpr int NINFO = STAGES + PREG + 3;
   static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "consumer sub-tile must be 32x32 blocks");
+  static_assert(!M16 || (TM16 % 2 == 0 && TN16 % 2 == 0 && BK % 32 == 0), "16x16 path: even block counts, BK of 64");
   static_assert(BK % 16 == 0 && (BK == 32 || BK == 64), "BK must be 32 or 64");
   static_assert((A_INSTR + B_INSTR) % NPROD == 0, "DMAs must split evenly over producers");
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles must be whole KB");
@@ -901,6 +910,278 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
 }
 
 // ---------------------------------------------------------------------------------------
+// Consumer role with 16x16x32 MFMAs (Cfg::M16)
+// ---------------------------------------------------------------------------------------
+// Register layout (B as the first MFMA operand, so each accumulator holds the transpose of
+// its 16 x 16 block): register t of acc[tm][tn], lane l, is row 16 tm + l % 16, column
+// 16 tn + 4 (l / 16) + t of the wave's sub-tile.  Lanes l, l + 16, l + 32, l + 48 hold
+// columns 0-3, 4-7, 8-11, 12-15 of the same row.
+
+// Start value of the accumulators: bias[col], or P[idx[row]][col] for a gathered launch.
+template <class C>
+__device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const TileInfo* ti,
+                                           const Guards* guards, int epi, int wm, int wn,
+                                           uint32_t* abort) {
+#pragma unroll
+  for (int tm = 0; tm < C::TM16; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN16; ++tn) acc[tm][tn] = f32x4{};
+  const uint64_t biasp = uni64(ti->bias);
+  const uint64_t gidxp = uni64(ti->gidx);
+  const bool gather = gidxp != 0;
+  const bool do_bias = (epi == EPI_BIAS || epi == EPI_BIAS_SILU) && biasp != 0 && !gather;
+  if (!do_bias && !gather) return true;
+  const int m_rows = (int)uni((uint32_t)ti->m_rows);
+  const int n_cols = (int)uni((uint32_t)ti->n_cols);
+  const uint64_t Pp = uni64(ti->P);
+  const int ldp = (int)uni((uint32_t)ti->ldp);
+  const uint32_t p_bytes = uni(ti->p_bytes);
+  if (m_rows < 1 || m_rows > C::BM || n_cols < 1 || n_cols > C::BN) {
+    raise_abort(abort, 2u);
+    return false;
+  }
+  const Guards& gd = *guards;
+  if ((do_bias && !inside(biasp, (uint64_t)n_cols * 4, uni64(gd.bias_lo), uni64(gd.bias_hi))) ||
+      (gather && (!inside(gidxp, (uint64_t)m_rows * 4, uni64(gd.gidx_lo), uni64(gd.gidx_hi)) ||
+                  !inside(Pp, p_bytes, uni64(gd.p_lo), uni64(gd.p_hi))))) {
+    raise_abort(abort, 8u);
+    return false;
+  }
+  const int lane = opaque_lane();
+  const int cq = (lane >> 4) * 4;  // this lane's first column within a 16-column block
+  if (do_bias) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<void*>(biasp), (uint32_t)(n_cols * 4));
+#pragma unroll
+    for (int tn = 0; tn < C::TN16; ++tn) {
+      const int col = wn * C::WTN + tn * 16 + cq;
+      const f32x4 b4 = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col < n_cols ? col * 4 : kOutOfRange, 0, 0));
+#pragma unroll
+      for (int tm = 0; tm < C::TM16; ++tm) acc[tm][tn] = b4;
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<void*>(gidxp), (uint32_t)(m_rows * 4));
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(reinterpret_cast<void*>(Pp), p_bytes);
+#pragma unroll
+    for (int tm = 0; tm < C::TM16; ++tm) {
+      const int row = wm * C::WTM + tm * 16 + (lane & 15);
+      const bool row_ok = row < m_rows;
+      const int prow = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, row_ok ? row * 4 : kOutOfRange, 0, 0);
+#pragma unroll
+      for (int tn = 0; tn < C::TN16; ++tn) {
+        const int col = wn * C::WTN + tn * 16 + cq;
+        const uint32_t po = (row_ok && col < n_cols) ? (uint32_t)(prow * ldp + col) * 4u : kOutOfRange;
+        acc[tm][tn] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, po, 0, 0));
+      }
+    }
+  }
+  return true;
+}
+
+// Epilogue: SiLU if asked, conversion, 16-byte stores.  fp32: one run of 4 columns per lane
+// and block.  bf16: runs of 4 packed to 8 bytes; for the block pairs (tn, tn + 1),
+// v_permlane16_swap trades the second 16-lane group's run of block tn against the first
+// group's run of block tn + 1 (and groups 3 and 2 likewise), after which lane group g holds
+// columns 8 (g / 2) .. + 7 of block tn + g % 2.
+template <class C>
+__device__ __forceinline__ void epilogue16(f32x4 (&acc)[C::TM16][C::TN16], int wm, int wn, int m_rows,
+                                           int n_cols, uint64_t Cp, int ldc, bool do_silu, bool f32out) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const int lane = opaque_lane();
+  const int grp = lane >> 4;
+  const int osz = f32out ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)(((m_rows - 1) * ldc + n_cols) * osz));
+#pragma unroll
+  for (int tm = 0; tm < C::TM16; ++tm) {
+    const int row = wm * C::WTM + tm * 16 + (lane & 15);
+    const bool row_ok = row < m_rows;
+#pragma unroll
+    for (int tn = 0; tn < C::TN16; tn += 2) {
+      f32x4& v0 = acc[tm][tn];
+      f32x4& v1 = acc[tm][tn + 1];
+      if (do_silu) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v0[t] = silu(v0[t]);
+          v1[t] = silu(v1[t]);
+        }
+      }
+      if (f32out) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = wn * C::WTN + (tn + h) * 16 + grp * 4;
+          const uint32_t vo = (row_ok && col < n_cols) ? (uint32_t)(row * ldc + col) * 4u : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, h ? v1 : v0), rc, vo, 0, 0);
+        }
+      } else {
+        uint32_t x0 = pack_bf16(v0[0], v0[1]), x1 = pack_bf16(v0[2], v0[3]);
+        uint32_t y0 = pack_bf16(v1[0], v1[1]), y1 = pack_bf16(v1[2], v1[3]);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+        const int col = wn * C::WTN + (tn + (grp & 1)) * 16 + (grp >> 1) * 8;
+        const uint32_t vo = (row_ok && col < n_cols) ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
+        const u32x4 d = {s0[0], s1[0], s0[1], s1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(d, rc, vo, 0, 0);
+      }
+    }
+  }
+}
+
+// The consumer loop.  Per 32-deep k-slice: 2 halves of TM16/2 row blocks.  The first half
+// runs row-major: a row block's fragment is refilled with the second half's fragment right
+// after its last MFMA.  The second half runs column-major: each B fragment is refilled with
+// the next slice's right after its last MFMA, and each A fragment with the next slice's
+// first-half fragment after the last column.  Fragments in registers: TM16/2 of A and TN16 of
+// B.  The ring slot is released as soon as the last fragment read from it has been consumed
+// (after the first column of the last slice's second half).
+template <class C>
+__device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info, uint32_t* full, uint32_t* empty,
+                                                uint32_t* abort, int cw, int epi, bool f32out,
+                                                const Guards* guards) {
+  constexpr int HM = C::TM16 / 2;
+  const int lane = lane_id();
+  const int wm = cw / C::WN, wn = cw % C::WN;
+  // A fragment (16x16x32): lane l holds row l % 16 of a 16-row block and 8 k-values from
+  // k-chunk l / 16 of the slice.  Physical chunk = (4 ks + l/16) ^ swz(row)
+  // = (4 ks) ^ (l/16 ^ swz(row)); swz depends on row % 16 only.
+  // The row starts at a multiple of 128 bytes and the chunk index occupies address bits
+  // 4-6, so slice ks (chunk XOR 4 ks) is the slice-0 offset XOR (ks << 6): one register,
+  // the XOR redone at each use (kept per slice, the variants would cost registers).
+  static_assert(C::BK == 64 || C::BK == 32, "slice offsets by XOR need rows of 64 or 32 bf16");
+  const int ra = wm * C::WTM + (lane & 15);
+  const int a_off = ra * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_A>(ra)) << 4);
+  int b_off = 0, b_kn0 = 0;
+  if constexpr (!C::B_KN) {
+    const int rb = wn * C::WTN + (lane & 15);
+    b_off = rb * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_B>(rb)) << 4);
+  } else {
+    // Transposing read per 16-lane group g: k-rows 8 g + i / 4 (and 4 further down) of the
+    // slice, columns 4 (i % 4) .. +3 of block tn; lane i receives column i.  Block tn moves
+    // the chunk index by 2 tn, which commutes with the swizzle XOR (the wave's first chunk
+    // has bits 1-2 clear): block tn reads at b_kn0 ^ (tn << 5).
+    static_assert(C::TN16 <= 4, "block offsets by XOR need 16 TN16 <= 64 columns per wave");
+    const int grp = lane >> 4, i = lane & 15;
+    const int k = grp * 8 + (i >> 2);
+    const int n = wn * C::WTN + (i & 3) * 4;
+    b_kn0 = k * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(k)) << 4) + ((n >> 2) & 1) * 8;
+  }
+  auto load_a = [&](const char* slot, int ks, int tm) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(slot + (opaque(a_off) ^ (ks << 6)) + tm * 16 * C::BK * 2);
+  };
+  auto load_b = [&](const char* slot, int ks, int tn) -> bf16x8 {
+    const char* slotB = slot + C::A_BYTES;
+    if constexpr (!C::B_KN) {
+      return *reinterpret_cast<const bf16x8*>(slotB + (opaque(b_off) ^ (ks << 6)) + tn * 16 * C::BK * 2);
+    } else {
+      const int off = opaque(b_kn0) ^ (tn << 5);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(slotB + off + ks * 32 * C::BN * 2));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(slotB + off + (ks * 32 + 4) * C::BN * 2));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  uint32_t g = 0;
+  for (int j = 0;; ++j) {
+    const int s0 = g % C::STAGES;
+    wait_at_least(&full[s0], (uint32_t)C::NPROD * (g / C::STAGES + 1), abort);
+    const TileInfo* ti = &info[j % C::NINFO];
+    const uint32_t tag = uni(ti->tag);
+    if (tag != tile_tag(j)) {
+      if (tag != end_tag(j)) raise_abort(abort, 2u);
+      lds_bump(&empty[s0]);
+      break;
+    }
+    const int K = (int)uni((uint32_t)ti->K);
+    const int nsteps = (K + C::BK - 1) / C::BK;
+    // idle wave: only takes part in the handoff (see consumer_role).  The extents are read
+    // with hand-issued LDS reads, so that no copy of them stays live across the k-loop (the
+    // epilogue reads the metadata again).
+    if (wm * C::WTM >= (int)uni(lds_peek(reinterpret_cast<const uint32_t*>(&ti->m_rows))) ||
+        wn * C::WTN >= (int)uni(lds_peek(reinterpret_cast<const uint32_t*>(&ti->n_cols)))) {
+      lds_bump(&empty[s0]);
+      ++g;
+      for (int st = 1; st < nsteps; ++st, ++g) {
+        const int s = g % C::STAGES;
+        wait_at_least(&full[s], (uint32_t)C::NPROD * (g / C::STAGES + 1), abort);
+        lds_bump(&empty[s]);
+      }
+      continue;
+    }
+
+    f32x4 acc[C::TM16][C::TN16];
+    if (!init_acc16<C>(acc, ti, guards, epi, wm, wn, abort)) break;
+
+    bf16x8 a[HM], b[C::TN16];
+    {
+      const char* slot0 = ring + s0 * C::STAGE_BYTES;
+#pragma unroll
+      for (int tn = 0; tn < C::TN16; ++tn) b[tn] = load_b(slot0, 0, tn);
+#pragma unroll
+      for (int tm = 0; tm < HM; ++tm) a[tm] = load_a(slot0, 0, tm);
+    }
+    for (int st = 0; st < nsteps; ++st, ++g) {
+      const int s = g % C::STAGES;
+      const char* slot = ring + s * C::STAGE_BYTES;
+      const bool more_steps = st + 1 < nsteps;
+      const int sn = (g + 1) % C::STAGES;
+      const char* next_slot = ring + sn * C::STAGE_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bool last_ks = ks == C::KS - 1;
+        const bool more = !last_ks || more_steps;   // a slice follows in this tile
+        const char* nslot = last_ks ? next_slot : slot;
+        const int nks = last_ks ? 0 : ks + 1;
+        __builtin_amdgcn_sched_barrier(0);
+        // first half: row blocks 0 .. HM-1, row-major; refill with the second half's rows
+#pragma unroll
+        for (int tm = 0; tm < HM; ++tm) {
+#pragma unroll
+          for (int tn = 0; tn < C::TN16; ++tn) {
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[tn], a[tm], acc[tm][tn], 0, 0, 0);
+          }
+          a[tm] = load_a(slot, ks, tm + HM);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // second half: row blocks HM .. TM16-1, column-major
+#pragma unroll
+        for (int tn = 0; tn < C::TN16; ++tn) {
+#pragma unroll
+          for (int tm = 0; tm < HM; ++tm) {
+            acc[tm + HM][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[tn], a[tm], acc[tm + HM][tn], 0, 0, 0);
+            if (tn == C::TN16 - 1 && more) a[tm] = load_a(nslot, nks, tm);
+          }
+          if (tn == 0 && last_ks) {
+            // every read of slot s has been consumed: release it, and make sure the next
+            // slot has landed before the first read from it
+            wait_lgkm0();
+            lds_bump(&empty[s]);
+            if (more) wait_at_least(&full[sn], (uint32_t)C::NPROD * ((g + 1) / C::STAGES + 1), abort);
+          }
+          if (more) b[tn] = load_b(nslot, nks, tn);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+
+    const int m_rows = (int)uni((uint32_t)ti->m_rows);
+    const int n_cols = (int)uni((uint32_t)ti->n_cols);
+    const uint64_t Cp = uni64(ti->C);
+    const int ldc = (int)uni((uint32_t)ti->ldc);
+    if (m_rows < 1 || m_rows > C::BM || n_cols < 1 || n_cols > C::BN || ldc < n_cols) {
+      raise_abort(abort, 2u);
+      break;
+    }
+    const uint64_t c_bytes = (uint64_t)((m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
+    if (!inside(Cp, c_bytes, uni64(guards->c_lo), uni64(guards->c_hi))) {
+      raise_abort(abort, 8u);
+      break;
+    }
+    epilogue16<C>(acc, wm, wn, m_rows, n_cols, Cp, ldc, epi == EPI_SILU || epi == EPI_BIAS_SILU, f32out);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------------------
 template <class C, class S>
@@ -925,7 +1206,10 @@ __global__ __launch_bounds__(C::NT, 1) void ptg_kernel(typename S::Args args) {
   const int wave = (int)uni(threadIdx.x >> 6);  // the same for every lane of a wave
   if (wave < C::NCONS) {
     __builtin_amdgcn_s_setprio(1);
-    consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
+    if constexpr (C::M16)
+      consumer_role16<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
+    else
+      consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
   } else {
     if constexpr (C::PREG == 1)
       producer_role_regs<C, S>(args, ring, info, full, empty, abort, wave - C::NCONS, sched_lds, guards);
