@@ -17,7 +17,8 @@ roofline         the GEMM kernel against MI355X's dense bf16 MFMA peak (2500 TFL
 cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload (some output
                  rows), on all host cores it uses, in the same unit
 secondary        grouped (mixture-of-experts), broadcast and batched workloads, timed the
-                 same way (TFLOP/s, % of peak, GB/s of compulsory traffic)
+                 same way (TFLOP/s, % of peak, GB/s of compulsory traffic), plus per-call
+                 cold-cache times (median, min, p90) with a 512 MB scratch write between calls
 """
 import argparse
 import hashlib
@@ -87,17 +88,44 @@ def time_calls(fn, steps, warmup, torch):
     return (t1 - t0) / steps, e0.elapsed_time(e1) / steps
 
 
-def secondary(torch, np, ptg, wl, steps, warmup):
+def time_cold(fn, reps, torch, flush_bytes=512 << 20):
+    """Per-call durations with the caches cold: before each call a 512 MB scratch buffer is
+    written (outside the event pair), which evicts the 256 MB last-level cache and the L2s.
+    Returns {median, min, p90} in milliseconds."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn()
+    pairs = []
+    for i in range(reps):
+        scratch.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in pairs)
+    del scratch
+    return {"median": round(t[len(t) // 2], 4), "min": round(t[0], 4),
+            "p90": round(t[min(len(t) - 1, (9 * len(t)) // 10)], 4), "reps": reps}
+
+
+def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
+    """Warm-cache throughput (back-to-back calls, as for the headline GEMM) plus per-call cold-cache
+    times (median, min, p90) for each of the memory-relevant workloads."""
     out = {}
     # grouped: 64 experts, 16384 rows, K=4096, N=1536, rank-Zipf(1.1) routing
     w = wl.config3("rank")
     X, W, off = to_dev(w.X, torch, np), to_dev(w.W, torch, np), torch.from_numpy(w.offsets).cuda()
     Y = torch.empty((w.M_total, w.N), dtype=torch.bfloat16, device="cuda")
-    _, ms = time_calls(lambda: ptg.grouped_gemm(X, W, off, out=Y), steps, warmup, torch)
+    call = lambda: ptg.grouped_gemm(X, W, off, out=Y)  # noqa: E731
+    _, ms = time_calls(call, steps, warmup, torch)
     f, b = wl.grouped_flops(w), wl.grouped_bytes(w)
     out["grouped_moe_64x16384x4096x1536"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS}
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
+        "cold_ms": time_cold(call, cold_reps, torch)}
     del X, W, off, Y, w
     # broadcast: 64 users, sum C_u = 81403 candidates, [2048 | 512] -> 1024
     w = wl.config4()
@@ -105,12 +133,14 @@ def secondary(torch, np, ptg, wl, steps, warmup):
                       torch.from_numpy(w.idx).cuda(), to_dev(w.W, torch, np))
     Y = torch.empty((w.Mc, w.N), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(ptg.broadcast_gemm_workspace(w.U, w.N), dtype=torch.uint8, device="cuda")
-    _, ms = time_calls(lambda: ptg.broadcast_gemm(Xu, Xc, idx, W, out=Y, workspace=ws), steps, warmup, torch)
+    call = lambda: ptg.broadcast_gemm(Xu, Xc, idx, W, out=Y, workspace=ws)  # noqa: E731
+    _, ms = time_calls(call, steps, warmup, torch)
     f, fm, b = wl.broadcast_flops(w), wl.broadcast_flops_materialised(w), wl.broadcast_bytes(w)
     out["broadcast_ikbo_64users_81403cand"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
         "effective_tflops_materialised_equivalent": fm / ms / 1e9,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS}
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
+        "cold_ms": time_cold(call, cold_reps, torch)}
     del Xu, Xc, idx, W, Y, ws, w
     # batch: 1024 independent GEMMs with fused bias + SiLU, one persistent launch
     pl = wl.config5()
@@ -121,11 +151,13 @@ def secondary(torch, np, ptg, wl, steps, warmup):
                       torch.from_numpy(p.bias).cuda()))
     ws = torch.empty(ptg.gemm_batch_workspace(len(probs)), dtype=torch.uint8, device="cuda")
     ptg.gemm_batch_prepare(probs, pl.epi, ws)
-    _, ms = time_calls(lambda: ptg.gemm_batch_run(len(probs), ws, torch.bfloat16, pl.epi), steps, warmup, torch)
+    call = lambda: ptg.gemm_batch_run(len(probs), ws, torch.bfloat16, pl.epi)  # noqa: E731
+    _, ms = time_calls(call, steps, warmup, torch)
     f, b = wl.problem_list_flops(pl), wl.problem_list_bytes(pl)
     out["batch_recsys_1024_bias_silu"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS}
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
+        "cold_ms": time_cold(call, cold_reps, torch)}
     return out
 
 
