@@ -52,7 +52,8 @@ def lib():
         L.oracle_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, i, p, i, p, i64, p]
         L.oracle_grouped_gemm.argtypes = [i32, i64, i64, i64, p, p, i, p, p, i, p, i64, p]
         L.oracle_broadcast_gemm.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, i, p, i, p, i64, p]
-        for f in (L.oracle_gemm, L.oracle_grouped_gemm, L.oracle_broadcast_gemm):
+        L.oracle_grouped_wgrad.argtypes = [i32, i64, i64, i64, p, p, p, p, i64, p]
+        for f in (L.oracle_gemm, L.oracle_grouped_gemm, L.oracle_broadcast_gemm, L.oracle_grouped_wgrad):
             f.restype = ctypes.c_int
         L.oracle_silu.argtypes = [ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
@@ -161,6 +162,23 @@ def broadcast_gemm(Xu, Xc, idx, W, w_layout: int, bias=None, epi: int = EPI_NONE
     out = np.empty((n, N), dtype=np.float64)
     _check(lib().oracle_broadcast_gemm(U, Mc, Ku, Kc, N, _ptr(Xu), _ptr(Xc), _ptr(idx), _ptr(W),
                                        w_layout, _ptr(bias), epi, _ptr(r), n, _ptr(out)))
+    return out
+
+
+def grouped_wgrad(X, dY, offsets, rows=None) -> np.ndarray:
+    """Weight gradient of the grouped GEMM: dW[g] = X_g^T . dY_g over group g's rows
+    (offsets[g] .. offsets[g+1]-1), zero for an empty group.  Returns float64 rows of dW
+    flattened to (G * K, N); `rows` selects flat row indices g * K + i."""
+    X, dY = _u16(X), _u16(dY)
+    M_total, K = X.shape
+    assert dY.shape[0] == M_total
+    N = dY.shape[1]
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+    G = off.shape[0] - 1
+    r, n = _rows(rows, G * K)
+    out = np.empty((n, N), dtype=np.float64)
+    _check(lib().oracle_grouped_wgrad(G, M_total, K, N, _ptr(X), _ptr(dY), _ptr(off), _ptr(r), n,
+                                      _ptr(out)))
     return out
 
 

@@ -17,6 +17,9 @@
  *     (How We Built TLX: "Case Study 2: In-Kernel Broadcast Optimization for RecSys", where
  *     the kernel is said to perform this broadcast implicitly; the oracle performs it
  *     literally).
+ *   - The weight gradient of the grouped form, dW_g = X_g^T . dY_g over each expert's rows,
+ *     is the same definition with the sum running over the expert's rows (same case study;
+ *     the gradient products of its pretraining use).
  *   - Epilogue: optional per-column bias, then optional SiLU(v) = v / (1 + exp(-v)).
  *
  * Arithmetic: inputs are the same bfloat16 bit patterns the GPU receives, decoded exactly;
@@ -268,4 +271,39 @@ int oracle_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t
         free(acc);
     }
     return failed ? OR_NO_MEMORY : OR_OK;
+}
+
+/* ---- grouped weight gradient ----------------------------------------------------------- *
+ * The backward pass of the expert GEMM Y_g = X_g . W_g with respect to the weights (How We
+ * Built TLX: "Case Study 3: Distributed Grouped GEMM for LLM Pretraining" names the grouped
+ * expert products of pretraining; their weight gradient is the textbook product below):
+ *     dW[g][i][j] = sum over r in [off[g], off[g+1]) of X[r][i] * dY[r][j],
+ * i.e. dW_g = X_g^T . dY_g, summed in ascending r.  A group with no rows has dW_g = 0.
+ * X is M_total x K, dY is M_total x N (both dense row-major); dW is G x K x N.  Output rows
+ * are selected by their flat index q = g * K + i in [0, G * K) (all of them, in order, when
+ * rows is NULL and nrows == G * K); out is nrows x N, dense. */
+int oracle_grouped_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t N, const uint16_t* X,
+                         const uint16_t* dY, const int32_t* off, const int64_t* rows,
+                         int64_t nrows, double* out) {
+    if (G <= 0 || M_total < 0 || K < 0 || N < 0 || !off) return OR_BAD_ARG;
+    if (off[0] != 0 || (int64_t)off[G] != M_total) return OR_BAD_OFFSETS;
+    for (int32_t g = 0; g < G; ++g)
+        if (off[g + 1] < off[g]) return OR_BAD_OFFSETS;
+    const int64_t total = (int64_t)G * K;
+    if (!rows && nrows != total) return OR_BAD_ARG;
+    for (int64_t t = 0; rows && t < nrows; ++t)
+        if (rows[t] < 0 || rows[t] >= total) return OR_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t q = rows ? rows[t] : t;
+        const int64_t g = q / K, i = q % K;
+        double* acc = out + t * N;
+        for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+        for (int64_t r = off[g]; r < (int64_t)off[g + 1]; ++r) {
+            const double x = bf16_value(X[r * K + i]);
+            const uint16_t* dyrow = dY + r * N;
+            for (int64_t j = 0; j < N; ++j) acc[j] += x * bf16_value(dyrow[j]);
+        }
+    }
+    return OR_OK;
 }

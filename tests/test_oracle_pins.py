@@ -319,6 +319,113 @@ def test_grouped_rejects_bad_offsets():
 
 
 # ---------------------------------------------------------------------------------------
+# grouped weight gradient: dW_g = X_g^T . dY_g
+# ---------------------------------------------------------------------------------------
+def test_wgrad_brute_force_tiny():
+    """Pure-Python loops over each group's rows (ascending r, double): equal to the last bit."""
+    counts = np.array([2, 0, 3, 1, 0])
+    G, K, N = len(counts), 3, 4
+    M = int(counts.sum())
+    rng = np.random.default_rng(40)
+    X, dY = rand_bf16(rng, (M, K)), rand_bf16(rng, (M, N))
+    off = _offsets(counts)
+    got = oracle.grouped_wgrad(X, dY, off).reshape(G, K, N)
+    x, dy = dec(X).tolist(), dec(dY).tolist()
+    for g in range(G):
+        for i in range(K):
+            for j in range(N):
+                s = 0.0
+                for r in range(int(off[g]), int(off[g + 1])):
+                    s += x[r][i] * dy[r][j]
+                assert got[g, i, j] == s
+
+
+def test_wgrad_vs_numpy_per_group():
+    """numpy's fp64 matmul of the transposed group slice (a library routine), empty groups
+    exactly zero."""
+    counts = np.array([37, 0, 100, 1, 64, 0, 9])
+    G, K, N = len(counts), 48, 40
+    M = int(counts.sum())
+    rng = np.random.default_rng(41)
+    X, dY = rand_bf16(rng, (M, K)), rand_bf16(rng, (M, N))
+    off = _offsets(counts)
+    got = oracle.grouped_wgrad(X, dY, off).reshape(G, K, N)
+    for g in range(G):
+        lo, hi = off[g], off[g + 1]
+        ref = dec(X[lo:hi]).T @ dec(dY[lo:hi])
+        if hi == lo:
+            assert np.array_equal(got[g], np.zeros((K, N)))
+        assert np.allclose(got[g], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_wgrad_one_hot_rows_closed_form():
+    """X[r] = e_{c(r)} (one-hot, exact in bfloat16): dW_g[i] is the sum of the dY rows of group
+    g whose hot column is i, an exact integer for integer dY."""
+    counts = np.array([5, 0, 11, 3])
+    G, K, N = len(counts), 6, 7
+    M = int(counts.sum())
+    rng = np.random.default_rng(42)
+    hot = rng.integers(0, K, M)
+    X = wl.f32_to_bf16_bits(np.eye(K, dtype=np.float32)[hot])
+    dY = int_bf16(rng, (M, N))
+    off = _offsets(counts)
+    got = oracle.grouped_wgrad(X, dY, off).reshape(G, K, N)
+    dy = dec(dY)
+    for g in range(G):
+        want = np.zeros((K, N))
+        for r in range(int(off[g]), int(off[g + 1])):
+            want[hot[r]] += dy[r]
+        assert np.array_equal(got[g], want)
+
+
+def test_wgrad_equals_gemm_of_transposed_slice_and_sums_to_full_product():
+    """Group by group equal to the oracle's plain gemm on an explicitly transposed copy of X_g
+    (same ascending order, so exactly), and the groups add up to X^T . dY over all rows."""
+    counts = np.array([20, 1, 0, 45])
+    G, K, N = len(counts), 24, 16
+    M = int(counts.sum())
+    rng = np.random.default_rng(43)
+    X, dY = int_bf16(rng, (M, K)), int_bf16(rng, (M, N))
+    off = _offsets(counts)
+    got = oracle.grouped_wgrad(X, dY, off).reshape(G, K, N)
+    for g in range(G):
+        lo, hi = off[g], off[g + 1]
+        if hi > lo:
+            assert np.array_equal(got[g], oracle.gemm(np.ascontiguousarray(X[lo:hi].T), dY[lo:hi], B_KN))
+    assert np.array_equal(got.sum(axis=0), dec(X).T @ dec(dY))
+
+
+def test_wgrad_selected_rows_and_bad_offsets():
+    counts = np.array([7, 0, 9])
+    G, K, N = len(counts), 5, 8
+    rng = np.random.default_rng(44)
+    X, dY = rand_bf16(rng, (16, K)), rand_bf16(rng, (16, N))
+    full = oracle.grouped_wgrad(X, dY, _offsets(counts))
+    sel = np.array([14, 0, 7, 3])
+    assert np.array_equal(oracle.grouped_wgrad(X, dY, _offsets(counts), rows=sel), full[sel])
+    for off in ([1, 7, 7, 16], [0, 9, 7, 16], [0, 7, 7, 15]):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.grouped_wgrad(X, dY, off)
+        assert e.value.code == 2
+
+
+def test_dgrad_is_grouped_gemm_with_transposed_weights():
+    """dX_g = dY_g . W_g^T: the grouped gemm with the K x N expert weights read as N x K
+    (layout NK) equals numpy's product with the transposed weights."""
+    counts = np.array([12, 0, 30, 5])
+    G, K, N = len(counts), 40, 24
+    M = int(counts.sum())
+    rng = np.random.default_rng(45)
+    dY = rand_bf16(rng, (M, N))
+    W = rand_bf16(rng, (G, K, N))                # forward weights, K x N per expert
+    off = _offsets(counts)
+    got = oracle.grouped_gemm(dY, W, B_NK, off)  # W[g] read as (output K) x (reduction N)
+    for g in range(G):
+        lo, hi = off[g], off[g + 1]
+        assert np.allclose(got[lo:hi], dec(dY[lo:hi]) @ dec(W[g]).T, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------
 # broadcast gemm
 # ---------------------------------------------------------------------------------------
 def test_broadcast_block_identities():
