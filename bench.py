@@ -16,8 +16,9 @@ roofline         the GEMM kernel against MI355X's dense bf16 MFMA peak (2500 TFL
                  a summary for the current kernel sources exists under profiles/, else null
 cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload (some output
                  rows), on all host cores it uses, in the same unit
-secondary        grouped (mixture-of-experts), broadcast and batched workloads, timed the
-                 same way (TFLOP/s, % of peak, GB/s of compulsory traffic), plus per-call
+secondary        grouped (mixture-of-experts) forward and weight gradient, broadcast and
+                 batched workloads, timed the same way (TFLOP/s, % of peak, GB/s of
+                 compulsory traffic), plus per-call
                  cold-cache times (median, min, p90) with a 512 MB scratch write between calls
 """
 import argparse
@@ -127,6 +128,18 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
         "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
         "cold_ms": time_cold(call, cold_reps, torch)}
     del X, W, off, Y, w
+    # weight gradient of the same MoE layer: dW_g = X_g^T . dY_g, 64 x 4096 x 1536 bf16
+    w = wl.moe_wgrad()
+    X, dY, off = to_dev(w.X, torch, np), to_dev(w.dY, torch, np), torch.from_numpy(w.offsets).cuda()
+    dW = torch.empty((w.G, w.K, w.N), dtype=torch.bfloat16, device="cuda")
+    call = lambda: ptg.grouped_gemm_wgrad(X, dY, off, out=dW)  # noqa: E731
+    _, ms = time_calls(call, steps, warmup, torch)
+    f, b = wl.wgrad_flops(w), wl.wgrad_bytes(w)
+    out["grouped_wgrad_moe_64x16384x4096x1536"] = {
+        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
+        "cold_ms": time_cold(call, cold_reps, torch)}
+    del X, dY, off, dW, w
     # broadcast: 64 users, sum C_u = 81403 candidates, [2048 | 512] -> 1024
     w = wl.config4()
     Xu, Xc, idx, W = (to_dev(w.Xu, torch, np), to_dev(w.Xc, torch, np),

@@ -103,6 +103,25 @@ ptg_status ptg_grouped_gemm_check(int32_t G, int64_t M_total, const int32_t* gro
                                   void* stream);
 
 /*
+ * ptg_grouped_gemm_wgrad - weight gradient of the grouped GEMM above, the second matrix
+ * product of its backward pass (same case study; the input gradient dX_g = dY_g . W_g^T is
+ * ptg_grouped_gemm with the forward's K x N weights passed as PTG_B_NK, N and K swapped):
+ *   dW[g] = X_g^T . dY_g,  X_g and dY_g the rows [offsets[g], offsets[g+1]) of X and dY
+ *   G             number of experts, 1 <= G <= 1024
+ *   M_total, K, N X is bf16 [M_total x K] dense (ld = K); dY is bf16 [M_total x N] dense
+ *                 (ld = N); K and N multiples of 8; M_total >= 0 (any value: the reduction
+ *                 length of expert g is its row count, which need not be a multiple of 8)
+ *   group_offsets DEVICE int32 [G + 1], same precondition as ptg_grouped_gemm
+ *   dW            [G x K x N] of dw_dtype, dense; fully overwritten, never read.  An expert
+ *                 without rows gets dW[g] = 0 (also when M_total = 0; X and dY may then be NULL).
+ * Errors: as ptg_grouped_gemm (no epilogue, no bias).  Accumulation is fp32 over the expert's
+ * rows; the result is not added to dW's previous content.
+ */
+ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t N,
+                                  const void* X, const void* dY, const int32_t* group_offsets,
+                                  void* dW, ptg_dtype dw_dtype, void* stream);
+
+/*
  * Batch of independent GEMMs in one persistent launch (the pointer-array form of the grouped
  * GEMM): problem p computes C_p = epi(A_p . B_p + bias_p) with B_p stored K x N (KN).
  * Short problems keep the pipeline full across problem boundaries ("Case Study 2", final

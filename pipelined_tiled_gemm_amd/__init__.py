@@ -20,7 +20,8 @@ from . import _ffi
 
 __all__ = [
     "PtgError", "B_KN", "B_NK", "EPI_NONE", "EPI_BIAS", "EPI_SILU", "EPI_BIAS_SILU",
-    "gemm", "grouped_gemm", "grouped_gemm_check", "gemm_batch_workspace", "gemm_batch_prepare",
+    "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "gemm_batch_workspace",
+    "gemm_batch_prepare",
     "gemm_batch_run", "gemm_batch", "broadcast_gemm_workspace", "broadcast_gemm",
     "broadcast_gemm_check", "watchdog", "version", "describe_config", "status_string",
     "last_error", "library_path",
@@ -158,6 +159,30 @@ def grouped_gemm(X: torch.Tensor, W: torch.Tensor, group_offsets: torch.Tensor, 
         _need(bias, "bias", torch.float32, 2)
     _check(_lib().ptg_grouped_gemm(G, M, N, K, _ptr(X), _ptr(W), w_layout, _ptr(group_offsets),
                                    _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi, _stream(stream)))
+    return out
+
+
+def grouped_gemm_wgrad(X: torch.Tensor, dY: torch.Tensor, group_offsets: torch.Tensor, *,
+                       out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                       stream=None) -> torch.Tensor:
+    """dW[g] = X_g^T . dY_g over rows offsets[g] <= r < offsets[g+1] (offsets on device);
+    returns dW of shape [G, K, N], zero for groups without rows."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(dY, "dY", torch.bfloat16, 2)
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    M, K = X.shape
+    if dY.shape[0] != M:
+        raise ValueError("X and dY must have the same number of rows")
+    N = dY.shape[1]
+    G = group_offsets.shape[0] - 1
+    if not (X.is_contiguous() and dY.is_contiguous() and group_offsets.is_contiguous()):
+        raise ValueError("X, dY and group_offsets must be contiguous")
+    if out is None:
+        out = torch.empty((G, K, N), dtype=out_dtype, device=X.device)
+    if not out.is_contiguous() or tuple(out.shape) != (G, K, N):
+        raise ValueError(f"out must be a contiguous [{G}, {K}, {N}] tensor")
+    _check(_lib().ptg_grouped_gemm_wgrad(G, M, K, N, _ptr(X), _ptr(dY), _ptr(group_offsets), _ptr(out),
+                                         _dtype_code(out.dtype), _stream(stream)))
     return out
 
 

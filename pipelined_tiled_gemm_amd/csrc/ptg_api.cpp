@@ -156,6 +156,41 @@ ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, co
   })
 }
 
+ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t N, const void* X,
+                                  const void* dY, const int32_t* group_offsets, void* dW,
+                                  ptg_dtype dw_dtype, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_grouped_gemm_wgrad";
+    if (G <= 0) return fail(PTG_ERR_INVALID_ARG, "%s: G must be positive", fn);
+    if (G > ptg::kMaxGroups) return fail(PTG_ERR_UNSUPPORTED, "%s: G exceeds %d", fn, ptg::kMaxGroups);
+    if (bad_dim(M_total) || bad_dim(K) || bad_dim(N))
+      return fail(PTG_ERR_INVALID_ARG, "%s: negative size (M_total=%lld K=%lld N=%lld)", fn,
+                  (long long)M_total, (long long)K, (long long)N);
+    if (K % 8 || N % 8)
+      return fail(PTG_ERR_UNSUPPORTED, "%s: K and N must be multiples of 8 (K=%lld N=%lld)", fn, (long long)K,
+                  (long long)N);
+    if (K > ptg::kMaxDim || N > ptg::kMaxDim) return fail(PTG_ERR_UNSUPPORTED, "%s: dimension too large", fn);
+    if (M_total >= ((int64_t)1 << 31)) return fail(PTG_ERR_UNSUPPORTED, "%s: M_total must fit int32 offsets", fn);
+    if (dw_dtype != PTG_BF16 && dw_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
+    if (K == 0 || N == 0) return PTG_OK;
+    if (!dW || !group_offsets || (M_total > 0 && (!X || !dY)))
+      return fail(PTG_ERR_INVALID_ARG, "%s: null operand", fn);
+    if ((X && !aligned16(X)) || (dY && !aligned16(dY)) || !aligned16(dW) ||
+        (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (offsets 4-byte)", fn);
+    // one tile's operand descriptors span up to an expert's whole row range of X and dY
+    if (!fits31(M_total, K, K) || !fits31(M_total, N, N) || !fits31(512, N, 2 * N))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand exceeds 2 GiB of addressing", fn);
+    ptg::WgradLaunch w{};
+    w.X = X; w.dY = dY; w.dW = dW; w.offsets = group_offsets;
+    w.M_total = M_total; w.K = K; w.N = N; w.G = G;
+    w.out_f32 = dw_dtype == PTG_F32;
+    hipError_t e = ptg::launch_grouped_wgrad(w, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PTG_OK;
+  })
+}
+
 ptg_status ptg_grouped_gemm_check(int32_t G, int64_t M_total, const int32_t* group_offsets, void* stream) {
   PTG_TRY({
     const char* fn = "ptg_grouped_gemm_check";

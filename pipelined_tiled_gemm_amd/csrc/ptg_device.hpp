@@ -65,7 +65,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // Tile configuration
 // ---------------------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_, int PREG_ = 0,
-          bool M16_ = false>
+          bool M16_ = false, bool A_KM_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   // k-steps a producer holds in registers ahead of the LDS ring (0: tiles go straight from
@@ -80,6 +80,9 @@ struct Cfg {
   static constexpr int NCONS = WM * WN, NPROD = NPROD_;
   static constexpr int NWAVES = NCONS + NPROD, NT = NWAVES * 64;
   static constexpr bool B_KN = B_KN_;
+  // A stored with k as the row index (K x M, M contiguous), as X^T is in a weight gradient
+  // X^T . dY: its tile is staged as BK rows of BM and read with transposing LDS reads.
+  static constexpr bool A_KM = A_KM_;
   static constexpr int WTM = BM / WM, WTN = BN / WN;    // one consumer wave's sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
   static constexpr int KSUB = BK / 16;                  // MFMA k-steps per ring slot
@@ -92,7 +95,7 @@ struct Cfg {
   // k-steps a producer keeps in flight before it waits for the oldest to land (bounded by
   // the ring and by the 6-bit vector-memory counter)
   static constexpr int INFLIGHT = (STAGES < 63 / LOADS) ? STAGES : 63 / LOADS;
-  static constexpr int CPR_A = BK / 8;                  // 16-byte chunks per A row
+  static constexpr int CPR_A = A_KM ? BM / 8 : BK / 8;  // 16-byte chunks per A row
   static constexpr int CPR_B = B_KN ? BN / 8 : BK / 8;  // 16-byte chunks per B row
   // rows covered by two consecutive 1 KB loads (one load covers 64 chunks)
   static constexpr int ROWS_A = 128 / CPR_A, ROWS_B = 128 / CPR_B;
@@ -116,7 +119,18 @@ struct Cfg {
   static_assert(PREG == 0 || PREG == 1, "0: memory to LDS; 1: one step staged in registers");
   static_assert(PREG == 0 || LOADS * 4 <= 128, "a register-staged step must fit the producer's registers");
   static_assert(NT <= 1024, "workgroup too large");
+  static_assert(!A_KM || (M16 && PREG == 1 && (TM16 & (TM16 - 1)) == 0),
+                "A stored K x M: register-staged producers and the 16x16 consumer, TM16 a power of two");
 };
+
+// k-steps of a tile with reduction length K.  A tile always has at least one step: an empty
+// reduction (K = 0, only the weight gradient of an expert without rows has one) runs one
+// step of zeros, so the ring's counting (one handoff per step) and the metadata slots'
+// lifetime rule hold for every tile, and the epilogue stores zeros.
+template <class C>
+__host__ __device__ constexpr int tile_steps(int K) {
+  return K > 0 ? (K + C::BK - 1) / C::BK : 1;
+}
 
 // Chunk swizzle for rows of BK bf16 (K contiguous), CPR chunks per row.  For 8 lanes
 // reading rows r..r+7 (and for 16 lanes reading r..r+15) at one logical chunk, the
@@ -318,8 +332,9 @@ template <class C>
 __host__ __device__ constexpr void chunk_of(int i, int lane, int& row, int& chunk) {
   if (i < C::A_INSTR) {
     const int P = i * 64 + lane;
-    row = P / C::CPR_A;
-    chunk = (P % C::CPR_A) ^ swz_k<C::CPR_A>(row);
+    row = P / C::CPR_A;  // m-row (A stored M x K) or k-row (K x M)
+    if constexpr (C::A_KM) chunk = (P % C::CPR_A) ^ swz_n<C::CPR_A>(row);
+    else chunk = (P % C::CPR_A) ^ swz_k<C::CPR_A>(row);
   } else {
     const int P = (i - C::A_INSTR) * 64 + lane;
     row = P / C::CPR_B;  // n-row (NK) or k-row (KN)
@@ -350,6 +365,7 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
                                               uint32_t* full, uint32_t* empty, uint32_t* abort, int pid,
                                               char* sched_lds, const Guards* guards) {
   static_assert(C::A_INSTR % C::LOADS == 0, "each producer copies either A or B chunks");
+  static_assert(!C::A_KM, "A stored K x M is staged through registers (producer_role_regs)");
   const int lane = lane_id();
   const int i0 = pid * C::LOADS;
   const bool opA = i0 < C::A_INSTR;                 // this producer's operand
@@ -368,7 +384,7 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
     int nsteps = 1;
     if (has) {
       const int K = t.info.K;
-      nsteps = (K + C::BK - 1) / C::BK;
+      nsteps = tile_steps<C>(K);
       if (opA) {
         src = t.A;
         src_bytes = (uint32_t)((int64_t)(t.info.m_rows - 1) * t.lda * 2 + (int64_t)K * 2);
@@ -487,8 +503,8 @@ struct FetchTile {
   int K, nsteps;
   bool has;             // false: no tile, the end marker was published
   uint32_t vbase0, vbase1;  // per-lane offsets of this producer's loads 0 and 1
-  int kbase0, kbase1;       // k (within a step) of loads 0 and 1; load q + 2 adds ROWS_B
-                            // k-rows in layout KN, nothing otherwise
+  int kbase0, kbase1;       // k (within a step) of loads 0 and 1; load q + 2 adds ROWS_A or
+                            // ROWS_B k-rows when k is the operand's row index, else nothing
 };
 
 template <class C, class S>
@@ -508,18 +524,24 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   }
   if (!f.has) return f;
   f.K = (int)uni((uint32_t)t.info.K);
-  f.nsteps = (f.K + C::BK - 1) / C::BK;
+  f.nsteps = tile_steps<C>(f.K);
   const int64_t ld = (int64_t)uni64((uint64_t)(opA ? t.lda : t.ldb));
   const int extent = (int)uni((uint32_t)(opA ? t.info.m_rows : t.info.n_cols));
   f.src = uni64(reinterpret_cast<uint64_t>(opA ? (const void*)t.A : (const void*)t.B));
-  if (opA || !C::B_KN) {
+  const bool kmajor = opA ? C::A_KM : C::B_KN;  // k is the operand's row index
+  if (!kmajor) {
     f.bytes = (uint32_t)((int64_t)(extent - 1) * ld * 2 + (int64_t)f.K * 2);
     f.kstride = 2;
   } else {
     f.bytes = (uint32_t)((int64_t)(f.K - 1) * ld * 2 + (int64_t)extent * 2);
     f.kstride = ld * 2;
   }
-  if (!inside(f.src, f.bytes, uni64(opA ? guards->a_lo : guards->b_lo), uni64(opA ? guards->a_hi : guards->b_hi))) {
+  if (f.K == 0) {
+    // an empty reduction (a weight gradient of an expert without rows): its one step is
+    // all zeros and touches no memory
+    f.src = 0;
+    f.bytes = 0;
+  } else if (!inside(f.src, f.bytes, uni64(opA ? guards->a_lo : guards->b_lo), uni64(opA ? guards->a_hi : guards->b_hi))) {
     raise_abort(abort, 4u);
     f.bytes = 0;  // every load of this tile is out of range: nothing is read
   }
@@ -532,8 +554,8 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   chunk_of<C>(i0 + 1, lane, row1, c1);
   f.vbase0 = (uint32_t)(row0 * ld * 2 + c0 * 16);
   f.vbase1 = (uint32_t)(row1 * ld * 2 + c1 * 16);
-  f.kbase0 = (!opA && C::B_KN) ? row0 : c0 * 8;  // k of the chunk's first element
-  f.kbase1 = (!opA && C::B_KN) ? row1 : c1 * 8;
+  f.kbase0 = kmajor ? row0 : c0 * 8;  // k of the chunk's first element
+  f.kbase1 = kmajor ? row1 : c1 * 8;
   f.rstep = (uint32_t)(ld * 2 * (opA ? C::ROWS_A : C::ROWS_B));
   return f;
 }
@@ -549,7 +571,7 @@ __device__ __forceinline__ void producer_role_regs(const typename S::Args& args,
   const int i0 = pid * C::LOADS;
   const bool opA = i0 < C::A_INSTR;  // this producer's operand
   const int lds_base = (opA ? i0 * 1024 : C::A_BYTES + (i0 - C::A_INSTR) * 1024) + lane * 16;
-  const int kq = (!opA && C::B_KN) ? C::ROWS_B : 0;
+  const int kq = opA ? (C::A_KM ? C::ROWS_A : 0) : (C::B_KN ? C::ROWS_B : 0);
 
   u32x4 R[C::LOADS];
   int fj = 0, fst = 0;  // tile and step the registers hold (or will hold)
@@ -745,6 +767,7 @@ template <class C>
 __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, uint32_t* full, uint32_t* empty,
                                               uint32_t* abort, int cw, int epi, bool f32out,
                                               const Guards* guards) {
+  static_assert(!C::A_KM, "A stored K x M is read by the 16x16 consumer (consumer_role16)");
   const int lane = lane_id();
   const int wm = cw / C::WN, wn = cw % C::WN;
   // A-fragment addressing: lane l holds row (l % 32) of a 32-row block and k-chunk l / 32.
@@ -790,7 +813,7 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
       break;
     }
     const int K = (int)uni((uint32_t)ti->K);
-    const int nsteps = (K + C::BK - 1) / C::BK;
+    const int nsteps = tile_steps<C>(K);
 
     // A wave whose sub-tile lies wholly outside the tile's valid rows or columns has nothing
     // to compute or store: it only takes part in the handoff, releasing each step as it
@@ -1049,8 +1072,22 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
   // 4-6, so slice ks (chunk XOR 4 ks) is the slice-0 offset XOR (ks << 6): one register,
   // the XOR redone at each use (kept per slice, the variants would cost registers).
   static_assert(C::BK == 64 || C::BK == 32, "slice offsets by XOR need rows of 64 or 32 bf16");
-  const int ra = wm * C::WTM + (lane & 15);
-  const int a_off = ra * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_A>(ra)) << 4);
+  int a_off = 0;
+  if constexpr (!C::A_KM) {
+    const int ra = wm * C::WTM + (lane & 15);
+    a_off = ra * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_A>(ra)) << 4);
+  } else {
+    // A stored K x M: the transposing read of the K x N B tile below, with m for n.  Per
+    // 16-lane group g, k-rows 8 g + i / 4 (and 4 further down) of the slice, m-columns
+    // 4 (i % 4) .. +3 of row block tm; lane i receives column i, i.e. row i of the fragment.
+    // The wave's first chunk, WTM / 8 tm-blocks of 2 chunks, is a multiple of 2 TM16 (a power
+    // of two), so block tm moves the chunk index by an XOR of 2 tm, which commutes with the
+    // swizzle XOR: block tm reads at a_off ^ (tm << 5).
+    const int grp = lane >> 4, i = lane & 15;
+    const int k = grp * 8 + (i >> 2);
+    const int m = wm * C::WTM + (i & 3) * 4;
+    a_off = k * C::BM * 2 + (((m >> 3) ^ swz_n<C::CPR_A>(k)) << 4) + ((m >> 2) & 1) * 8;
+  }
   int b_off = 0, b_kn0 = 0;
   if constexpr (!C::B_KN) {
     const int rb = wn * C::WTN + (lane & 15);
@@ -1067,7 +1104,14 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
     b_kn0 = k * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(k)) << 4) + ((n >> 2) & 1) * 8;
   }
   auto load_a = [&](const char* slot, int ks, int tm) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(slot + (opaque(a_off) ^ (ks << 6)) + tm * 16 * C::BK * 2);
+    if constexpr (!C::A_KM) {
+      return *reinterpret_cast<const bf16x8*>(slot + (opaque(a_off) ^ (ks << 6)) + tm * 16 * C::BK * 2);
+    } else {
+      const int off = opaque(a_off) ^ (tm << 5);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(slot + off + ks * 32 * C::BM * 2));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(slot + off + (ks * 32 + 4) * C::BM * 2));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
   auto load_b = [&](const char* slot, int ks, int tn) -> bf16x8 {
     const char* slotB = slot + C::A_BYTES;
@@ -1093,7 +1137,7 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
       break;
     }
     const int K = (int)uni((uint32_t)ti->K);
-    const int nsteps = (K + C::BK - 1) / C::BK;
+    const int nsteps = tile_steps<C>(K);
     // idle wave: only takes part in the handoff (see consumer_role).  The extents are read
     // with hand-issued LDS reads, so that no copy of them stays live across the k-loop (the
     // epilogue reads the metadata again).

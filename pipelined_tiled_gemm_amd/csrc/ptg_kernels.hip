@@ -6,6 +6,8 @@
 //             in device memory (How We Built TLX, "Case Study 3: Distributed Grouped GEMM for
 //             LLM Pretraining"); the per-expert tile prefix is rebuilt in LDS by every
 //             workgroup, so the host never reads the offsets.
+//   Wgrad   - the weight gradient of the grouped GEMM, dW_g = X_g^T . dY_g: a full output per
+//             expert, reduced over the expert's rows (the A operand is X read transposed).
 //   Batch   - independent problems (pointer-array form) from a table in the caller's
 //             workspace, with the tile prefix staged in LDS; the persistent workgroups run
 //             across problem boundaries without draining the ring ("Case Study 2", final
@@ -246,6 +248,88 @@ struct GroupedSched {
 };
 
 // ---------------------------------------------------------------------------------------
+// Grouped weight-gradient scheduler: dW_g = X_g^T . dY_g
+// ---------------------------------------------------------------------------------------
+// The backward counterpart of the grouped GEMM above (same case study: the expert products
+// of pretraining).  Every expert owns a full K x N output, cut into BM x BN tiles; the
+// reduction runs over the expert's rows, so a tile's cost is its expert's row count and
+// varies from nothing (an expert without rows: one step of zeros, dW_g = 0) to most of the
+// batch.  Each workgroup orders the experts by decreasing row count (ties by index) in LDS,
+// and the tiles of the heaviest experts are handed out first, in snake rounds over the
+// workgroups, so that the long reductions start early and the short ones fill in at the end.
+// Within an expert, tiles go down the m-tiles of one column strip of dY_g, then the next.
+struct WgradSched {
+  struct Args {
+    const __bf16* X;       // [M_total x K]
+    const __bf16* dY;      // [M_total x N]
+    char* dW;              // [G x K x N]
+    const int32_t* offsets;
+    int64_t M_total;
+    int32_t G, K, N, tiles_m, tiles_n;
+    int32_t epi, out_f32, out_bytes;
+    Guards guard;
+  };
+  __device__ static Guards guards(const Args& a) { return a.guard; }
+  // offsets[G + 1], experts by decreasing row count [G]
+  static constexpr int LDS_BYTES = (2 * kMaxGroups + 1) * 4 + 16;
+
+  template <class C>
+  __device__ static void init(const Args& a, char* lds) {
+    int32_t* off = reinterpret_cast<int32_t*>(lds);
+    int32_t* order = off + kMaxGroups + 1;
+    // clamped to [0, M_total] (see GroupedSched::init)
+    for (int i = threadIdx.x; i <= a.G; i += C::NT) {
+      const int64_t o = a.offsets[i];
+      off[i] = (int32_t)(o < 0 ? 0 : (o > a.M_total ? a.M_total : o));
+    }
+    __syncthreads();
+    // rank of expert g: experts with more rows, or as many and a smaller index, come first
+    for (int g = threadIdx.x; g < a.G; g += C::NT) {
+      const int cg = max(off[g + 1] - off[g], 0);
+      int rank = 0;
+      for (int h = 0; h < a.G; ++h) {
+        const int ch = max(off[h + 1] - off[h], 0);
+        rank += (ch > cg || (ch == cg && h < g)) ? 1 : 0;
+      }
+      order[rank] = g;
+    }
+    // the kernel's barrier after init publishes `order`
+  }
+
+  template <class C>
+  __device__ static bool tile(const Args& a, int j, TileSrc& t, char* lds) {
+    const int32_t* off = reinterpret_cast<const int32_t*>(lds);
+    const int32_t* order = off + kMaxGroups + 1;
+    const int r = (int)xcd_rank(blockIdx.x, gridDim.x);
+    const int64_t L = (int64_t)j * gridDim.x + ((j & 1) ? (int64_t)gridDim.x - 1 - r : r);
+    const int per = a.tiles_m * a.tiles_n;
+    if (L >= (int64_t)a.G * per) return false;
+    const int g = order[(int)(L / per)];
+    const int local = (int)(L % per);
+    const int mt = local % a.tiles_m, nt = local / a.tiles_m;
+    const int64_t row0 = off[g];
+    const int cnt = max(off[g + 1] - off[g], 0);
+    const int64_t m0 = (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
+    t.A = a.X + row0 * a.K + m0;   // X_g^T: k = row of X, m = column of X
+    t.lda = a.K;
+    t.B = a.dY + row0 * a.N + n0;
+    t.ldb = a.N;
+    t.info.tag = 0;  // set by the producer when it publishes the slot
+    t.info.K = cnt;
+    t.info.m_rows = (int)min((int64_t)C::BM, (int64_t)a.K - m0);
+    t.info.n_cols = (int)min((int64_t)C::BN, (int64_t)a.N - n0);
+    t.info.C = (uint64_t)(a.dW + (((int64_t)g * a.K + m0) * a.N + n0) * a.out_bytes);
+    t.info.ldc = a.N;
+    t.info.bias = 0;
+    t.info.gidx = 0;
+    t.info.P = 0;
+    t.info.ldp = 0;
+    t.info.p_bytes = 0;
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // Batch (pointer-array) scheduler
 // ---------------------------------------------------------------------------------------
 struct BatchSched {
@@ -305,6 +389,8 @@ struct BatchSched {
 template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN, 1, true>;
 template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN>;
 template <bool KN> using CfgGrouped = CfgLarge<KN>;
+// Weight gradient X^T . dY: the large tile with A (X^T) stored K x M and B (dY) K x N.
+using CfgWgrad = Cfg<256, 256, 64, 2, 2, 4, 4, true, 1, true, true>;
 
 struct DeviceInfo {
   int cus = 0;
@@ -479,6 +565,27 @@ static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream)
 hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream) {
   if (g.M_total == 0 || g.N == 0) return hipSuccess;
   return g.b_kn ? launch_grouped_cfg<CfgGrouped<true>>(g, stream) : launch_grouped_cfg<CfgGrouped<false>>(g, stream);
+}
+
+hipError_t launch_grouped_wgrad(const WgradLaunch& w, hipStream_t stream) {
+  using C = CfgWgrad;
+  if (w.K == 0 || w.N == 0) return hipSuccess;
+  WgradSched::Args a;
+  a.X = reinterpret_cast<const __bf16*>(w.X);
+  a.dY = reinterpret_cast<const __bf16*>(w.dY);
+  a.dW = reinterpret_cast<char*>(w.dW);
+  a.offsets = w.offsets;
+  a.M_total = w.M_total;
+  a.G = w.G; a.K = (int32_t)w.K; a.N = (int32_t)w.N;
+  a.tiles_m = (int32_t)((w.K + C::BM - 1) / C::BM);
+  a.tiles_n = (int32_t)((w.N + C::BN - 1) / C::BN);
+  a.epi = 0; a.out_f32 = w.out_f32; a.out_bytes = w.out_f32 ? 4 : 2;
+  Guards& gd = a.guard;
+  gd = Guards{};
+  span(w.X, (uint64_t)w.M_total * w.K * 2, gd.a_lo, gd.a_hi);
+  span(w.dY, (uint64_t)w.M_total * w.N * 2, gd.b_lo, gd.b_hi);
+  span(w.dW, (uint64_t)w.G * w.K * w.N * a.out_bytes, gd.c_lo, gd.c_hi);
+  return launch_persistent<C, WgradSched>(a, (int64_t)a.G * a.tiles_m * a.tiles_n, stream);
 }
 
 hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream) {

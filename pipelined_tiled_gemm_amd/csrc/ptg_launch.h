@@ -38,6 +38,16 @@ struct GroupedLaunch {
   int b_kn, epi, out_f32;
 };
 
+// Weight gradient of the grouped GEMM: dW[g] = X_g^T . dY_g over group g's rows.
+struct WgradLaunch {
+  const void* X;              // [M_total x K]
+  const void* dY;             // [M_total x N]
+  void* dW;                   // [G x K x N]
+  const int32_t* offsets;     // device [G + 1]
+  int64_t M_total, K, N;
+  int32_t G;
+  int out_f32;
+};
 // Device-side record of one problem of a batch (written by ptg_gemm_batch_prepare).
 struct BatchProblem {
   const void* A;
@@ -103,6 +113,7 @@ hipError_t launch_reduce_splits(float* out, const float* parts, int64_t count, i
 int32_t broadcast_user_splits(int64_t U, int64_t N);
 hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream);
 hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream);
+hipError_t launch_grouped_wgrad(const WgradLaunch& w, hipStream_t stream);
 // Validation of device-resident preconditions: runs a check kernel on `stream`, waits for
 // it, and sets *bad to 1 if the data violates the precondition (0 otherwise).
 hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hipStream_t stream,

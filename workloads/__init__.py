@@ -127,6 +127,20 @@ class Grouped:
 
 
 @dataclasses.dataclass
+class Wgrad:
+    """dW[g] = X_g^T . dY_g over the rows r of group g: off[g] <= r < off[g+1]."""
+    G: int
+    M_total: int
+    K: int
+    N: int
+    X: np.ndarray            # uint16 [M_total, K]
+    dY: np.ndarray           # uint16 [M_total, N]
+    counts: np.ndarray       # int64 [G]
+    offsets: np.ndarray      # int32 [G + 1]
+    out_dtype: str = "bf16"
+
+
+@dataclasses.dataclass
 class Broadcast:
     """Y[r] = epi([Xu[idx[r]] | Xc[r]].W + bias), W is (Ku + Kc) x N (KN) or N x (Ku + Kc) (NK)."""
     U: int
@@ -236,6 +250,38 @@ def config3(reading: str = "rank") -> Grouped:
     return grouped(3, 64, 16384, 4096, 1536, reading=reading)
 
 
+def wgrad(seed: int, G: int, M_total: int, K: int, N: int, *, reading: str = "rank",
+          zipf_s: float = 1.1, x_dist: str = "normal", dy_dist: str = "normal",
+          out_dtype: str = "bf16", counts: Optional[np.ndarray] = None) -> Wgrad:
+    """Weight gradient of the grouped GEMM: draw the group counts and X exactly as ``grouped``
+    does with the same seed (same routing, same activations), then dY [M_total x N] in place
+    of the weights."""
+    rng = np.random.default_rng(seed)
+    if counts is None:
+        if reading == "rank":
+            p = zipf_rank_weights(G, zipf_s)
+        elif reading == "sampled":
+            w = rng.zipf(zipf_s, G).astype(np.float64)
+            p = w / w.sum()
+        else:
+            raise ValueError(reading)
+        counts = rng.multinomial(M_total, p).astype(np.int64)
+    else:
+        counts = np.asarray(counts, dtype=np.int64)
+        assert counts.sum() == M_total and len(counts) == G
+    offsets = np.zeros(G + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    X = _draw_rows(rng, M_total, K, x_dist)
+    dY = _draw_rows(rng, M_total, N, dy_dist)
+    return Wgrad(G, M_total, K, N, X, dY, counts, offsets, out_dtype)
+
+
+def moe_wgrad(reading: str = "rank") -> Wgrad:
+    """Backward of the MoE workload: routing and X of the 64-expert, 16384-row, K = 4096,
+    N = 1536 grouped GEMM (seed 3), dY ~ N(0,1); dW is 64 x 4096 x 1536."""
+    return wgrad(3, 64, 16384, 4096, 1536, reading=reading)
+
+
 def broadcast(seed: int, U: int, Ku: int, Kc: int, N: int, *, cmin: int = 256, cmax: int = 2048,
               w_layout: int = B_KN, w_std: float = 0.02, out_dtype: str = "bf16",
               epi: int = EPI_NONE, with_bias: bool = False, shuffle: bool = False) -> Broadcast:
@@ -314,6 +360,15 @@ def grouped_flops(w: Grouped) -> float:
 def grouped_bytes(w: Grouped) -> float:
     live = int((w.counts > 0).sum())
     return 2.0 * (w.M_total * w.K + live * w.K * w.N) + out_bytes(w.out_dtype) * w.M_total * w.N
+
+
+def wgrad_flops(w: Wgrad) -> float:
+    return 2.0 * w.M_total * w.K * w.N
+
+
+def wgrad_bytes(w: Wgrad) -> float:
+    """X and dY read once, every expert's K x N gradient written (zeros for empty experts)."""
+    return 2.0 * w.M_total * (w.K + w.N) + out_bytes(w.out_dtype) * w.G * w.K * w.N
 
 
 def broadcast_flops(w: Broadcast) -> float:
