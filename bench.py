@@ -132,14 +132,15 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
     w = wl.moe_wgrad()
     X, dY, off = to_dev(w.X, torch, np), to_dev(w.dY, torch, np), torch.from_numpy(w.offsets).cuda()
     dW = torch.empty((w.G, w.K, w.N), dtype=torch.bfloat16, device="cuda")
-    call = lambda: ptg.grouped_gemm_wgrad(X, dY, off, out=dW)  # noqa: E731
+    wq = torch.empty(ptg.grouped_gemm_wgrad_workspace(), dtype=torch.uint8, device="cuda")
+    call = lambda: ptg.grouped_gemm_wgrad(X, dY, off, out=dW, workspace=wq)  # noqa: E731
     _, ms = time_calls(call, steps, warmup, torch)
     f, b = wl.wgrad_flops(w), wl.wgrad_bytes(w)
     out["grouped_wgrad_moe_64x16384x4096x1536"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
         "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
         "cold_ms": time_cold(call, cold_reps, torch)}
-    del X, dY, off, dW, w
+    del X, dY, off, dW, wq, w
     # broadcast: 64 users, sum C_u = 81403 candidates, [2048 | 512] -> 1024
     w = wl.config4()
     Xu, Xc, idx, W = (to_dev(w.Xu, torch, np), to_dev(w.Xc, torch, np),

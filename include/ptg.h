@@ -114,12 +114,18 @@ ptg_status ptg_grouped_gemm_check(int32_t G, int64_t M_total, const int32_t* gro
  *   group_offsets DEVICE int32 [G + 1], same precondition as ptg_grouped_gemm
  *   dW            [G x K x N] of dw_dtype, dense; fully overwritten, never read.  An expert
  *                 without rows gets dW[g] = 0 (also when M_total = 0; X and dY may then be NULL).
- * Errors: as ptg_grouped_gemm (no epilogue, no bias).  Accumulation is fp32 over the expert's
- * rows; the result is not added to dW's previous content.
+ *   workspace     DEVICE, 16-byte aligned, ws_bytes >= ptg_grouped_gemm_wgrad_workspace()
+ *                 (256): the queue from which the persistent workgroups take tiles.  Owned by
+ *                 the caller; its content on entry does not matter (the call resets it on
+ *                 `stream` first).  Calls that run at the same time must not share one.
+ * Errors: as ptg_grouped_gemm (no epilogue, no bias), plus PTG_ERR_WORKSPACE.  Accumulation is
+ * fp32 over the expert's rows; the result is not added to dW's previous content.
  */
+size_t ptg_grouped_gemm_wgrad_workspace(void);
 ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t N,
                                   const void* X, const void* dY, const int32_t* group_offsets,
-                                  void* dW, ptg_dtype dw_dtype, void* stream);
+                                  void* dW, ptg_dtype dw_dtype, void* workspace, size_t ws_bytes,
+                                  void* stream);
 
 /*
  * Batch of independent GEMMs in one persistent launch (the pointer-array form of the grouped

@@ -20,7 +20,8 @@ from . import _ffi
 
 __all__ = [
     "PtgError", "B_KN", "B_NK", "EPI_NONE", "EPI_BIAS", "EPI_SILU", "EPI_BIAS_SILU",
-    "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "gemm_batch_workspace",
+    "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace",
+    "gemm_batch_workspace",
     "gemm_batch_prepare",
     "gemm_batch_run", "gemm_batch", "broadcast_gemm_workspace", "broadcast_gemm",
     "broadcast_gemm_check", "watchdog", "version", "describe_config", "status_string",
@@ -162,11 +163,17 @@ def grouped_gemm(X: torch.Tensor, W: torch.Tensor, group_offsets: torch.Tensor, 
     return out
 
 
+def grouped_gemm_wgrad_workspace() -> int:
+    return int(_lib().ptg_grouped_gemm_wgrad_workspace())
+
+
 def grouped_gemm_wgrad(X: torch.Tensor, dY: torch.Tensor, group_offsets: torch.Tensor, *,
                        out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
-                       stream=None) -> torch.Tensor:
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """dW[g] = X_g^T . dY_g over rows offsets[g] <= r < offsets[g+1] (offsets on device);
-    returns dW of shape [G, K, N], zero for groups without rows."""
+    returns dW of shape [G, K, N], zero for groups without rows.  `workspace` (uint8, device,
+    at least grouped_gemm_wgrad_workspace() bytes) holds the tile queue; one is taken from
+    torch's allocator when none is given."""
     _need(X, "X", torch.bfloat16, 2)
     _need(dY, "dY", torch.bfloat16, 2)
     _need(group_offsets, "group_offsets", torch.int32, 1)
@@ -181,8 +188,11 @@ def grouped_gemm_wgrad(X: torch.Tensor, dY: torch.Tensor, group_offsets: torch.T
         out = torch.empty((G, K, N), dtype=out_dtype, device=X.device)
     if not out.is_contiguous() or tuple(out.shape) != (G, K, N):
         raise ValueError(f"out must be a contiguous [{G}, {K}, {N}] tensor")
+    if workspace is None:
+        workspace = torch.empty(grouped_gemm_wgrad_workspace(), dtype=torch.uint8, device=X.device)
     _check(_lib().ptg_grouped_gemm_wgrad(G, M, K, N, _ptr(X), _ptr(dY), _ptr(group_offsets), _ptr(out),
-                                         _dtype_code(out.dtype), _stream(stream)))
+                                         _dtype_code(out.dtype), _ptr(workspace), workspace.numel(),
+                                         _stream(stream)))
     return out
 
 

@@ -23,6 +23,7 @@ STATUS_NAMES = {
 # Every symbol include/ptg.h declares (checked by the CPU tests).
 EXPORTS = (
     "ptg_gemm", "ptg_grouped_gemm", "ptg_grouped_gemm_check", "ptg_grouped_gemm_wgrad",
+    "ptg_grouped_gemm_wgrad_workspace",
     "ptg_gemm_batch_workspace", "ptg_gemm_batch_prepare", "ptg_gemm_batch_run", "ptg_gemm_batch",
     "ptg_broadcast_gemm_workspace", "ptg_broadcast_gemm", "ptg_broadcast_gemm_check",
     "ptg_status_string", "ptg_last_error", "ptg_watchdog", "ptg_version", "ptg_describe_config",
@@ -57,7 +58,9 @@ def load(path: str = LIB_PATH):
     L.ptg_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, e, p, i64, e, p, e, p]
     L.ptg_grouped_gemm.argtypes = [i32, i64, i64, i64, p, p, e, p, p, e, p, e, p]
     L.ptg_grouped_gemm_check.argtypes = [i32, i64, p, p]
-    L.ptg_grouped_gemm_wgrad.argtypes = [i32, i64, i64, i64, p, p, p, p, e, p]
+    L.ptg_grouped_gemm_wgrad.argtypes = [i32, i64, i64, i64, p, p, p, p, e, p, sz, p]
+    L.ptg_grouped_gemm_wgrad_workspace.argtypes = []
+    L.ptg_grouped_gemm_wgrad_workspace.restype = sz
     L.ptg_gemm_batch_workspace.argtypes = [i32]
     L.ptg_gemm_batch_workspace.restype = sz
     L.ptg_gemm_batch_prepare.argtypes = [i32, ctypes.POINTER(ProblemStruct), e, p, sz, p]

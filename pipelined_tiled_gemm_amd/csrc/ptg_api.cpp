@@ -156,9 +156,11 @@ ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, co
   })
 }
 
+size_t ptg_grouped_gemm_wgrad_workspace(void) { return ptg::kWgradWorkspace; }
+
 ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t N, const void* X,
                                   const void* dY, const int32_t* group_offsets, void* dW,
-                                  ptg_dtype dw_dtype, void* stream) {
+                                  ptg_dtype dw_dtype, void* workspace, size_t ws_bytes, void* stream) {
   PTG_TRY({
     const char* fn = "ptg_grouped_gemm_wgrad";
     if (G <= 0) return fail(PTG_ERR_INVALID_ARG, "%s: G must be positive", fn);
@@ -175,14 +177,16 @@ ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t
     if (K == 0 || N == 0) return PTG_OK;
     if (!dW || !group_offsets || (M_total > 0 && (!X || !dY)))
       return fail(PTG_ERR_INVALID_ARG, "%s: null operand", fn);
-    if ((X && !aligned16(X)) || (dY && !aligned16(dY)) || !aligned16(dW) ||
+    if (!workspace || ws_bytes < ptg::kWgradWorkspace)
+      return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, ptg::kWgradWorkspace, ws_bytes);
+    if ((X && !aligned16(X)) || (dY && !aligned16(dY)) || !aligned16(dW) || !aligned16(workspace) ||
         (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
       return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (offsets 4-byte)", fn);
     // one tile's operand descriptors span up to an expert's whole row range of X and dY
     if (!fits31(M_total, K, K) || !fits31(M_total, N, N) || !fits31(512, N, 2 * N))
       return fail(PTG_ERR_UNSUPPORTED, "%s: operand exceeds 2 GiB of addressing", fn);
     ptg::WgradLaunch w{};
-    w.X = X; w.dY = dY; w.dW = dW; w.offsets = group_offsets;
+    w.X = X; w.dY = dY; w.dW = dW; w.offsets = group_offsets; w.workspace = workspace;
     w.M_total = M_total; w.K = K; w.N = N; w.G = G;
     w.out_f32 = dw_dtype == PTG_F32;
     hipError_t e = ptg::launch_grouped_wgrad(w, reinterpret_cast<hipStream_t>(stream));

@@ -65,7 +65,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // Tile configuration
 // ---------------------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_, int PREG_ = 0,
-          bool M16_ = false, bool A_KM_ = false>
+          bool M16_ = false, bool A_KM_ = false, bool STREAM_OUT_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   // k-steps a producer holds in registers ahead of the LDS ring (0: tiles go straight from
@@ -83,6 +83,10 @@ struct Cfg {
   // A stored with k as the row index (K x M, M contiguous), as X^T is in a weight gradient
   // X^T . dY: its tile is staged as BK rows of BM and read with transposing LDS reads.
   static constexpr bool A_KM = A_KM_;
+  // Output written as streaming (non-temporal) stores of whole 128-byte row segments: for
+  // outputs that are large and not read back soon (a weight gradient), where the writes
+  // bound the kernel.  16x16 consumer only.
+  static constexpr bool STREAM_OUT = STREAM_OUT_;
   static constexpr int WTM = BM / WM, WTN = BN / WN;    // one consumer wave's sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
   static constexpr int KSUB = BK / 16;                  // MFMA k-steps per ring slot
@@ -121,6 +125,7 @@ struct Cfg {
   static_assert(NT <= 1024, "workgroup too large");
   static_assert(!A_KM || (M16 && PREG == 1 && (TM16 & (TM16 - 1)) == 0),
                 "A stored K x M: register-staged producers and the 16x16 consumer, TM16 a power of two");
+  static_assert(!STREAM_OUT || (M16 && TN16 == 4), "streaming output: 16x16 consumer, 64 columns per wave");
 };
 
 // k-steps of a tile with reduction length K.  A tile always has at least one step: an empty
@@ -245,6 +250,17 @@ __device__ __forceinline__ void lds_bump(uint32_t* p) {
   }
 }
 
+__device__ __forceinline__ uint64_t lds_peek64(const uint64_t* p) {
+  uint64_t v;
+  __asm__ volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void lds_put64(uint64_t* p, uint64_t v) {
+  __asm__ volatile("" ::: "memory");
+  if (lane_id() == 0) __asm__ volatile("ds_write_b64 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
 extern __device__ uint32_t g_watchdog;
 
 // Stop the workgroup: raise its abort word (every wait returns at once) and record `why`
@@ -366,6 +382,7 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
                                               char* sched_lds, const Guards* guards) {
   static_assert(C::A_INSTR % C::LOADS == 0, "each producer copies either A or B chunks");
   static_assert(!C::A_KM, "A stored K x M is staged through registers (producer_role_regs)");
+  static_assert(!S::kDynamic, "dynamic tile queues are served by producer_role_regs");
   const int lane = lane_id();
   const int i0 = pid * C::LOADS;
   const bool opA = i0 < C::A_INSTR;                 // this producer's operand
@@ -507,6 +524,49 @@ struct FetchTile {
                             // ROWS_B k-rows when k is the operand's row index, else nothing
 };
 
+// The tile a workgroup runs as its j-th.  A static scheduler derives it from j.  A dynamic one
+// (S::kDynamic) hands out queue positions: producer 0 takes the next position from a counter
+// in global memory (one vector atomic per tile) and posts it, tagged with j + 1, in an LDS
+// slot; the other producers wait for that tag.  Slot j mod kClaimSlots is rewritten for
+// tile j + kClaimSlots only after every producer has fetched tile j: producers cannot drift
+// further apart than the ring's depth in steps, and every tile has at least one step.
+template <class C, class S>
+__device__ __forceinline__ bool schedule_tile(const typename S::Args& args, int j, int pid, TileSrc& t,
+                                              char* sched_lds, uint32_t* abort) {
+  if constexpr (!S::kDynamic) {
+    (void)pid;
+    (void)abort;
+    return S::template tile<C>(args, j, t, sched_lds);
+  } else {
+    static_assert(S::kClaimSlots >= C::NINFO + C::STAGES, "claim slots must outlive the producers' drift");
+    uint64_t* slot = S::claim_slots(sched_lds) + (j % S::kClaimSlots);
+    const uint32_t tag = (uint32_t)j + 1u;
+    uint32_t pos;
+    if (pid == 0) {
+      uint32_t got = 0;
+      if (lane_id() == 0) got = atomicAdd(args.queue, 1u);
+      pos = uni(got);
+      lds_put64(slot, ((uint64_t)tag << 32) | pos);
+    } else {
+      uint32_t polls = 0;
+      uint64_t v = lds_peek64(slot);
+      while (uni((uint32_t)(v >> 32)) != tag) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++polls & 63) == 0) {
+          if (uni(lds_peek(abort)) != 0) return false;
+          if (polls >= kSpinLimit) {
+            raise_abort(abort, 1u);
+            return false;
+          }
+        }
+        v = lds_peek64(slot);
+      }
+      pos = uni((uint32_t)v);
+    }
+    return S::template tile_at<C>(args, pos, t, sched_lds);
+  }
+}
+
 template <class C, class S>
 __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, int j, int pid, bool opA,
                                                 int i0, char* sched_lds, TileInfo* info,
@@ -516,7 +576,7 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   FetchTile f = {};
   // Every value is the same across the wave; saying so keeps the fetch state in scalar
   // registers (a scheduler may read LDS, whose loads the compiler treats as per-lane).
-  f.has = uni(S::template tile<C>(args, j, t, sched_lds) ? 1u : 0u) != 0;
+  f.has = uni(schedule_tile<C, S>(args, j, pid, t, sched_lds, abort) ? 1u : 0u) != 0;
   if (pid == 0 && lane == 0) {
     TileInfo ti = t.info;
     ti.tag = f.has ? tile_tag(j) : end_tag(j);
@@ -1001,6 +1061,35 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
   return true;
 }
 
+// Streaming stores of 16 rows as whole 128-byte segments.  On entry lane (g, r) of the wave
+// (16-lane group g, row r of 16) holds 16-byte runs X and Y of row r, at columns colX and colY;
+// for each row the four groups' X runs are 64 contiguous bytes and their Y runs the next 64.
+// Lanes r and r ^ 8 trade (a DPP rotation by 8 within each 16-lane row), so that one store
+// writes rows 0-7 and the other rows 8-15, each as 128 contiguous bytes.  Rows at or past
+// m_rows, and runs at or past n_cols, take an out-of-range offset (the store is dropped).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+__device__ __forceinline__ void store_rows128(u32x4_t X, u32x4_t Y, int colX, int colY, int row0, int lane,
+                                              int m_rows, int n_cols, int ldc, uint32_t osz,
+                                              __amdgpu_buffer_rsrc_t rc) {
+  const bool lo = (lane & 8) == 0;
+  u32x4_t A, B;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t xr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)X[q], 0x128, 0xF, 0xF, false);  // row_ror:8
+    const uint32_t yr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)Y[q], 0x128, 0xF, 0xF, false);
+    A[q] = lo ? X[q] : yr;
+    B[q] = lo ? xr : Y[q];
+  }
+  const int col = lo ? colX : colY;
+  const int rowA = row0 + (lane & 7), rowB = rowA + 8;
+  const bool col_ok = col < n_cols;
+  const uint32_t vA = (rowA < m_rows && col_ok) ? (uint32_t)(rowA * ldc + col) * osz : kOutOfRange;
+  const uint32_t vB = (rowB < m_rows && col_ok) ? (uint32_t)(rowB * ldc + col) * osz : kOutOfRange;
+  // cache policy 2: non-temporal
+  __builtin_amdgcn_raw_buffer_store_b128(A, rc, vA, 0, 2);
+  __builtin_amdgcn_raw_buffer_store_b128(B, rc, vB, 0, 2);
+}
+
 // Epilogue: SiLU if asked, conversion, 16-byte stores.  fp32: one run of 4 columns per lane
 // and block.  bf16: runs of 4 packed to 8 bytes; for the block pairs (tn, tn + 1),
 // v_permlane16_swap trades the second 16-lane group's run of block tn against the first
@@ -1019,6 +1108,42 @@ __device__ __forceinline__ void epilogue16(f32x4 (&acc)[C::TM16][C::TN16], int w
   for (int tm = 0; tm < C::TM16; ++tm) {
     const int row = wm * C::WTM + tm * 16 + (lane & 15);
     const bool row_ok = row < m_rows;
+    if constexpr (C::STREAM_OUT) {
+      // fp32: blocks tn and tn + 1 of a row are 128 contiguous bytes; bf16: the two block
+      // pairs after the group trade below are
+      const int row0 = wm * C::WTM + tm * 16;
+      u32x4 pair0 = {};
+#pragma unroll
+      for (int tn = 0; tn < C::TN16; tn += 2) {
+        f32x4& v0 = acc[tm][tn];
+        f32x4& v1 = acc[tm][tn + 1];
+        if (do_silu) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v0[t] = silu(v0[t]);
+            v1[t] = silu(v1[t]);
+          }
+        }
+        if (f32out) {
+          const int colX = wn * C::WTN + tn * 16 + grp * 4;
+          store_rows128(__builtin_bit_cast(u32x4, v0), __builtin_bit_cast(u32x4, v1), colX, colX + 16, row0,
+                        lane, m_rows, n_cols, ldc, 4u, rc);
+        } else {
+          const uint32_t x0 = pack_bf16(v0[0], v0[1]), x1 = pack_bf16(v0[2], v0[3]);
+          const uint32_t y0 = pack_bf16(v1[0], v1[1]), y1 = pack_bf16(v1[2], v1[3]);
+          const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+          const u32x4 d = {s0[0], s1[0], s0[1], s1[1]};
+          if (tn == 0) {
+            pair0 = d;
+          } else {
+            const int colX = wn * C::WTN + (grp & 1) * 16 + (grp >> 1) * 8;
+            store_rows128(pair0, d, colX, colX + 32, row0, lane, m_rows, n_cols, ldc, 2u, rc);
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int tn = 0; tn < C::TN16; tn += 2) {
       f32x4& v0 = acc[tm][tn];

@@ -54,6 +54,7 @@ struct DenseSched {
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
   static constexpr int LDS_BYTES = 16;
+  static constexpr bool kDynamic = false;
 
   template <class C>
   __device__ static void init(const Args&, char*) {}
@@ -168,6 +169,7 @@ struct GroupedSched {
   __device__ static Guards guards(const Args& a) { return a.guard; }
   // offsets[G + 1], full-tile prefix[G + 1], half-tile prefix[G + 1], scan scratch
   static constexpr int LDS_BYTES = 3 * (kMaxGroups + 1) * 4 + 20 * 4;
+  static constexpr bool kDynamic = false;
 
   // full (more than BM/2 valid rows) and half m-tiles of a group of cnt rows
   template <class C>
@@ -254,9 +256,13 @@ struct GroupedSched {
 // of pretraining).  Every expert owns a full K x N output, cut into BM x BN tiles; the
 // reduction runs over the expert's rows, so a tile's cost is its expert's row count and
 // varies from nothing (an expert without rows: one step of zeros, dW_g = 0) to most of the
-// batch.  Each workgroup orders the experts by decreasing row count (ties by index) in LDS,
-// and the tiles of the heaviest experts are handed out first, in snake rounds over the
-// workgroups, so that the long reductions start early and the short ones fill in at the end.
+// batch, while every tile writes the same BM x BN output.  A static assignment cannot balance
+// such costs without knowing the row counts, which live on the device, so the workgroups take
+// tiles from a queue (one counter in the caller's workspace, reset by a one-thread kernel
+// before the launch).  Queue positions alternate between the heaviest and the lightest tile
+// not yet handed out (experts ordered by row count in LDS by every workgroup): the long
+// reductions start early, and the cheap, store-heavy tiles are spread over the whole run
+// instead of crowding its end, which keeps the output writes overlapped with the matrix work.
 // Within an expert, tiles go down the m-tiles of one column strip of dY_g, then the next.
 struct WgradSched {
   struct Args {
@@ -264,19 +270,26 @@ struct WgradSched {
     const __bf16* dY;      // [M_total x N]
     char* dW;              // [G x K x N]
     const int32_t* offsets;
+    uint32_t* queue;       // tile-queue counter (workspace), 0 at launch
     int64_t M_total;
     int32_t G, K, N, tiles_m, tiles_n;
     int32_t epi, out_f32, out_bytes;
     Guards guard;
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
-  // offsets[G + 1], experts by decreasing row count [G]
-  static constexpr int LDS_BYTES = (2 * kMaxGroups + 1) * 4 + 16;
+  static constexpr bool kDynamic = true;
+  static constexpr int kClaimSlots = 16;
+  // claim slots [16] (8-byte aligned first), offsets[G + 1], experts by decreasing row count [G]
+  static constexpr int LDS_BYTES = kClaimSlots * 8 + (2 * kMaxGroups + 1) * 4 + 16;
+  __device__ static uint64_t* claim_slots(char* lds) { return reinterpret_cast<uint64_t*>(lds); }
+  __device__ static int32_t* offsets_lds(char* lds) { return reinterpret_cast<int32_t*>(lds + kClaimSlots * 8); }
 
   template <class C>
   __device__ static void init(const Args& a, char* lds) {
-    int32_t* off = reinterpret_cast<int32_t*>(lds);
+    uint64_t* slots = claim_slots(lds);
+    int32_t* off = offsets_lds(lds);
     int32_t* order = off + kMaxGroups + 1;
+    if (threadIdx.x < kClaimSlots) slots[threadIdx.x] = 0;  // no tag matches before a claim
     // clamped to [0, M_total] (see GroupedSched::init)
     for (int i = threadIdx.x; i <= a.G; i += C::NT) {
       const int64_t o = a.offsets[i];
@@ -293,19 +306,21 @@ struct WgradSched {
       }
       order[rank] = g;
     }
-    // the kernel's barrier after init publishes `order`
+    // the kernel's barrier after init publishes `order` and the cleared slots
   }
 
+  // The tile at queue position q: positions alternate between the front (heaviest) and the
+  // back (lightest) of the tiles ordered by cost.
   template <class C>
-  __device__ static bool tile(const Args& a, int j, TileSrc& t, char* lds) {
-    const int32_t* off = reinterpret_cast<const int32_t*>(lds);
+  __device__ static bool tile_at(const Args& a, uint32_t q, TileSrc& t, char* lds) {
+    const int32_t* off = offsets_lds(lds);
     const int32_t* order = off + kMaxGroups + 1;
-    const int r = (int)xcd_rank(blockIdx.x, gridDim.x);
-    const int64_t L = (int64_t)j * gridDim.x + ((j & 1) ? (int64_t)gridDim.x - 1 - r : r);
     const int per = a.tiles_m * a.tiles_n;
-    if (L >= (int64_t)a.G * per) return false;
-    const int g = order[(int)(L / per)];
-    const int local = (int)(L % per);
+    const int64_t T = (int64_t)a.G * per;
+    if ((int64_t)q >= T) return false;
+    const int64_t p = (q & 1u) ? T - 1 - (int64_t)(q >> 1) : (int64_t)(q >> 1);
+    const int g = order[(int)(p / per)];
+    const int local = (int)(p % per);
     const int mt = local % a.tiles_m, nt = local / a.tiles_m;
     const int64_t row0 = off[g];
     const int cnt = max(off[g + 1] - off[g], 0);
@@ -329,6 +344,11 @@ struct WgradSched {
   }
 };
 
+// Resets a tile-queue counter (one vector store) ahead of the kernel that drains it.
+__global__ void arm_queue_kernel(uint32_t* queue) {
+  if (threadIdx.x == 0) queue[0] = 0;
+}
+
 // ---------------------------------------------------------------------------------------
 // Batch (pointer-array) scheduler
 // ---------------------------------------------------------------------------------------
@@ -342,6 +362,7 @@ struct BatchSched {
   };
   __device__ static Guards guards(const Args& a) { return *a.guard_ptr; }
   static constexpr int LDS_BYTES = (kMaxBatch + 1) * 4 + 16;
+  static constexpr bool kDynamic = false;
 
   template <class C>
   __device__ static void init(const Args& a, char* lds) {
@@ -389,8 +410,9 @@ struct BatchSched {
 template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN, 1, true>;
 template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN>;
 template <bool KN> using CfgGrouped = CfgLarge<KN>;
-// Weight gradient X^T . dY: the large tile with A (X^T) stored K x M and B (dY) K x N.
-using CfgWgrad = Cfg<256, 256, 64, 2, 2, 4, 4, true, 1, true, true>;
+// Weight gradient X^T . dY: the large tile with A (X^T) stored K x M and B (dY) K x N, its
+// output (a full K x N per expert, the bulk of the traffic) written as streaming stores.
+using CfgWgrad = Cfg<256, 256, 64, 2, 2, 4, 4, true, 1, true, true, true>;
 
 struct DeviceInfo {
   int cus = 0;
@@ -575,6 +597,7 @@ hipError_t launch_grouped_wgrad(const WgradLaunch& w, hipStream_t stream) {
   a.dY = reinterpret_cast<const __bf16*>(w.dY);
   a.dW = reinterpret_cast<char*>(w.dW);
   a.offsets = w.offsets;
+  a.queue = reinterpret_cast<uint32_t*>(w.workspace);
   a.M_total = w.M_total;
   a.G = w.G; a.K = (int32_t)w.K; a.N = (int32_t)w.N;
   a.tiles_m = (int32_t)((w.K + C::BM - 1) / C::BM);
@@ -585,6 +608,9 @@ hipError_t launch_grouped_wgrad(const WgradLaunch& w, hipStream_t stream) {
   span(w.X, (uint64_t)w.M_total * w.K * 2, gd.a_lo, gd.a_hi);
   span(w.dY, (uint64_t)w.M_total * w.N * 2, gd.b_lo, gd.b_hi);
   span(w.dW, (uint64_t)w.G * w.K * w.N * a.out_bytes, gd.c_lo, gd.c_hi);
+  hipLaunchKernelGGL(arm_queue_kernel, dim3(1), dim3(64), 0, stream, a.queue);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return launch_persistent<C, WgradSched>(a, (int64_t)a.G * a.tiles_m * a.tiles_n, stream);
 }
 

@@ -44,10 +44,12 @@ struct WgradLaunch {
   const void* dY;             // [M_total x N]
   void* dW;                   // [G x K x N]
   const int32_t* offsets;     // device [G + 1]
+  void* workspace;            // kWgradWorkspace bytes: the tile-queue counter
   int64_t M_total, K, N;
   int32_t G;
   int out_f32;
 };
+constexpr size_t kWgradWorkspace = 256;
 // Device-side record of one problem of a batch (written by ptg_gemm_batch_prepare).
 struct BatchProblem {
   const void* A;

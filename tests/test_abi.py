@@ -137,6 +137,30 @@ def test_broadcast_validation(L):
     assert b(Mc=0, Xu=None, Xc=None, idx=None, W=None, Y=None, ws=None, wsb=0) == OK
 
 
+def test_wgrad_validation(L):
+    need = L.ptg_grouped_gemm_wgrad_workspace()
+    assert need == 256
+
+    def w(G=4, M=100, K=64, N=32, X=P, dY=P, off=P, dW=P, dtype=0, ws=P, wsb=need):
+        return L.ptg_grouped_gemm_wgrad(G, M, K, N, X, dY, off, dW, dtype, ws, wsb, None)
+    assert w(G=0) == INVALID
+    assert w(G=1025) == UNSUPPORTED
+    assert w(M=-1) == INVALID
+    assert w(K=12) == UNSUPPORTED
+    assert w(N=20) == UNSUPPORTED
+    assert w(dtype=7) == UNSUPPORTED
+    assert w(X=None) == INVALID
+    assert w(off=None) == INVALID
+    assert w(dW=None) == INVALID
+    assert w(ws=None) == WORKSPACE
+    assert w(wsb=need - 1) == WORKSPACE
+    assert w(ws=P + 8) == UNSUPPORTED
+    assert w(off=P + 2) == UNSUPPORTED
+    assert w(M=1 << 31) == UNSUPPORTED
+    assert w(K=0, X=None, dY=None, dW=None, off=None, ws=None) == OK   # empty output: no-op
+    assert w(N=0, X=None, dY=None, dW=None, off=None, ws=None) == OK
+
+
 def test_describe_config(L):
     cfg = (ctypes.c_int32 * 6)()
     assert L.ptg_describe_config(8192, 8192, 8192, 1, cfg) == OK

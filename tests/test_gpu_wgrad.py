@@ -3,7 +3,8 @@
 Weight gradient dW_g = X_g^T . dY_g (ptg_grouped_gemm_wgrad): the reduction runs over each
 expert's rows, so the cases cover empty experts (dW_g = 0), experts of one row, reduction
 tails that are not multiples of 8, ragged m and n tiles, and (at full size) the 64-expert
-Zipf(1.1) routing of the forward workload.  Input gradient dX_g = dY_g . W_g^T is the grouped
+Zipf(1.1) routing of the forward workload; the workgroups take tiles from a queue in a small
+caller workspace, whose prior content must not matter.  Input gradient dX_g = dY_g . W_g^T is the grouped
 GEMM with the forward weights read as N x K.
 """
 import numpy as np
@@ -137,12 +138,30 @@ def test_wgrad_repeat_is_bit_identical():
     assert torch.equal(a, b)
 
 
+def test_wgrad_workspace_content_does_not_matter():
+    """The tile queue is reset on the stream before every launch: a workspace full of arbitrary
+    bytes, and one reused by back-to-back calls, give the same bits."""
+    w = wl.wgrad(68, len(COUNTS), int(COUNTS.sum()), 520, 392, counts=COUNTS)
+    X, dY, off = dev_bf16(w.X), dev_bf16(w.dY), dev(w.offsets)
+    ws = torch.full((ptg.grouped_gemm_wgrad_workspace(),), 0xA5, dtype=torch.uint8, device="cuda")
+    a = ptg.grouped_gemm_wgrad(X, dY, off, out_dtype=torch.float32, workspace=ws)
+    ws.fill_(0xFF)
+    b = ptg.grouped_gemm_wgrad(X, dY, off, out_dtype=torch.float32, workspace=ws)
+    c = ptg.grouped_gemm_wgrad(X, dY, off, out_dtype=torch.float32, workspace=ws)
+    assert torch.equal(a, b) and torch.equal(b, c)
+    check(a.reshape(w.G * w.K, w.N), oracle.grouped_wgrad(w.X, w.dY, w.offsets), int(COUNTS.max()), "workspace")
+
+
 def test_wgrad_rejects_bad_arguments():
     X = torch.zeros((16, 12), dtype=torch.bfloat16, device="cuda")  # K = 12: not a multiple of 8
     dY = torch.zeros((16, 8), dtype=torch.bfloat16, device="cuda")
     off = dev(np.array([0, 16], np.int32))
     with pytest.raises(ptg.PtgError):
         ptg.grouped_gemm_wgrad(X, dY, off)
+    X = torch.zeros((16, 16), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ptg.PtgError):
+        ptg.grouped_gemm_wgrad(X, dY, off, workspace=small)
 
 
 def test_dgrad_is_grouped_gemm_nk():
