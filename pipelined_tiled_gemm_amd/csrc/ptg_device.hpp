@@ -150,15 +150,18 @@ __host__ __device__ constexpr int swz_k(int r) {
   }
 }
 
-// Chunk swizzle for rows of BN bf16 (N contiguous, layout KN), CPR chunks per row.  A
-// transposing read takes 4 consecutive k-rows x 32 bytes per 16 lanes; the XOR values of
-// 4 consecutive rows differ in bits 1-2 and in bits 2-3 so that both 16- and 32-lane
-// service groups see distinct banks.
+// Chunk swizzle for rows of BN bf16 (N contiguous, layout KN; also A stored K x M), CPR
+// chunks per row.  A transposing read takes 4 consecutive k-rows x 32 bytes per 16 lanes; the
+// XOR values of 4 consecutive rows differ in bits 1-2 and in bits 2-3 so that both 16- and
+// 32-lane service groups see distinct banks.  Bit 3 of k flips bit 1 of the XOR: the 16x16
+// consumer's two 16-lane groups of a 32-lane service group read the same columns of rows
+// 8 apart (k-values 0-7 and 8-15 of a 32-deep slice), which then land on the other 8 chunk
+// pairs of the row instead of the same banks.
 template <int CPR>
 __host__ __device__ constexpr int swz_n(int k) {
   if constexpr (CPR >= 16) {
-    const int m = k & 3;  // 0, 6, 10, 12 for m = 0..3
-    return ((m & 1) * 6) ^ ((m & 2) * 5);
+    const int m = k & 3;  // 0, 6, 10, 12 for m = 0..3, then XOR 2 when bit 3 of k is set
+    return ((m & 1) * 6) ^ ((m & 2) * 5) ^ (((k >> 3) & 1) << 1);
   } else {
     static_assert(CPR == 8, "BN of 64 or more");
     return (k & 3) << 1;
@@ -359,18 +362,30 @@ __host__ __device__ constexpr void chunk_of(int i, int lane, int& row, int& chun
   }
 }
 
-// The chunk pattern of load index i repeats every two loads, shifted by ROWS rows: for every
-// lane, load i + 2 fetches the same chunk as load i, ROWS_A (A) or ROWS_B (B) rows further on.
-// Checked at compile time for each configuration that stages through registers.
+// Load q of a producer (index i0 + q) fetches, for every lane, the chunk of load q mod 2 (its
+// first two loads), (q / 2) ROWS_A or ROWS_B rows further on; for an operand stored with k as
+// the row index the chunk also flips bit 1 when bit 2 of q is set (bit 3 of the k-row, see
+// swz_n).  Two per-lane bases, a row step and a per-lane flip offset then describe all of a
+// producer's loads.  Checked at compile time for each configuration that stages through
+// registers.
 template <class C>
-constexpr bool chunk_period2() {
-  for (int i = 0; i + 2 < C::A_INSTR + C::B_INSTR; ++i) {
-    if ((i < C::A_INSTR) != (i + 2 < C::A_INSTR)) continue;
-    for (int lane = 0; lane < 64; ++lane) {
-      int r0 = 0, c0 = 0, r2 = 0, c2 = 0;
-      chunk_of<C>(i, lane, r0, c0);
-      chunk_of<C>(i + 2, lane, r2, c2);
-      if (c2 != c0 || r2 != r0 + (i < C::A_INSTR ? C::ROWS_A : C::ROWS_B)) return false;
+constexpr bool load_flip(int i, int q) {
+  return ((i < C::A_INSTR) ? C::A_KM : C::B_KN) && ((q >> 2) & 1);
+}
+
+template <class C>
+constexpr bool chunk_pattern_ok() {
+  for (int p = 0; p < C::NPROD; ++p) {
+    const int i0 = p * C::LOADS;
+    for (int q = 0; q < C::LOADS; ++q) {
+      const int i = i0 + q;
+      const int rows = (i < C::A_INSTR) ? C::ROWS_A : C::ROWS_B;
+      for (int lane = 0; lane < 64; ++lane) {
+        int rb = 0, cb = 0, r = 0, c = 0;
+        chunk_of<C>(i0 + (q & 1), lane, rb, cb);
+        chunk_of<C>(i, lane, r, c);
+        if (r != rb + (q >> 1) * rows || c != (cb ^ (load_flip<C>(i, q) ? 2 : 0))) return false;
+      }
     }
   }
   return true;
@@ -520,6 +535,7 @@ struct FetchTile {
   int K, nsteps;
   bool has;             // false: no tile, the end marker was published
   uint32_t vbase0, vbase1;  // per-lane offsets of this producer's loads 0 and 1
+  int32_t vflip0, vflip1;   // byte offset added to load q (parity 0 or 1) when it flips (load_flip)
   int kbase0, kbase1;       // k (within a step) of loads 0 and 1; load q + 2 adds ROWS_A or
                             // ROWS_B k-rows when k is the operand's row index, else nothing
 };
@@ -607,17 +623,27 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   }
   // Rows and columns beyond the tile lie beyond the descriptor (a row past the last valid
   // one starts past its end) or in columns the epilogue never stores, so only the k tail
-  // needs masking.  Chunk offsets repeat with period 2 in the load index (chunk_period2),
-  // so two per-lane bases and a row step describe all of them.
+  // needs masking.  Two per-lane bases, a row step and a per-lane flip offset describe every
+  // load's offset (chunk_pattern_ok).
   int row0 = 0, c0 = 0, row1 = 0, c1 = 0;
   chunk_of<C>(i0, lane, row0, c0);
   chunk_of<C>(i0 + 1, lane, row1, c1);
   f.vbase0 = (uint32_t)(row0 * ld * 2 + c0 * 16);
   f.vbase1 = (uint32_t)(row1 * ld * 2 + c1 * 16);
+  f.vflip0 = kmajor ? ((c0 ^ 2) - c0) * 16 : 0;
+  f.vflip1 = kmajor ? ((c1 ^ 2) - c1) * 16 : 0;
   f.kbase0 = kmajor ? row0 : c0 * 8;  // k of the chunk's first element
   f.kbase1 = kmajor ? row1 : c1 * 8;
   f.rstep = (uint32_t)(ld * 2 * (opA ? C::ROWS_A : C::ROWS_B));
   return f;
+}
+
+// Byte offset of a producer's load q within the step (see chunk_pattern_ok); q is a
+// compile-time index after unrolling, so the flip is a compile-time choice.
+template <class C>
+__device__ __forceinline__ uint32_t load_off(const FetchTile& f, int q) {
+  const uint32_t base = ((q & 1) ? f.vbase1 : f.vbase0) + (uint32_t)(q >> 1) * f.rstep;
+  return ((q >> 2) & 1) ? base + (uint32_t)((q & 1) ? f.vflip1 : f.vflip0) : base;
 }
 
 template <class C, class S>
@@ -626,7 +652,7 @@ __device__ __forceinline__ void producer_role_regs(const typename S::Args& args,
                                                    char* sched_lds, const Guards* guards) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   static_assert(C::A_INSTR % C::LOADS == 0, "each producer copies either A or B chunks");
-  static_assert(C::LOADS % 2 == 0 && chunk_period2<C>(), "load offsets must repeat every two loads");
+  static_assert(C::LOADS % 2 == 0 && chunk_pattern_ok<C>(), "load offsets must follow the two-base pattern");
   const int lane = lane_id();
   const int i0 = pid * C::LOADS;
   const bool opA = i0 < C::A_INSTR;  // this producer's operand
@@ -646,12 +672,12 @@ __device__ __forceinline__ void producer_role_regs(const typename S::Args& args,
       if (k0 + C::BK <= f.K) {
 #pragma unroll
         for (int q = 0; q < C::LOADS; ++q)
-          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((q & 1) ? f.vbase1 : f.vbase0) + (uint32_t)(q >> 1) * f.rstep, 0, 0);
+          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, load_off<C>(f, q), 0, 0);
       } else {
 #pragma unroll
         for (int q = 0; q < C::LOADS; ++q) {
           const int kpos = ((q & 1) ? f.kbase1 : f.kbase0) + (q >> 1) * kq;
-          const uint32_t vo = ((q & 1) ? f.vbase1 : f.vbase0) + (uint32_t)(q >> 1) * f.rstep;
+          const uint32_t vo = load_off<C>(f, q);
           R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, k0 + kpos < f.K ? vo : kOutOfRange, 0, 0);
         }
       }
