@@ -541,9 +541,9 @@ struct FetchTile {
 };
 
 // The tile a workgroup runs as its j-th.  A static scheduler derives it from j.  A dynamic one
-// (S::kDynamic) hands out queue positions: producer 0 takes the next position from a counter
-// in global memory (one vector atomic per tile) and posts it, tagged with j + 1, in an LDS
-// slot; the other producers wait for that tag.  Slot j mod kClaimSlots is rewritten for
+// (S::kDynamic) hands out tickets: producer 0 takes the next one from counters in global
+// memory (S::claim, vector atomics) and posts it, tagged with j + 1, in an LDS slot; the other
+// producers wait for that tag.  Slot j mod kClaimSlots is rewritten for
 // tile j + kClaimSlots only after every producer has fetched tile j: producers cannot drift
 // further apart than the ring's depth in steps, and every tile has at least one step.
 template <class C, class S>
@@ -560,7 +560,7 @@ __device__ __forceinline__ bool schedule_tile(const typename S::Args& args, int 
     uint32_t pos;
     if (pid == 0) {
       uint32_t got = 0;
-      if (lane_id() == 0) got = atomicAdd(args.queue, 1u);
+      if (lane_id() == 0) got = S::claim(args);
       pos = uni(got);
       lds_put64(slot, ((uint64_t)tag << 32) | pos);
     } else {

@@ -258,27 +258,37 @@ struct GroupedSched {
 // varies from nothing (an expert without rows: one step of zeros, dW_g = 0) to most of the
 // batch, while every tile writes the same BM x BN output.  A static assignment cannot balance
 // such costs without knowing the row counts, which live on the device, so the workgroups take
-// tiles from a queue (one counter in the caller's workspace, reset by a one-thread kernel
-// before the launch).  Queue positions alternate between the heaviest and the lightest tile
-// not yet handed out (experts ordered by row count in LDS by every workgroup): the long
-// reductions start early, and the cheap, store-heavy tiles are spread over the whole run
-// instead of crowding its end, which keeps the output writes overlapped with the matrix work.
-// Within an expert, tiles go down the m-tiles of one column strip of dY_g, then the next.
+// tiles from queues (counters in the caller's workspace, reset by a small kernel before the
+// launch).
+//   - One queue per XCD.  Queue x holds block x of every expert's tile grid: the m-tiles are
+//     cut into pm blocks and the n-tiles into pn blocks (pm * pn = 8, chosen by the host to
+//     minimise pn |X| + pm |dY|), so a slice of X_g is fetched into pn L2s and a slice of dY_g
+//     into pm, instead of into whichever XCDs happen to take its tiles.  A workgroup takes
+//     from its own XCD's queue, and from the others in turn once that one is drained.
+//   - Within a queue, positions alternate between the heaviest and the lightest tile not yet
+//     handed out (experts ordered by row count in LDS by every workgroup): the long reductions
+//     start early, and the cheap, store-heavy tiles are spread over the whole run instead of
+//     crowding its end, which keeps the output writes overlapped with the matrix work.
+//   - Within an expert's block, tiles go down the m-tiles of one column strip, then the next.
 struct WgradSched {
   struct Args {
     const __bf16* X;       // [M_total x K]
     const __bf16* dY;      // [M_total x N]
     char* dW;              // [G x K x N]
     const int32_t* offsets;
-    uint32_t* queue;       // tile-queue counter (workspace), 0 at launch
+    uint32_t* queue;       // kQueues counters, kQueueStride words apart (workspace), 0 at launch
     int64_t M_total;
     int32_t G, K, N, tiles_m, tiles_n;
+    int32_t pm, pn;        // blocks of m-tiles and of n-tiles, pm * pn = kQueues
     int32_t epi, out_f32, out_bytes;
     Guards guard;
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
   static constexpr bool kDynamic = true;
   static constexpr int kClaimSlots = 16;
+  static constexpr int kQueues = 8;          // one per XCD
+  static constexpr int kQueueStride = 8;     // 32 bytes between counters
+  static constexpr uint32_t kNoTile = 0xFFFFFFFFu;
   // claim slots [16] (8-byte aligned first), offsets[G + 1], experts by decreasing row count [G]
   static constexpr int LDS_BYTES = kClaimSlots * 8 + (2 * kMaxGroups + 1) * 4 + 16;
   __device__ static uint64_t* claim_slots(char* lds) { return reinterpret_cast<uint64_t*>(lds); }
@@ -309,19 +319,50 @@ struct WgradSched {
     // the kernel's barrier after init publishes `order` and the cleared slots
   }
 
-  // The tile at queue position q: positions alternate between the front (heaviest) and the
-  // back (lightest) of the tiles ordered by cost.
+  // Block x of an expert's tile grid: m-tiles [mlo, mlo + mc), n-tiles [nlo, nlo + nc).
+  __device__ static void block_of(const Args& a, int x, int& mlo, int& mc, int& nlo, int& nc) {
+    const int bm = x / a.pn, bn = x % a.pn;
+    mlo = bm * a.tiles_m / a.pm;
+    mc = (bm + 1) * a.tiles_m / a.pm - mlo;
+    nlo = bn * a.tiles_n / a.pn;
+    nc = (bn + 1) * a.tiles_n / a.pn - nlo;
+  }
+
+  // A ticket for the calling workgroup's next tile: queue (4 bits) and position (28 bits), or
+  // kNoTile when every queue is drained.  Called by one lane.  The XCD of a workgroup is
+  // blockIdx.x mod 8 (workgroups are dealt to the XCDs round-robin).
+  __device__ static uint32_t claim(const Args& a) {
+    const int x0 = (int)(blockIdx.x % kQueues);
+    for (int d = 0; d < kQueues; ++d) {
+      const int x = (x0 + d) % kQueues;
+      int mlo, mc, nlo, nc;
+      block_of(a, x, mlo, mc, nlo, nc);
+      const uint32_t T = (uint32_t)a.G * (uint32_t)(mc * nc);
+      if (T == 0) continue;
+      const uint32_t pos = atomicAdd(a.queue + x * kQueueStride, 1u);
+      if (pos < T) return ((uint32_t)x << 28) | pos;
+    }
+    return kNoTile;
+  }
+
+  // The tile of a ticket: positions of a queue alternate between the front (heaviest) and the
+  // back (lightest) of its tiles ordered by cost.
   template <class C>
-  __device__ static bool tile_at(const Args& a, uint32_t q, TileSrc& t, char* lds) {
+  __device__ static bool tile_at(const Args& a, uint32_t ticket, TileSrc& t, char* lds) {
     const int32_t* off = offsets_lds(lds);
     const int32_t* order = off + kMaxGroups + 1;
-    const int per = a.tiles_m * a.tiles_n;
+    if (ticket == kNoTile) return false;
+    const int x = (int)(ticket >> 28);
+    const uint32_t q = ticket & 0x0FFFFFFFu;
+    int mlo, mc, nlo, nc;
+    block_of(a, x, mlo, mc, nlo, nc);
+    const int per = mc * nc;
     const int64_t T = (int64_t)a.G * per;
-    if ((int64_t)q >= T) return false;
+    if (per == 0 || (int64_t)q >= T) return false;
     const int64_t p = (q & 1u) ? T - 1 - (int64_t)(q >> 1) : (int64_t)(q >> 1);
     const int g = order[(int)(p / per)];
     const int local = (int)(p % per);
-    const int mt = local % a.tiles_m, nt = local / a.tiles_m;
+    const int mt = mlo + local % mc, nt = nlo + local / mc;
     const int64_t row0 = off[g];
     const int cnt = max(off[g + 1] - off[g], 0);
     const int64_t m0 = (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
@@ -344,9 +385,9 @@ struct WgradSched {
   }
 };
 
-// Resets a tile-queue counter (one vector store) ahead of the kernel that drains it.
+// Resets the tile-queue counters (vector stores) ahead of the kernel that drains them.
 __global__ void arm_queue_kernel(uint32_t* queue) {
-  if (threadIdx.x == 0) queue[0] = 0;
+  if (threadIdx.x < WgradSched::kQueues) queue[threadIdx.x * WgradSched::kQueueStride] = 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -602,6 +643,23 @@ hipError_t launch_grouped_wgrad(const WgradLaunch& w, hipStream_t stream) {
   a.G = w.G; a.K = (int32_t)w.K; a.N = (int32_t)w.N;
   a.tiles_m = (int32_t)((w.K + C::BM - 1) / C::BM);
   a.tiles_n = (int32_t)((w.N + C::BN - 1) / C::BN);
+  // XCD blocks: the split that reads X and dY into the fewest L2s (pn copies of X, pm of dY),
+  // preferring splits that cut the tile grid evenly
+  {
+    static const int32_t splits[4][2] = {{8, 1}, {4, 2}, {2, 4}, {1, 8}};
+    double best = 0;
+    int bi = -1;
+    for (int pass = 0; pass < 2 && bi < 0; ++pass) {
+      for (int i = 0; i < 4; ++i) {
+        const int32_t pm = splits[i][0], pn = splits[i][1];
+        if (pass == 0 && (a.tiles_m % pm != 0 || a.tiles_n % pn != 0)) continue;
+        const double cost = (double)pn * (double)w.K + (double)pm * (double)w.N;
+        if (bi < 0 || cost < best) { best = cost; bi = i; }
+      }
+    }
+    a.pm = splits[bi][0];
+    a.pn = splits[bi][1];
+  }
   a.epi = 0; a.out_f32 = w.out_f32; a.out_bytes = w.out_f32 ? 4 : 2;
   Guards& gd = a.guard;
   gd = Guards{};
