@@ -83,9 +83,9 @@ struct Cfg {
   // A stored with k as the row index (K x M, M contiguous), as X^T is in a weight gradient
   // X^T . dY: its tile is staged as BK rows of BM and read with transposing LDS reads.
   static constexpr bool A_KM = A_KM_;
-  // Output written as streaming (non-temporal) stores of whole 128-byte row segments: for
-  // outputs that are large and not read back soon (a weight gradient), where the writes
-  // bound the kernel.  16x16 consumer only.
+  // Output written as streaming (non-temporal) stores of whole 128-byte row segments instead
+  // of 64-byte halves; measured faster wherever the output is a sizeable part of the traffic
+  // (weight gradient, broadcast candidates, grouped and dense GEMMs).  16x16 consumer only.
   static constexpr bool STREAM_OUT = STREAM_OUT_;
   static constexpr int WTM = BM / WM, WTN = BN / WN;    // one consumer wave's sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA blocks per wave
