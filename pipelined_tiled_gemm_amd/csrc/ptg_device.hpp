@@ -65,7 +65,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // Tile configuration
 // ---------------------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int NPROD_, bool B_KN_, int PREG_ = 0,
-          bool M16_ = false, bool A_KM_ = false, bool STREAM_OUT_ = false>
+          bool M16_ = false, bool A_KM_ = false, bool STREAM_OUT_ = false, int CG_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   // k-steps a producer holds in registers ahead of the LDS ring (0: tiles go straight from
@@ -77,7 +77,12 @@ struct Cfg {
   // higher clock under the same power.
   static constexpr bool M16 = M16_;
   static constexpr int WM = WM_, WN = WN_;             // consumer waves along M and N
-  static constexpr int NCONS = WM * WN, NPROD = NPROD_;
+  // Consumer groups ("ping-pong"): group c runs the tiles j with j mod CG = c, so that one
+  // group's epilogue (conversion and output stores) overlaps the other group's matrix work.
+  // Every step is released by the NCG waves of the group that runs its tile.
+  static constexpr int CG = CG_;
+  static constexpr int NCG = WM * WN;                   // consumer waves per group
+  static constexpr int NCONS = NCG * CG, NPROD = NPROD_;
   static constexpr int NWAVES = NCONS + NPROD, NT = NWAVES * 64;
   static constexpr bool B_KN = B_KN_;
   // A stored with k as the row index (K x M, M contiguous), as X^T is in a weight gradient
@@ -109,8 +114,10 @@ struct Cfg {
   // slot it fills last, and it fills that slot only after the release of the step STAGES
   // earlier; with NINFO = STAGES + PREG + 3, that released step belongs to tile j + 1 or a
   // later one (every tile has at least one step), so the consumers have finished tile j,
-  // epilogue included.
-  static constexpr int NINFO = STAGES + PREG + 3;
+  // epilogue included.  With two consumer groups, the group in tile j's epilogue holds back
+  // the steps of its next tile, j + 2, so the ring (filled in order) cannot pass j + 2 by more
+  // than STAGES steps: two more slots cover it.
+  static constexpr int NINFO = STAGES + PREG + 3 + 2 * (CG - 1);
   static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "consumer sub-tile must be 32x32 blocks");
   static_assert(!M16 || (TM16 % 2 == 0 && TN16 % 2 == 0 && BK % 32 == 0), "16x16 path: even block counts, BK of 64");
@@ -123,6 +130,7 @@ struct Cfg {
   static_assert(PREG == 0 || PREG == 1, "0: memory to LDS; 1: one step staged in registers");
   static_assert(PREG == 0 || LOADS * 4 <= 128, "a register-staged step must fit the producer's registers");
   static_assert(NT <= 1024, "workgroup too large");
+  static_assert(CG == 1 || CG == 2, "one or two consumer groups");
   static_assert(!A_KM || (M16 && PREG == 1 && (TM16 & (TM16 - 1)) == 0),
                 "A stored K x M: register-staged producers and the 16x16 consumer, TM16 a power of two");
   static_assert(!STREAM_OUT || (M16 && TN16 == 4), "streaming output: 16x16 consumer, 64 columns per wave");
@@ -364,13 +372,18 @@ __host__ __device__ constexpr void chunk_of(int i, int lane, int& row, int& chun
 
 // Load q of a producer (index i0 + q) fetches, for every lane, the chunk of load q mod 2 (its
 // first two loads), (q / 2) ROWS_A or ROWS_B rows further on; for an operand stored with k as
-// the row index the chunk also flips bit 1 when bit 2 of q is set (bit 3 of the k-row, see
-// swz_n).  Two per-lane bases, a row step and a per-lane flip offset then describe all of a
-// producer's loads.  Checked at compile time for each configuration that stages through
-// registers.
+// the row index the chunk also flips bit 1 when that row offset has bit 3 set (bit 3 of the
+// k-row, see swz_n; a producer's first row is a multiple of 16).  Two per-lane bases, a row
+// step and a per-lane flip offset then describe all of a producer's loads.  Checked at
+// compile time for each configuration that stages through registers.
+template <int ROWS>
+constexpr bool row_flip(int q) {
+  return (((q >> 1) * ROWS) >> 3) & 1;
+}
+
 template <class C>
 constexpr bool load_flip(int i, int q) {
-  return ((i < C::A_INSTR) ? C::A_KM : C::B_KN) && ((q >> 2) & 1);
+  return (i < C::A_INSTR) ? (C::A_KM && row_flip<C::ROWS_A>(q)) : (C::B_KN && row_flip<C::ROWS_B>(q));
 }
 
 template <class C>
@@ -454,7 +467,7 @@ __device__ __forceinline__ void producer_role(const typename S::Args& args, char
     }
     for (int st = 0; st < nsteps; ++st, ++g) {
       const int s = g % C::STAGES;
-      const uint32_t released = (uint32_t)C::NCONS * (g / C::STAGES);
+      const uint32_t released = (uint32_t)C::NCG * (g / C::STAGES);
       if ((uint32_t)__builtin_amdgcn_readfirstlane(lds_peek(&empty[s])) < released) {
         // The slot is still in use: before sleeping on it, hand every step in flight to the
         // consumers as soon as it has landed, so that no step waits on a later issue.
@@ -641,9 +654,10 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
 // Byte offset of a producer's load q within the step (see chunk_pattern_ok); q is a
 // compile-time index after unrolling, so the flip is a compile-time choice.
 template <class C>
-__device__ __forceinline__ uint32_t load_off(const FetchTile& f, int q) {
+__device__ __forceinline__ uint32_t load_off(const FetchTile& f, int q, bool opA) {
   const uint32_t base = ((q & 1) ? f.vbase1 : f.vbase0) + (uint32_t)(q >> 1) * f.rstep;
-  return ((q >> 2) & 1) ? base + (uint32_t)((q & 1) ? f.vflip1 : f.vflip0) : base;
+  const bool flip = opA ? row_flip<C::ROWS_A>(q) : row_flip<C::ROWS_B>(q);  // vflip is 0 unless k-major
+  return flip ? base + (uint32_t)((q & 1) ? f.vflip1 : f.vflip0) : base;
 }
 
 template <class C, class S>
@@ -672,19 +686,19 @@ __device__ __forceinline__ void producer_role_regs(const typename S::Args& args,
       if (k0 + C::BK <= f.K) {
 #pragma unroll
         for (int q = 0; q < C::LOADS; ++q)
-          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, load_off<C>(f, q), 0, 0);
+          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, load_off<C>(f, q, opA), 0, 0);
       } else {
 #pragma unroll
         for (int q = 0; q < C::LOADS; ++q) {
           const int kpos = ((q & 1) ? f.kbase1 : f.kbase0) + (q >> 1) * kq;
-          const uint32_t vo = load_off<C>(f, q);
+          const uint32_t vo = load_off<C>(f, q, opA);
           R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, k0 + kpos < f.K ? vo : kOutOfRange, 0, 0);
         }
       }
     }
     // ---- ring: step g goes to slot s once the consumers have released it ---------------
     const int s = g % C::STAGES;
-    wait_at_least(&empty[s], (uint32_t)C::NCONS * (g / C::STAGES), abort);
+    wait_at_least(&empty[s], (uint32_t)C::NCG * (g / C::STAGES), abort);
     if (!f.has) {
       lds_bump(&full[s]);  // the end marker's step carries no data
       break;
@@ -855,7 +869,8 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
                                               const Guards* guards) {
   static_assert(!C::A_KM, "A stored K x M is read by the 16x16 consumer (consumer_role16)");
   const int lane = lane_id();
-  const int wm = cw / C::WN, wn = cw % C::WN;
+  const int cgrp = cw / C::NCG;                // consumer group
+  const int wm = (cw % C::NCG) / C::WN, wn = (cw % C::NCG) % C::WN;
   // A-fragment addressing: lane l holds row (l % 32) of a 32-row block and k-chunk l / 32.
   // Physical chunk = (2 kk + l/32) ^ swz(row) = (2 kk) ^ (l/32 ^ swz(row)) since bit 0 of
   // 2 kk is clear; swz(row) depends only on row % 16, the same for every block of the wave.
@@ -900,6 +915,11 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
     }
     const int K = (int)uni((uint32_t)ti->K);
     const int nsteps = tile_steps<C>(K);
+    if (C::CG > 1 && j % C::CG != cgrp) {
+      // the other group's tile: only its step count matters here
+      g += (uint32_t)nsteps;
+      continue;
+    }
 
     // A wave whose sub-tile lies wholly outside the tile's valid rows or columns has nothing
     // to compute or store: it only takes part in the handoff, releasing each step as it
@@ -1215,7 +1235,8 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
                                                 const Guards* guards) {
   constexpr int HM = C::TM16 / 2;
   const int lane = lane_id();
-  const int wm = cw / C::WN, wn = cw % C::WN;
+  const int cgrp = cw / C::NCG;                // consumer group
+  const int wm = (cw % C::NCG) / C::WN, wn = (cw % C::NCG) % C::WN;
   // A fragment (16x16x32): lane l holds row l % 16 of a 16-row block and 8 k-values from
   // k-chunk l / 16 of the slice.  Physical chunk = (4 ks + l/16) ^ swz(row)
   // = (4 ks) ^ (l/16 ^ swz(row)); swz depends on row % 16 only.
@@ -1289,6 +1310,11 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
     }
     const int K = (int)uni((uint32_t)ti->K);
     const int nsteps = tile_steps<C>(K);
+    if (C::CG > 1 && j % C::CG != cgrp) {
+      // the other group's tile: only its step count matters here
+      g += (uint32_t)nsteps;
+      continue;
+    }
     // idle wave: only takes part in the handoff (see consumer_role).  The extents are read
     // with hand-issued LDS reads, so that no copy of them stays live across the k-loop (the
     // epilogue reads the metadata again).

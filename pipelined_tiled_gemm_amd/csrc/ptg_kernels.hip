@@ -445,12 +445,13 @@ struct BatchSched {
 // ---------------------------------------------------------------------------------------
 // Large problems: 256 x 256 tiles, 8 consumer waves (2 x 4, 128 x 64 each) on 16x16x32
 // MFMAs, 4 producers staging one k-step in registers, two 64 KB ring slots, output written as
-// streaming stores of whole 128-byte row segments.  Medium/small: 128 x 128 tiles, 4
-// consumers (64 x 64 each), 2 producers, four 32 KB slots.  Grouped (mixture-of-experts)
+// streaming stores of whole 128-byte row segments.  Medium/small: 128 x 128 tiles on 32x32x16
+// MFMAs, two consumer groups of 4 waves (64 x 64 each) taking alternate tiles, so that one
+// group's epilogue overlaps the other's matrix work, 2 producers, four 32 KB slots.  Grouped (mixture-of-experts)
 // problems use the large tiles too: a group's last partial tile with at most 128 valid rows
 // runs on half the consumer waves at about half the cost.
 template <bool KN> using CfgLarge = Cfg<256, 256, 64, 2, 2, 4, 4, KN, 1, true, false, true>;
-template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN>;
+template <bool KN> using CfgMedium = Cfg<128, 128, 64, 4, 2, 2, 2, KN, 0, false, false, false, 2>;
 template <bool KN> using CfgGrouped = CfgLarge<KN>;
 // Weight gradient X^T . dY: the large tile with A (X^T) stored K x M and B (dY) K x N, its
 // output (a full K x N per expert, the bulk of the traffic) written as streaming stores.
