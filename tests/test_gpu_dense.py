@@ -56,6 +56,20 @@ def test_medium_tiles_ragged(layout, epi, out_dtype):
     check(out, v, w.K, f"dense 200x136x328 layout={layout} epi={epi}")
 
 
+@pytest.mark.parametrize("shape", [(128, 128, 64), (256, 128, 64), (384, 128, 8), (200, 520, 72),
+                                   (2560, 2560, 136)])
+def test_medium_tiles_both_consumer_groups(shape):
+    """The medium tile runs alternate tiles on two consumer groups: one tile (the second group
+    only sees the end), two, three (odd), a ragged grid, and 400 tiles (some workgroups run two,
+    one per group) on integer data, bit-exact against the oracle."""
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K)
+    A, B = int_bf16(rng, (M, K)), int_bf16(rng, (K, N))
+    assert ptg.describe_config(M, N, K, wl.B_KN)["BM"] == 128
+    out = ptg.gemm(dev_bf16(A), dev_bf16(B), b_layout=wl.B_KN, out_dtype=torch.float32)
+    exact(out, oracle.gemm(A, B, wl.B_KN), f"medium {shape}")
+
+
 @pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
 @pytest.mark.parametrize("epi", [wl.EPI_NONE, wl.EPI_BIAS_SILU])
 def test_large_tiles_ragged(layout, epi):
