@@ -131,6 +131,21 @@ __device__ __forceinline__ void block_exclusive_scan(int n, F val, int32_t* out,
   __syncthreads();
 }
 
+// Largest index p in [0, n) with pre[p] <= x (pre nondecreasing, pre[0] <= x < pre[n], n at most
+// 64 * 64), found by the 64 lanes of a wave in two rounds of LDS reads: the lanes test 64
+// evenly spaced entries, then the entries of the interval that holds x.  Much shorter than a
+// serial bisection (two dependent LDS reads instead of about log2 n).
+__device__ __forceinline__ int wave_upper_index(const int32_t* pre, int n, int32_t x) {
+  const int lane = lane_id();
+  const int step = (n + 63) >> 6;
+  const int i1 = min(lane * step, n);
+  const uint64_t b1 = __ballot(pre[i1] <= x);           // lane 0 always: pre[0] <= x
+  const int base = (63 - __builtin_clzll(b1)) * step;
+  const int i2 = min(base + lane, n);
+  const uint64_t b2 = __ballot(lane < step && pre[i2] <= x);  // lane 0 always
+  return base + (63 - __builtin_clzll(b2));
+}
+
 // Largest index g in [0, n) with pre[g] <= x (pre nondecreasing, pre[0] <= x < pre[n]).
 __device__ __forceinline__ int upper_index(const int32_t* pre, int n, int64_t x) {
   int lo = 0, hi = n;  // invariant: pre[lo] <= x < pre[hi]
@@ -411,14 +426,19 @@ struct BatchSched {
     for (int i = threadIdx.x; i <= a.count; i += C::NT) pre[i] = a.prefix[i];
   }
 
+  // The problem record is read with scalar loads (constant address space, wave-uniform index):
+  // their completion is counted apart from the vector-memory counter, so the producer does not
+  // wait for its own buffer-to-LDS copies in flight before it can use the record, as it would
+  // after an ordinary (vector) load.
   template <class C>
   __device__ static bool tile(const Args& a, int j, TileSrc& t, char* lds) {
+    typedef const __attribute__((address_space(4))) BatchProblem ConstProblem;
     const int32_t* pre = reinterpret_cast<const int32_t*>(lds);
     const int64_t L = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
     if (L >= pre[a.count]) return false;
-    const int p = upper_index(pre, a.count, L);
+    const int p = (int)uni((uint32_t)wave_upper_index(pre, a.count, (int32_t)L));
     const int local = (int)(L - pre[p]);
-    const BatchProblem& q = a.probs[p];
+    ConstProblem& q = reinterpret_cast<ConstProblem*>(reinterpret_cast<uintptr_t>(a.probs))[p];
     const int mt = local % q.tiles_m, nt = local / q.tiles_m;
     const int64_t m0 = (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
     t.A = reinterpret_cast<const __bf16*>(q.A) + m0 * q.lda;
