@@ -53,7 +53,9 @@ def lib():
         L.oracle_grouped_gemm.argtypes = [i32, i64, i64, i64, p, p, i, p, p, i, p, i64, p]
         L.oracle_broadcast_gemm.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, i, p, i, p, i64, p]
         L.oracle_grouped_wgrad.argtypes = [i32, i64, i64, i64, p, p, p, p, i64, p]
-        for f in (L.oracle_gemm, L.oracle_grouped_gemm, L.oracle_broadcast_gemm, L.oracle_grouped_wgrad):
+        L.oracle_ikbo_attention.argtypes = [i64, i64, i64, i64, i64, ctypes.c_double, p, p, p, p, p, i64, p]
+        for f in (L.oracle_gemm, L.oracle_grouped_gemm, L.oracle_broadcast_gemm, L.oracle_grouped_wgrad,
+                  L.oracle_ikbo_attention):
             f.restype = ctypes.c_int
         L.oracle_silu.argtypes = [ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
@@ -179,6 +181,23 @@ def grouped_wgrad(X, dY, offsets, rows=None) -> np.ndarray:
     out = np.empty((n, N), dtype=np.float64)
     _check(lib().oracle_grouped_wgrad(G, M_total, K, N, _ptr(X), _ptr(dY), _ptr(off), _ptr(r), n,
                                       _ptr(out)))
+    return out
+
+
+def ikbo_attention(Q, K, V, offsets, scale: float, rows=None) -> np.ndarray:
+    """Attention of every candidate's query over its user's keys and values: Q [Mc, H, D],
+    K and V [U, L, H, D] (uint16 bfloat16 bits), offsets [U + 1] (candidates contiguous by user).
+    Returns float64 [nrows, H, D] for the selected candidate rows (all by default)."""
+    Q, K, V = _u16(Q), _u16(K), _u16(V)
+    Mc, H, D = Q.shape
+    U, L = K.shape[0], K.shape[1]
+    assert K.shape == (U, L, H, D) and V.shape == K.shape
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+    assert off.shape == (U + 1,)
+    r, n = _rows(rows, Mc)
+    out = np.empty((n, H, D), dtype=np.float64)
+    _check(lib().oracle_ikbo_attention(U, Mc, H, D, L, float(scale), _ptr(off), _ptr(Q), _ptr(K), _ptr(V),
+                                       _ptr(r), n, _ptr(out)))
     return out
 
 

@@ -20,6 +20,8 @@
  *   - The weight gradient of the grouped form, dW_g = X_g^T . dY_g over each expert's rows,
  *     is the same definition with the sum running over the expert's rows (same case study;
  *     the gradient products of its pretraining use).
+ *   - IKBO attention: each candidate's query attends to its user's keys and values, the
+ *     attention form of the same broadcast (case study 2), as the textbook softmax attention.
  *   - Epilogue: optional per-column bias, then optional SiLU(v) = v / (1 + exp(-v)).
  *
  * Arithmetic: inputs are the same bfloat16 bit patterns the GPU receives, decoded exactly;
@@ -306,4 +308,70 @@ int oracle_grouped_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t N, const
         }
     }
     return OR_OK;
+}
+
+/* ---- IKBO attention --------------------------------------------------------------------- *
+ * The attention form of the in-kernel broadcast (How We Built TLX: "Case Study 2: In-Kernel
+ * Broadcast Optimization for RecSys" states that for FlashAttention the co-design amortises
+ * the K/V reads across the candidates sharing one user context).  Candidates are contiguous
+ * by user: user u owns candidates [off[u], off[u+1]).  For candidate c of user u and head h:
+ *     s_j = scale * sum_e Q[c][h][e] * K[u][j][h][e]          (j = 0 .. L-1)
+ *     p_j = exp(s_j - max_j s_j) / sum_j exp(s_j - max_j s_j)
+ *     O[c][h][e] = sum_j p_j * V[u][j][h][e]
+ * Q and O are [Mc][H][D], K and V are [U][L][H][D] (all dense).  Every sum runs in double in
+ * ascending index order.  Output rows are selected by candidate index (all of them when rows is
+ * NULL and nrows == Mc); out is nrows x H x D. */
+int oracle_ikbo_attention(int64_t U, int64_t Mc, int64_t H, int64_t D, int64_t L, double scale,
+                          const int32_t* off, const uint16_t* Q, const uint16_t* K,
+                          const uint16_t* V, const int64_t* rows, int64_t nrows, double* out) {
+    if (U <= 0 || Mc < 0 || H <= 0 || D <= 0 || L <= 0 || !off) return OR_BAD_ARG;
+    if (off[0] != 0 || (int64_t)off[U] != Mc) return OR_BAD_OFFSETS;
+    for (int64_t u = 0; u < U; ++u)
+        if (off[u + 1] < off[u]) return OR_BAD_OFFSETS;
+    if (!rows && nrows != Mc) return OR_BAD_ARG;
+    for (int64_t t = 0; rows && t < nrows; ++t)
+        if (rows[t] < 0 || rows[t] >= Mc) return OR_BAD_ARG;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)L);
+        double* q = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < nrows; ++t) {
+            if (!s || !q) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            const int64_t c = rows ? rows[t] : t;
+            int64_t u = 0; /* the user whose (nonempty) range holds candidate c */
+            while (!((int64_t)off[u] <= c && c < (int64_t)off[u + 1])) ++u;
+            for (int64_t h = 0; h < H; ++h) {
+                for (int64_t e = 0; e < D; ++e) q[e] = bf16_value(Q[(c * H + h) * D + e]);
+                double mx = -INFINITY;
+                for (int64_t j = 0; j < L; ++j) {
+                    const uint16_t* kr = K + ((u * L + j) * H + h) * D;
+                    double acc = 0.0;
+                    for (int64_t e = 0; e < D; ++e) acc += q[e] * bf16_value(kr[e]);
+                    s[j] = scale * acc;
+                    if (s[j] > mx) mx = s[j];
+                }
+                double den = 0.0;
+                for (int64_t j = 0; j < L; ++j) {
+                    s[j] = exp(s[j] - mx);
+                    den += s[j];
+                }
+                double* o = out + (t * H + h) * D;
+                for (int64_t e = 0; e < D; ++e) o[e] = 0.0;
+                for (int64_t j = 0; j < L; ++j) {
+                    const uint16_t* vr = V + ((u * L + j) * H + h) * D;
+                    const double p = s[j] / den;
+                    for (int64_t e = 0; e < D; ++e) o[e] += p * bf16_value(vr[e]);
+                }
+            }
+        }
+        free(s);
+        free(q);
+    }
+    return failed ? OR_NO_MEMORY : OR_OK;
 }

@@ -426,6 +426,91 @@ def test_dgrad_is_grouped_gemm_with_transposed_weights():
 
 
 # ---------------------------------------------------------------------------------------
+# IKBO attention: O[c] = softmax(scale * Q[c] . K[u]^T) . V[u] per head, u the user of c
+# ---------------------------------------------------------------------------------------
+def _attn_case(seed, counts, H, D, L):
+    rng = np.random.default_rng(seed)
+    U, Mc = len(counts), int(np.sum(counts))
+    Q = rand_bf16(rng, (Mc, H, D))
+    K = rand_bf16(rng, (U, L, H, D))
+    V = rand_bf16(rng, (U, L, H, D))
+    return Q, K, V, _offsets(np.asarray(counts))
+
+
+def test_attention_brute_force_tiny():
+    """Pure-Python loops with math.exp (ascending order, double): equal to 1e-15 relative."""
+    counts = [2, 0, 3]
+    H, D, L = 2, 3, 4
+    Q, K, V, off = _attn_case(50, counts, H, D, L)
+    scale = 0.7
+    got = oracle.ikbo_attention(Q, K, V, off, scale)
+    q, k, v = dec(Q).tolist(), dec(K).tolist(), dec(V).tolist()
+    user = np.repeat(np.arange(len(counts)), counts)
+    for c in range(int(sum(counts))):
+        u = int(user[c])
+        for h in range(H):
+            s = [scale * sum(q[c][h][e] * k[u][j][h][e] for e in range(D)) for j in range(L)]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            z = sum(w)
+            for e in range(D):
+                want = sum(w[j] / z * v[u][j][h][e] for j in range(L))
+                assert abs(got[c, h, e] - want) <= 1e-15 * max(1.0, abs(want))
+
+
+def test_attention_vs_scipy_softmax():
+    """numpy products and scipy's softmax (library routines), users of 1 to 70 candidates."""
+    counts = [70, 1, 0, 33]
+    H, D, L = 3, 16, 40
+    Q, K, V, off = _attn_case(51, counts, H, D, L)
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.ikbo_attention(Q, K, V, off, scale)
+    q, k, v = dec(Q), dec(K), dec(V)
+    for u in range(len(counts)):
+        lo, hi = off[u], off[u + 1]
+        for h in range(H):
+            p = scipy.special.softmax(scale * q[lo:hi, h] @ k[u, :, h].T, axis=1)
+            assert np.allclose(got[lo:hi, h], p @ v[u, :, h], rtol=1e-12, atol=1e-14)
+
+
+def test_attention_closed_forms():
+    """Constant value rows come back exactly; zero keys give the plain mean of the values; one
+    key with an overwhelming score returns its value row; a candidate never sees another
+    user's keys."""
+    counts = [3, 4]
+    H, D, L = 2, 8, 16
+    Q, K, V, off = _attn_case(52, counts, H, D, L)
+    # constant value rows: any weights summing to one give that constant
+    Vc = wl.f32_to_bf16_bits(np.full(V.shape, 0.375, np.float32))
+    assert np.allclose(oracle.ikbo_attention(Q, K, Vc, off, 0.5), 0.375, rtol=0, atol=1e-15)
+    # zero keys: uniform weights, the mean over the user's L value rows
+    Kz = np.zeros_like(K)
+    got = oracle.ikbo_attention(Q, Kz, V, off, 0.5)
+    v = dec(V)
+    user = np.repeat(np.arange(2), counts)
+    for c in range(7):
+        assert np.allclose(got[c], v[user[c]].mean(axis=0), rtol=1e-13, atol=1e-15)
+    # one dominant key: Q = e_0, K[u, j] = 64 e_0 for j = 5 only, scale 1 -> weight 1 - O(e^-64)
+    Qe = np.zeros(Q.shape, np.float32); Qe[:, :, 0] = 1.0
+    Ke = np.zeros(K.shape, np.float32); Ke[:, 5, :, 0] = 64.0
+    got = oracle.ikbo_attention(wl.f32_to_bf16_bits(Qe), wl.f32_to_bf16_bits(Ke), V, off, 1.0)
+    for c in range(7):
+        assert np.allclose(got[c], v[user[c], 5], rtol=1e-12, atol=1e-12)
+
+
+def test_attention_selected_rows_and_bad_offsets():
+    counts = [5, 2]
+    Q, K, V, off = _attn_case(53, counts, 1, 4, 8)
+    full = oracle.ikbo_attention(Q, K, V, off, 0.3)
+    sel = np.array([6, 0, 3])
+    assert np.array_equal(oracle.ikbo_attention(Q, K, V, off, 0.3, rows=sel), full[sel])
+    for bad in ([1, 5, 7], [0, 6, 5], [0, 5, 6]):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.ikbo_attention(Q, K, V, bad, 0.3)
+        assert e.value.code == 2
+
+
+# ---------------------------------------------------------------------------------------
 # broadcast gemm
 # ---------------------------------------------------------------------------------------
 def test_broadcast_block_identities():

@@ -141,6 +141,23 @@ class Wgrad:
 
 
 @dataclasses.dataclass
+class Attention:
+    """O[c] = softmax(scale Q[c] . K[u]^T) . V[u] per head, u the user of candidate c."""
+    U: int
+    Mc: int
+    H: int
+    D: int
+    L: int
+    Q: np.ndarray            # uint16 [Mc, H, D]
+    K: np.ndarray            # uint16 [U, L, H, D]
+    V: np.ndarray            # uint16 [U, L, H, D]
+    counts: np.ndarray       # int64 [U] candidates per user
+    offsets: np.ndarray      # int32 [U + 1]
+    scale: float
+    out_dtype: str = "bf16"
+
+
+@dataclasses.dataclass
 class Broadcast:
     """Y[r] = epi([Xu[idx[r]] | Xc[r]].W + bias), W is (Ku + Kc) x N (KN) or N x (Ku + Kc) (NK)."""
     U: int
@@ -311,6 +328,42 @@ def broadcast(seed: int, U: int, Ku: int, Kc: int, N: int, *, cmin: int = 256, c
 def config4() -> Broadcast:
     """IKBO linear compression: 64 users, Xu 64x2048, Xc (sum C_u)x512, W 2560x1024 (seed 4)."""
     return broadcast(4, 64, 2048, 512, 1024)
+
+
+def attention(seed: int, U: int, H: int, D: int, L: int, *, cmin: int = 256, cmax: int = 2048,
+              counts: Optional[np.ndarray] = None, out_dtype: str = "bf16") -> Attention:
+    """Draw C_u ~ U{cmin..cmax} per user (unless ``counts`` is given), then Q, K, V ~ N(0,1);
+    candidates contiguous by user; scale 1/sqrt(D)."""
+    rng = np.random.default_rng(seed)
+    if counts is None:
+        counts = rng.integers(cmin, cmax + 1, U).astype(np.int64)
+    else:
+        counts = np.asarray(counts, dtype=np.int64)
+        assert len(counts) == U
+    Mc = int(counts.sum())
+    offsets = np.zeros(U + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    Q = _draw_rows(rng, Mc * H, D, "normal").reshape(Mc, H, D)
+    K = _draw_rows(rng, U * L * H, D, "normal").reshape(U, L, H, D)
+    V = _draw_rows(rng, U * L * H, D, "normal").reshape(U, L, H, D)
+    return Attention(U, Mc, H, D, L, Q, K, V, counts, offsets, 1.0 / float(np.sqrt(D)), out_dtype)
+
+
+def ikbo_attention_workload() -> Attention:
+    """IKBO attention: 64 users with C_u ~ U{256..2048} candidates (seed 7), user context of
+    L = 1024 keys, 4 heads of dimension 128."""
+    return attention(7, 64, 4, 128, 1024)
+
+
+def attention_flops(w: Attention) -> float:
+    """Two products (Q.K^T and P.V) of 2 Mc L D flops per head."""
+    return 4.0 * w.Mc * w.L * w.D * w.H
+
+
+def attention_bytes(w: Attention) -> float:
+    """Q and O once per candidate, K and V once per user."""
+    ob = out_bytes(w.out_dtype)
+    return (2.0 + ob) * w.Mc * w.H * w.D + 2.0 * 2.0 * w.U * w.L * w.H * w.D
 
 
 def problem_list(seed: int, P: int, *, mmin: int = 64, mmax: int = 1024,
