@@ -128,6 +128,29 @@ ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t
                                   void* stream);
 
 /*
+ * ptg_ikbo_attention - the attention form of the in-kernel broadcast ("Case Study 2: In-Kernel
+ * Broadcast Optimization for RecSys": for FlashAttention, the K/V reads are amortised across
+ * the candidates that share one user context).  Candidates are sorted by user; user u owns
+ * candidates [user_offsets[u], user_offsets[u+1]).  For candidate c of user u and head h:
+ *   O[c][h] = softmax_j(scale * Q[c][h] . K[u][j][h]) . V[u][j][h]   (j = 0 .. L-1, no mask)
+ *   U             users, 1 <= U <= 1024
+ *   Mc            candidates (rows of Q and O), >= 0
+ *   H, D          heads and head dimension; D must be 128
+ *   L             keys per user context, a positive multiple of 64
+ *   scale         finite score scale (1/sqrt(D) for the usual attention)
+ *   Q             bf16 [Mc x H x D] dense
+ *   K, V          bf16 [U x L x H x D] dense
+ *   user_offsets  DEVICE int32 [U + 1]: 0 first, nondecreasing, Mc last (empty users allowed);
+ *                 ptg_grouped_gemm_check(U, Mc, user_offsets, stream) validates it
+ *   O             [Mc x H x D] of o_dtype, fully overwritten
+ * Softmax in fp32 (running maximum and sum over 64-key blocks), products in bf16 MFMAs with
+ * fp32 accumulation.  Errors as ptg_gemm; PTG_ERR_UNSUPPORTED for D != 128 or L % 64 != 0.
+ */
+ptg_status ptg_ikbo_attention(int64_t U, int64_t Mc, int64_t H, int64_t D, int64_t L, float scale,
+                              const void* Q, const void* K, const void* V,
+                              const int32_t* user_offsets, void* O, ptg_dtype o_dtype, void* stream);
+
+/*
  * Batch of independent GEMMs in one persistent launch (the pointer-array form of the grouped
  * GEMM): problem p computes C_p = epi(A_p . B_p + bias_p) with B_p stored K x N (KN).
  * Short problems keep the pipeline full across problem boundaries ("Case Study 2", final

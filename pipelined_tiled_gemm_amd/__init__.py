@@ -20,7 +20,7 @@ from . import _ffi
 
 __all__ = [
     "PtgError", "B_KN", "B_NK", "EPI_NONE", "EPI_BIAS", "EPI_SILU", "EPI_BIAS_SILU",
-    "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace",
+    "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace", "ikbo_attention",
     "gemm_batch_workspace",
     "gemm_batch_prepare",
     "gemm_batch_run", "gemm_batch", "broadcast_gemm_workspace", "broadcast_gemm",
@@ -193,6 +193,34 @@ def grouped_gemm_wgrad(X: torch.Tensor, dY: torch.Tensor, group_offsets: torch.T
     _check(_lib().ptg_grouped_gemm_wgrad(G, M, K, N, _ptr(X), _ptr(dY), _ptr(group_offsets), _ptr(out),
                                          _dtype_code(out.dtype), _ptr(workspace), workspace.numel(),
                                          _stream(stream)))
+    return out
+
+
+def ikbo_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, user_offsets: torch.Tensor, *,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """O[c] = softmax(scale Q[c] . K[u]^T) . V[u] per head, u the user of candidate c
+    (offsets[u] <= c < offsets[u+1], on device).  Q [Mc, H, D]; K, V [U, L, H, D]; D = 128."""
+    _need(Q, "Q", torch.bfloat16, 3)
+    _need(K, "K", torch.bfloat16, 4)
+    _need(V, "V", torch.bfloat16, 4)
+    _need(user_offsets, "user_offsets", torch.int32, 1)
+    Mc, H, D = Q.shape
+    U, L = K.shape[0], K.shape[1]
+    if tuple(K.shape) != (U, L, H, D) or tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K and V must be [U, L, H, D] matching Q's H and D")
+    if user_offsets.shape[0] != U + 1:
+        raise ValueError("user_offsets must have U + 1 entries")
+    if not (Q.is_contiguous() and K.is_contiguous() and V.is_contiguous() and user_offsets.is_contiguous()):
+        raise ValueError("Q, K, V and user_offsets must be contiguous")
+    if scale is None:
+        scale = float(D) ** -0.5
+    if out is None:
+        out = torch.empty((Mc, H, D), dtype=out_dtype, device=Q.device)
+    if not out.is_contiguous() or tuple(out.shape) != (Mc, H, D):
+        raise ValueError(f"out must be a contiguous [{Mc}, {H}, {D}] tensor")
+    _check(_lib().ptg_ikbo_attention(U, Mc, H, D, L, float(scale), _ptr(Q), _ptr(K), _ptr(V), _ptr(user_offsets),
+                                     _ptr(out), _dtype_code(out.dtype), _stream(stream)))
     return out
 
 

@@ -23,7 +23,7 @@ STATUS_NAMES = {
 # Every symbol include/ptg.h declares (checked by the CPU tests).
 EXPORTS = (
     "ptg_gemm", "ptg_grouped_gemm", "ptg_grouped_gemm_check", "ptg_grouped_gemm_wgrad",
-    "ptg_grouped_gemm_wgrad_workspace",
+    "ptg_grouped_gemm_wgrad_workspace", "ptg_ikbo_attention",
     "ptg_gemm_batch_workspace", "ptg_gemm_batch_prepare", "ptg_gemm_batch_run", "ptg_gemm_batch",
     "ptg_broadcast_gemm_workspace", "ptg_broadcast_gemm", "ptg_broadcast_gemm_check",
     "ptg_status_string", "ptg_last_error", "ptg_watchdog", "ptg_version", "ptg_describe_config",
@@ -59,6 +59,7 @@ def load(path: str = LIB_PATH):
     L.ptg_grouped_gemm.argtypes = [i32, i64, i64, i64, p, p, e, p, p, e, p, e, p]
     L.ptg_grouped_gemm_check.argtypes = [i32, i64, p, p]
     L.ptg_grouped_gemm_wgrad.argtypes = [i32, i64, i64, i64, p, p, p, p, e, p, sz, p]
+    L.ptg_ikbo_attention.argtypes = [i64, i64, i64, i64, i64, ctypes.c_float, p, p, p, p, p, e, p]
     L.ptg_grouped_gemm_wgrad_workspace.argtypes = []
     L.ptg_grouped_gemm_wgrad_workspace.restype = sz
     L.ptg_gemm_batch_workspace.argtypes = [i32]
@@ -70,7 +71,7 @@ def load(path: str = LIB_PATH):
     L.ptg_broadcast_gemm_workspace.restype = sz
     L.ptg_broadcast_gemm.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, e, p, e, p, e, p, sz, p]
     L.ptg_broadcast_gemm_check.argtypes = [i64, i64, p, p]
-    for f in (L.ptg_gemm, L.ptg_grouped_gemm, L.ptg_grouped_gemm_check, L.ptg_grouped_gemm_wgrad,
+    for f in (L.ptg_gemm, L.ptg_grouped_gemm, L.ptg_grouped_gemm_check, L.ptg_grouped_gemm_wgrad, L.ptg_ikbo_attention,
               L.ptg_gemm_batch_prepare,
               L.ptg_gemm_batch_run, L.ptg_gemm_batch, L.ptg_broadcast_gemm,
               L.ptg_broadcast_gemm_check):

@@ -10,6 +10,8 @@
 #include <vector>
 
 #include "ptg.h"
+
+#include <cmath>
 #include "ptg_launch.h"
 
 namespace {
@@ -190,6 +192,37 @@ ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t
     w.M_total = M_total; w.K = K; w.N = N; w.G = G;
     w.out_f32 = dw_dtype == PTG_F32;
     hipError_t e = ptg::launch_grouped_wgrad(w, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return PTG_OK;
+  })
+}
+
+ptg_status ptg_ikbo_attention(int64_t U, int64_t Mc, int64_t H, int64_t D, int64_t L, float scale,
+                              const void* Q, const void* K, const void* V, const int32_t* user_offsets,
+                              void* O, ptg_dtype o_dtype, void* stream) {
+  PTG_TRY({
+    const char* fn = "ptg_ikbo_attention";
+    if (U <= 0 || Mc < 0 || H <= 0 || D <= 0 || L <= 0)
+      return fail(PTG_ERR_INVALID_ARG, "%s: U, H, D, L must be positive and Mc >= 0", fn);
+    if (U > ptg::kMaxGroups) return fail(PTG_ERR_UNSUPPORTED, "%s: U exceeds %d", fn, ptg::kMaxGroups);
+    if (D != ptg::kAttnHeadDim) return fail(PTG_ERR_UNSUPPORTED, "%s: head dimension must be %d", fn, ptg::kAttnHeadDim);
+    if (L % 64) return fail(PTG_ERR_UNSUPPORTED, "%s: L must be a multiple of 64 (L=%lld)", fn, (long long)L);
+    if (o_dtype != PTG_BF16 && o_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+      return fail(PTG_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    if (Mc == 0) return PTG_OK;
+    if (!Q || !K || !V || !O || !user_offsets) return fail(PTG_ERR_INVALID_ARG, "%s: null operand", fn);
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+        (reinterpret_cast<uintptr_t>(user_offsets) & 3u))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (offsets 4-byte)", fn);
+    // 32-bit buffer offsets: all of Q or O, and one user's and head's rows of K or V
+    const int64_t row_elems = H * D;
+    if (Mc >= ((int64_t)1 << 31) || Mc * row_elems * 4 >= ((int64_t)1 << 31) || L * row_elems * 2 >= ((int64_t)1 << 31))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand exceeds 2 GiB of addressing", fn);
+    ptg::AttentionLaunch a{};
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.offsets = user_offsets;
+    a.U = U; a.Mc = Mc; a.H = H; a.L = L; a.scale = scale; a.out_f32 = o_dtype == PTG_F32;
+    hipError_t e = ptg::launch_attention(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
   })

@@ -770,3 +770,5 @@ hipError_t read_watchdog(uint32_t* value, int clear) {
 }
 
 }  // namespace ptg
+
+#include "ptg_attention.hpp"

@@ -116,6 +116,19 @@ int32_t broadcast_user_splits(int64_t U, int64_t N);
 hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream);
 hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream);
 hipError_t launch_grouped_wgrad(const WgradLaunch& w, hipStream_t stream);
+// IKBO attention: O[c] = softmax(scale Q[c] . K[u]^T) . V[u] per head, u the user of c.
+constexpr int kAttnHeadDim = 128;
+struct AttentionLaunch {
+  const void* Q;              // [Mc x H x D] bf16
+  const void* K;              // [U x L x H x D] bf16
+  const void* V;              // [U x L x H x D] bf16
+  void* O;                    // [Mc x H x D]
+  const int32_t* offsets;     // device [U + 1]
+  int64_t U, Mc, H, L;
+  double scale;
+  int out_f32;
+};
+hipError_t launch_attention(const AttentionLaunch& p, hipStream_t stream);
 // Validation of device-resident preconditions: runs a check kernel on `stream`, waits for
 // it, and sets *bad to 1 if the data violates the precondition (0 otherwise).
 hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hipStream_t stream,
