@@ -16,8 +16,8 @@ roofline         the GEMM kernel against MI355X's dense bf16 MFMA peak (2500 TFL
                  a summary for the current kernel sources exists under profiles/, else null
 cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload (some output
                  rows), on all host cores it uses, in the same unit
-secondary        grouped (mixture-of-experts) forward and weight gradient, broadcast and
-                 batched workloads, timed the same way (TFLOP/s, % of peak, GB/s of
+secondary        grouped (mixture-of-experts) forward and weight gradient, broadcast, IKBO
+                 attention and batched workloads, timed the same way (TFLOP/s, % of peak, GB/s of
                  compulsory traffic), plus per-call
                  cold-cache times (median, min, p90) with a 512 MB scratch write between calls
 """
@@ -156,6 +156,21 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
         "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
         "cold_ms": time_cold(call, cold_reps, torch)}
     del Xu, Xc, idx, W, Y, ws, w
+    # IKBO attention: 64 users (C_u ~ U{256..2048}), context of 1024 keys, 4 heads of 128
+    w = wl.ikbo_attention_workload()
+    Q, K, V = (to_dev(w.Q.reshape(w.Mc, -1), torch, np).view(w.Mc, w.H, w.D),
+               to_dev(w.K.reshape(w.U, -1), torch, np).view(w.U, w.L, w.H, w.D),
+               to_dev(w.V.reshape(w.U, -1), torch, np).view(w.U, w.L, w.H, w.D))
+    off = torch.from_numpy(w.offsets).cuda()
+    O = torch.empty((w.Mc, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    call = lambda: ptg.ikbo_attention(Q, K, V, off, scale=w.scale, out=O)  # noqa: E731
+    _, ms = time_calls(call, steps, warmup, torch)
+    f, b = wl.attention_flops(w), wl.attention_bytes(w)
+    out["ikbo_attention_64users_77801cand_L1024_H4_D128"] = {
+        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
+        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
+        "cold_ms": time_cold(call, cold_reps, torch)}
+    del Q, K, V, off, O, w
     # batch: 1024 independent GEMMs with fused bias + SiLU, one persistent launch
     pl = wl.config5()
     probs = []

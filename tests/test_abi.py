@@ -161,6 +161,25 @@ def test_wgrad_validation(L):
     assert w(N=0, X=None, dY=None, dW=None, off=None, ws=None) == OK
 
 
+def test_attention_validation(L):
+    def a(U=2, Mc=10, H=2, D=128, Lk=64, scale=0.088, Q=P, K=P, V=P, off=P, O=P, dtype=0):
+        return L.ptg_ikbo_attention(U, Mc, H, D, Lk, scale, Q, K, V, off, O, dtype, None)
+    assert a(U=0) == INVALID
+    assert a(U=1025) == UNSUPPORTED
+    assert a(H=0) == INVALID
+    assert a(D=64) == UNSUPPORTED
+    assert a(Lk=96) == UNSUPPORTED
+    assert a(Lk=0) == INVALID
+    assert a(dtype=5) == UNSUPPORTED
+    assert a(scale=float("inf")) == INVALID
+    assert a(scale=float("nan")) == INVALID
+    assert a(Q=None) == INVALID
+    assert a(off=None) == INVALID
+    assert a(off=P + 2) == UNSUPPORTED
+    assert a(O=P + 8) == UNSUPPORTED
+    assert a(Mc=0, Q=None, K=None, V=None, off=None, O=None) == OK
+
+
 def test_describe_config(L):
     cfg = (ctypes.c_int32 * 6)()
     assert L.ptg_describe_config(8192, 8192, 8192, 1, cfg) == OK
