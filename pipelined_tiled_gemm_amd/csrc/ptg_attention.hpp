@@ -197,14 +197,8 @@ __device__ __forceinline__ void consumer(const Args& a, const int32_t* off, cons
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     float m = -__builtin_inff(), l = 0.0f;
 
-    for (int st = 0; st < nsteps; ++st, ++g) {
-      const int s = g % STAGES;
-      wait_at_least(&full[s], (uint32_t)NPROD * (g / STAGES + 1), abort);
-      if (uni(lds_peek(abort)) != 0) return;
-      const char* kb_lds = ring + s * STEP_BYTES;
-      const char* vb_lds = kb_lds + BLK_BYTES;
-      // ---- S^T = K . Q^T for the step's 64 keys (two 32-key blocks) ----------------------
-      f32x16 sc[2];
+    // S^T = K . Q^T for the 64 keys of a staged step (two 32-key blocks).
+    auto qk = [&](const char* kb_lds, f32x16 (&sc)[2]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sc[kb] = f32x16{};
@@ -215,7 +209,10 @@ __device__ __forceinline__ void consumer(const Args& a, const int32_t* off, cons
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc[kb], 0, 0, 0);
         }
       }
-      // ---- online softmax (log2 domain) ------------------------------------------------
+    };
+    // Online softmax of one step's scores (log2 domain): updates the running maximum and sum,
+    // rescales O, and leaves the weights in place of the scores.
+    auto softmax = [&](f32x16 (&sc)[2]) {
       float mx = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -242,37 +239,64 @@ __device__ __forceinline__ void consumer(const Args& a, const int32_t* off, cons
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      // ---- O^T += V^T . P^T over four 16-key slices ------------------------------------
+    };
+    // O^T += V^T . P^T over the step's four 16-key slices.  The P^T fragment of slice (kb, sl):
+    // keys 8 hi .. + 7 for query lane % 32; register group r / 4 = gq holds keys 8 gq + 4 hi +
+    // (0..3), and lanes l and l + 32 trade so that each holds 8 consecutive keys.
+    auto pv = [&](const char* vb_lds, const f32x16 (&sc)[2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int sl4 = 0; sl4 < 4; ++sl4) {
+        const int kb = sl4 >> 1, g0 = 2 * (sl4 & 1), g1 = g0 + 1;
+        const uint32_t a0 = pack_bf16(sc[kb][4 * g0], sc[kb][4 * g0 + 1]);
+        const uint32_t a1 = pack_bf16(sc[kb][4 * g0 + 2], sc[kb][4 * g0 + 3]);
+        const uint32_t b0 = pack_bf16(sc[kb][4 * g1], sc[kb][4 * g1 + 1]);
+        const uint32_t b1 = pack_bf16(sc[kb][4 * g1 + 2], sc[kb][4 * g1 + 3]);
+        const auto w0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto w1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        const u32x4 pw = {w0[0], w1[0], w0[1], w1[1]};
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          // P^T fragment: keys 8 hi .. + 7 of slice (kb, sl) for query lane % 32.  Register
-          // group r / 4 = gq holds keys 8 gq + 4 hi + (0..3); lanes l and l + 32 trade so
-          // that each holds 8 consecutive keys.
-          const int g0 = 2 * sl, g1 = 2 * sl + 1;
-          const uint32_t a0 = pack_bf16(sc[kb][4 * g0], sc[kb][4 * g0 + 1]);
-          const uint32_t a1 = pack_bf16(sc[kb][4 * g0 + 2], sc[kb][4 * g0 + 3]);
-          const uint32_t b0 = pack_bf16(sc[kb][4 * g1], sc[kb][4 * g1 + 1]);
-          const uint32_t b1 = pack_bf16(sc[kb][4 * g1 + 2], sc[kb][4 * g1 + 3]);
-          const auto w0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-          const auto w1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-          const u32x4 pv = {w0[0], w1[0], w0[1], w1[1]};
-          const bf16x8 pf = __builtin_bit_cast(bf16x8, pv);
-          const int key0 = kb * 32 + sl * 16;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int off_v = (opaque(v_off) ^ (db << 6)) + key0 * ROW_BYTES;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_lds + off_v));
-            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_lds + off_v + 4 * ROW_BYTES));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
-          }
+        for (int db = 0; db < 4; ++db) {
+          const int off_v = (opaque(v_off) ^ (db << 6)) + sl4 * 16 * ROW_BYTES;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_lds + off_v));
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_lds + off_v + 4 * ROW_BYTES));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
         }
       }
-      // every read of the slot has landed in registers: release it
+    };
+
+    // Software pipeline over the steps: the next step's S^T MFMAs are issued together with the
+    // current step's softmax (independent work for the matrix core and the vector ALU of the
+    // same wave), then the current step's O^T MFMAs.  The last step runs without a successor.
+    f32x16 sc[2];
+    {
+      const int s = g % STAGES;
+      wait_at_least(&full[s], (uint32_t)NPROD * (g / STAGES + 1), abort);
+      if (uni(lds_peek(abort)) != 0) return;
+      qk(ring + s * STEP_BYTES, sc);
+    }
+    for (int st = 0; st + 1 < nsteps; ++st, ++g) {
+      const int s = g % STAGES, sn = (g + 1) % STAGES;
+      wait_at_least(&full[sn], (uint32_t)NPROD * ((g + 1) / STAGES + 1), abort);
+      if (uni(lds_peek(abort)) != 0) return;
+      f32x16 scn[2];
+      qk(ring + sn * STEP_BYTES, scn);
+      softmax(sc);
+      pv(ring + s * STEP_BYTES + BLK_BYTES, sc);
+      // every read of slot s has landed in registers: release it
       wait_lgkm0();
       lds_bump(&empty[s]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[kb] = scn[kb];
+    }
+    {
+      const int s = g % STAGES;
+      softmax(sc);
+      pv(ring + s * STEP_BYTES + BLK_BYTES, sc);
+      wait_lgkm0();
+      lds_bump(&empty[s]);
+      ++g;
     }
     // ---- epilogue: O = O^T / l; register r of o[db] is d = 32 db + 8 (r / 4) + 4 hi + r % 4 -
     const float inv = 1.0f / l;
