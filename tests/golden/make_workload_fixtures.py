@@ -30,6 +30,10 @@ def main():
         n = int(rng.choice((128, 256, 512)))
         k = int(rng.choice((128, 256, 512)))
         shapes.append([m, n, k])
+    rng = np.random.default_rng(7)
+    cu_attn = rng.integers(256, 2049, 64)
+    wg = wl.wgrad(30, 5, 300, 16, 24, counts=np.array([100, 0, 7, 150, 43]))
+    att = wl.attention(70, 3, 2, 128, 64, counts=np.array([5, 0, 9]))
     small = wl.dense(100, 33, 40, 24, dist="normal", b_layout=wl.B_NK, scale=0.5)
     fx = {
         "_about": "Seeded synthetic workloads standing in for the production cases of the pages "
@@ -41,6 +45,9 @@ def main():
         "config3_counts_sampled_zipf": [int(x) for x in counts_sampled],
         "config4_candidates_per_user": [int(x) for x in cu],
         "config5_shapes": shapes,
+        "attention_candidates_per_user": [int(x) for x in cu_attn],
+        "wgrad_small_digest": wl.digest(wg.X, wg.dY),
+        "attention_small_digest": wl.digest(att.Q, att.K, att.V),
     }
     with open(os.path.join(HERE, "workload_fixtures.json"), "w") as f:
         json.dump(fx, f, indent=1)

@@ -77,6 +77,27 @@ def test_broadcast_counts(fx):
     assert sorted(sh.idx.tolist()) == b.idx.tolist()
 
 
+def test_wgrad_workload(fx):
+    """The weight-gradient workload draws the forward MoE routing and X, then dY."""
+    w = wl.wgrad(3, 64, 16384, 8, 8)
+    g = wl.grouped(3, 64, 16384, 8, 8)
+    assert w.counts.tolist() == fx["config3_counts_rank_zipf"]
+    assert np.array_equal(w.X, g.X) and np.array_equal(w.offsets, g.offsets)
+    assert w.dY.shape == (16384, 8)
+    small = wl.wgrad(30, 5, 300, 16, 24, counts=np.array([100, 0, 7, 150, 43]))
+    assert wl.digest(small.X, small.dY) == fx["wgrad_small_digest"]
+
+
+def test_attention_workload(fx):
+    a = wl.attention(7, 64, 1, 128, 64)
+    assert a.counts.tolist() == fx["attention_candidates_per_user"]
+    assert a.Mc == 77801 and a.offsets[-1] == 77801
+    assert a.Q.shape == (77801, 1, 128) and a.K.shape == (64, 64, 1, 128)
+    assert a.scale == pytest.approx(128 ** -0.5)
+    small = wl.attention(70, 3, 2, 128, 64, counts=np.array([5, 0, 9]))
+    assert wl.digest(small.Q, small.K, small.V) == fx["attention_small_digest"]
+
+
 def test_problem_list_shapes(fx):
     shapes = fx["config5_shapes"]
     assert len(shapes) == 1024 and sum(s[0] for s in shapes) == 560558
