@@ -18,7 +18,9 @@
 //     queries' fragments held in registers for the whole tile), then the online softmax per
 //     query (a lane and its partner 32 lanes away hold the query's scores), then
 //     O^T = V^T . P^T, with P handed from the S^T accumulators to the MFMA operand layout by one
-//     v_permlane32_swap.  The running maximum, sum and the rescaling of O are lane-local.
+//     v_permlane32_swap.  The running maximum, sum and the rescaling of O are lane-local; the
+//     maximum is lazy (it moves only when a score passes it by more than 2^8 in weight), so O
+//     is rescaled on few steps.
 //   - The epilogue divides by the softmax sum and stores runs of 16 bytes.
 // Included by ptg_kernels.hip (one translation unit: the watchdog word and the XCD-aware tile
 // order are shared).
@@ -43,6 +45,8 @@ constexpr int STEP_BYTES = 2 * BLK_BYTES;         // K block, then V block
 constexpr int LOADS = BLK_BYTES / 1024;           // 1 KB copies per producer per step
 constexpr int INFLIGHT = (STAGES < 63 / LOADS) ? STAGES : 63 / LOADS;
 static_assert(D == 128 && BLK_BYTES % 1024 == 0, "head dimension 128");
+// How far (log2 units) the lazy running maximum of the softmax may trail the true one.
+constexpr float kLazyMax = 8.0f;
 
 // K rows are read by ds_read_b128 (16 lanes = 16 consecutive keys at one chunk): the chunk
 // index XOR the key's low 4 bits puts them in 16 distinct 16-byte bank groups.  V rows are read
@@ -154,12 +158,15 @@ __device__ __forceinline__ float partner(float v, int lane) {
   return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
 }
 
+// NEG: the scale is negative.
+template <bool NEG>
 __device__ __forceinline__ void consumer(const Args& a, const int32_t* off, const int32_t* pre, char* ring,
                                          uint32_t* full, uint32_t* empty, uint32_t* abort, int cw) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   const int lane = lane_id();
   const int hi = lane >> 5;
   const int nsteps = a.L / BKV;
+  const float s_log2 = a.scale_log2, s_abs = NEG ? -a.scale_log2 : a.scale_log2;
   // K fragment (MFMA A operand: key row lane % 32 of a 32-key block, d-chunk 2 kk + hi of the
   // 16-deep slice kk): physical chunk (2 kk + hi) ^ (key & 15) = (hi ^ (lane & 15)) ^ 2 kk.
   const int k_off = (lane & 31) * ROW_BYTES + ((hi ^ (lane & 15)) << 4);
@@ -174,6 +181,13 @@ __device__ __forceinline__ void consumer(const Args& a, const int32_t* off, cons
     const int d = (b & 1) * 16 + (i & 3) * 4;
     v_off = key * ROW_BYTES + (((d >> 3) ^ swz_n<16>(key)) << 4) + ((d >> 2) & 1) * 8;
   }
+  // the per-slice K offsets and per-d-block V offsets, kept in registers so that a fragment
+  // read costs one address add (the slot) and an immediate offset (block, slice)
+  int koff[8], voff[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = k_off ^ (kk << 5);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) voff[db] = v_off ^ (db << 6);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.Q, (uint32_t)a.q_bytes);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.O, (uint32_t)a.o_bytes);
 
@@ -205,40 +219,45 @@ __device__ __forceinline__ void consumer(const Args& a, const int32_t* off, cons
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(kb_lds + kb * 32 * ROW_BYTES + (opaque(k_off) ^ (kk << 5)));
+              *reinterpret_cast<const bf16x8*>(kb_lds + kb * 32 * ROW_BYTES + koff[kk]);
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc[kb], 0, 0, 0);
         }
       }
     };
-    // Online softmax of one step's scores (log2 domain): updates the running maximum and sum,
-    // rescales O, and leaves the weights in place of the scores.
+    // Online softmax of one step's scores (log2 domain, scale s), with a lazy running maximum:
+    // m moves only when some query of the wave meets a score more than kLazyMax above it.
+    // Until then the weights exp2(s x - m) stay below 2^kLazyMax and O and l keep their scale
+    // (numerator and denominator share it, so the quotient is the same softmax), which saves
+    // the rescaling of O on almost every step.  The maximum of s x is taken as |s| times the
+    // maximum of x (of -x when s < 0): the same value, since rounding is monotone.
     auto softmax = [&](f32x16 (&sc)[2]) {
       float mx = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sc[kb][r] *= a.scale_log2;
-          mx = fmaxf(mx, sc[kb][r]);
-        }
-      mx = fmaxf(mx, partner(mx, lane));
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      float rs = 0.0f;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, NEG ? -sc[kb][r] : sc[kb][r]);
+      mx = fmaxf(mx, partner(mx, lane)) * s_abs;
+      if (__builtin_amdgcn_ballot_w64(mx > m + kLazyMax) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four partial sums: no 32-long add chain
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sc[kb][r] = __builtin_amdgcn_exp2f(sc[kb][r] - m_new);
-          rs += sc[kb][r];
+          sc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], s_log2, -m));
+          rp[r & 3] += sc[kb][r];
         }
+      float rs = (rp[0] + rp[1]) + (rp[2] + rp[3]);
       rs += partner(rs, lane);
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l += rs;
     };
     // O^T += V^T . P^T over the step's four 16-key slices.  The P^T fragment of slice (kb, sl):
     // keys 8 hi .. + 7 for query lane % 32; register group r / 4 = gq holds keys 8 gq + 4 hi +
@@ -257,7 +276,7 @@ __device__ __forceinline__ void consumer(const Args& a, const int32_t* off, cons
         const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const int off_v = (opaque(v_off) ^ (db << 6)) + sl4 * 16 * ROW_BYTES;
+          const int off_v = voff[db] + sl4 * 16 * ROW_BYTES;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_lds + off_v));
           const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_lds + off_v + 4 * ROW_BYTES));
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -390,7 +409,8 @@ __global__ __launch_bounds__(NT, 1) void attention_kernel(Args a) {
   const int wave = (int)uni(threadIdx.x >> 6);
   if (wave < NCONS) {
     __builtin_amdgcn_s_setprio(1);
-    consumer(a, off, pre, ring, full, empty, abort, wave);
+    if (a.scale_log2 < 0.0f) consumer<true>(a, off, pre, ring, full, empty, abort, wave);
+    else consumer<false>(a, off, pre, ring, full, empty, abort, wave);
   } else {
     producer(a, off, pre, ring, full, empty, abort, wave - NCONS);
   }

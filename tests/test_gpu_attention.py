@@ -70,6 +70,40 @@ def test_attention_small(out_dtype, L):
     check_attn(O, v, w.V, f"attention L={L} {out_dtype}")
 
 
+def test_attention_negative_scale():
+    """A negative scale (the running maximum is then taken over the negated scores)."""
+    w = wl.attention(76, 3, 2, 128, 128, counts=np.array([90, 200, 5]))
+    for out_dtype in (torch.float32, torch.bfloat16):
+        O = ptg.ikbo_attention(dev_bf16(w.Q), dev_bf16(w.K), dev_bf16(w.V), dev(w.offsets), scale=-0.3,
+                               out_dtype=out_dtype)
+        v = oracle.ikbo_attention(w.Q, w.K, w.V, w.offsets, -0.3)
+        check_attn(O, v, w.V, f"negative scale {out_dtype}")
+
+
+def test_attention_rising_scores():
+    """Scores that climb about 6 (log2 units) per 64-key block and reach 48: the running maximum
+    the kernel keeps may trail the true one for a block (weights up to 2^8) and must catch up
+    within the context, so both the kept and the rescaled paths run, per query and head."""
+    counts = np.array([70, 129, 3])
+    U, H, D, L = len(counts), 2, 128, 512
+    rng = np.random.default_rng(77)
+    Mc = int(counts.sum())
+    off = np.zeros(U + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    Qf = np.zeros((Mc, H, D), np.float32)
+    Qf[:, :, 0] = rng.uniform(0.5, 1.0, (Mc, H))
+    Qf[:, :, 1:] = rng.normal(0.0, 0.05, (Mc, H, D - 1))
+    Kf = rng.normal(0.0, 0.05, (U, L, H, D)).astype(np.float32)
+    ramp = np.arange(L, dtype=np.float32) * (6.0 / 64.0 / float(np.log2(np.e)))
+    Kf[:, :, :, 0] = ramp[None, :, None] + rng.normal(0.0, 0.3, (U, L, H))
+    Q, K = wl.f32_to_bf16_bits(Qf), wl.f32_to_bf16_bits(Kf)
+    V = wl.f32_to_bf16_bits(rng.uniform(-1, 1, (U, L, H, D)).astype(np.float32))
+    v = oracle.ikbo_attention(Q, K, V, off, 1.0)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        O = ptg.ikbo_attention(dev_bf16(Q), dev_bf16(K), dev_bf16(V), dev(off), scale=1.0, out_dtype=out_dtype)
+        check_attn(O, v, V, f"rising scores {out_dtype}")
+
+
 def test_attention_zero_keys_give_the_mean_exactly():
     """K = 0: every weight is exactly 1, so O is the plain mean of the user's value rows; with
     integer values and L = 128 that mean is exact in fp32 (pins the value path per user and head)."""
