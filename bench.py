@@ -116,18 +116,36 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
     """Warm-cache throughput (back-to-back calls, as for the headline GEMM) plus per-call cold-cache
     times (median, min, p90) for each of the memory-relevant workloads."""
     out = {}
-    # grouped: 64 experts, 16384 rows, K=4096, N=1536, rank-Zipf(1.1) routing
-    w = wl.config3("rank")
-    X, W, off = to_dev(w.X, torch, np), to_dev(w.W, torch, np), torch.from_numpy(w.offsets).cuda()
-    Y = torch.empty((w.M_total, w.N), dtype=torch.bfloat16, device="cuda")
-    call = lambda: ptg.grouped_gemm(X, W, off, out=Y)  # noqa: E731
+    # single small GEMM, 256 cubed, fp32 output: launch- and latency-bound (its fraction of
+    # the MFMA or HBM roof says nothing about the kernel), so time per call is the figure
+    w = wl.config1()
+    A, B = to_dev(w.A, torch, np), to_dev(w.B, torch, np)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    call = lambda: ptg.gemm(A, B, b_layout=w.b_layout, out=C)  # noqa: E731
     _, ms = time_calls(call, steps, warmup, torch)
-    f, b = wl.grouped_flops(w), wl.grouped_bytes(w)
-    out["grouped_moe_64x16384x4096x1536"] = {
-        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
-        "cold_ms": time_cold(call, cold_reps, torch)}
-    del X, W, off, Y, w
+    f, b = wl.dense_flops(w.M, w.N, w.K), wl.dense_bytes(w.M, w.N, w.K, "f32")
+    out["dense_256_f32_latency"] = {
+        "us": ms * 1e3, "tflops": f / ms / 1e9, "gbs": b / ms / 1e6,
+        "cold_ms": time_cold(call, cold_reps, torch),
+        "note": "latency-bound (0.5 MB, 34 MFLOP): no roofline fraction is meaningful"}
+    del A, B, C, w
+    # grouped: 64 experts, 16384 rows, K=4096, N=1536, Zipf(1.1) routing under both readings
+    # of the weights: rank-Zipf (expert e weighted (e+1)^-1.1; every expert gets rows) and
+    # Zipf-sampled weights (most experts empty, one or a few take nearly every row)
+    for reading, name in (("rank", "grouped_moe_64x16384x4096x1536"),
+                          ("sampled", "grouped_moe_64x16384x4096x1536_sampled_zipf")):
+        w = wl.config3(reading)
+        X, W, off = to_dev(w.X, torch, np), to_dev(w.W, torch, np), torch.from_numpy(w.offsets).cuda()
+        Y = torch.empty((w.M_total, w.N), dtype=torch.bfloat16, device="cuda")
+        call = lambda: ptg.grouped_gemm(X, W, off, out=Y)  # noqa: E731
+        _, ms = time_calls(call, steps, warmup, torch)
+        f, b = wl.grouped_flops(w), wl.grouped_bytes(w)
+        out[name] = {
+            "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
+            "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
+            "live_groups": int((w.counts > 0).sum()),
+            "cold_ms": time_cold(call, cold_reps, torch)}
+        del X, W, off, Y, w
     # weight gradient of the same MoE layer: dW_g = X_g^T . dY_g, 64 x 4096 x 1536 bf16
     w = wl.moe_wgrad()
     X, dY, off = to_dev(w.X, torch, np), to_dev(w.dY, torch, np), torch.from_numpy(w.offsets).cuda()
