@@ -116,19 +116,6 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
     """Warm-cache throughput (back-to-back calls, as for the headline GEMM) plus per-call cold-cache
     times (median, min, p90) for each of the memory-relevant workloads."""
     out = {}
-    # single small GEMM, 256 cubed, fp32 output: launch- and latency-bound (its fraction of
-    # the MFMA or HBM roof says nothing about the kernel), so time per call is the figure
-    w = wl.config1()
-    A, B = to_dev(w.A, torch, np), to_dev(w.B, torch, np)
-    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
-    call = lambda: ptg.gemm(A, B, b_layout=w.b_layout, out=C)  # noqa: E731
-    _, ms = time_calls(call, steps, warmup, torch)
-    f, b = wl.dense_flops(w.M, w.N, w.K), wl.dense_bytes(w.M, w.N, w.K, "f32")
-    out["dense_256_f32_latency"] = {
-        "us": ms * 1e3, "tflops": f / ms / 1e9, "gbs": b / ms / 1e6,
-        "cold_ms": time_cold(call, cold_reps, torch),
-        "note": "latency-bound (0.5 MB, 34 MFLOP): no roofline fraction is meaningful"}
-    del A, B, C, w
     # grouped: 64 experts, 16384 rows, K=4096, N=1536, Zipf(1.1) routing under both readings
     # of the weights: rank-Zipf (expert e weighted (e+1)^-1.1; every expert gets rows) and
     # Zipf-sampled weights (most experts empty, one or a few take nearly every row)
