@@ -1091,16 +1091,43 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
   } else {
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<void*>(gidxp), (uint32_t)(m_rows * 4));
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(reinterpret_cast<void*>(Pp), p_bytes);
+    int prow[C::TM16];
 #pragma unroll
     for (int tm = 0; tm < C::TM16; ++tm) {
       const int row = wm * C::WTM + tm * 16 + (lane & 15);
-      const bool row_ok = row < m_rows;
-      const int prow = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, row_ok ? row * 4 : kOutOfRange, 0, 0);
+      prow[tm] = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, row < m_rows ? row * 4 : kOutOfRange, 0, 0);
+    }
+    // Candidates come in runs of one user's rows, so the wave's rows usually all gather the
+    // same P row.  Then its columns are loaded once and copied into every row block (rows
+    // past m_rows take them too; the epilogue never stores those rows).  Lane 0 holds the
+    // wave's first row, which is valid: an idle wave does not get here.
+    const int p0 = (int)uni((uint32_t)prow[0]);
+    bool same = true;
+#pragma unroll
+    for (int tm = 0; tm < C::TM16; ++tm) {
+      const int row = wm * C::WTM + tm * 16 + (lane & 15);
+      if (row < m_rows && prow[tm] != p0) same = false;
+    }
+    if (__builtin_amdgcn_ballot_w64(!same) == 0) {
 #pragma unroll
       for (int tn = 0; tn < C::TN16; ++tn) {
         const int col = wn * C::WTN + tn * 16 + cq;
-        const uint32_t po = (row_ok && col < n_cols) ? (uint32_t)(prow * ldp + col) * 4u : kOutOfRange;
-        acc[tm][tn] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, po, 0, 0));
+        const uint32_t po = col < n_cols ? (uint32_t)(p0 * ldp + col) * 4u : kOutOfRange;
+        const f32x4 p4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, po, 0, 0));
+#pragma unroll
+        for (int tm = 0; tm < C::TM16; ++tm) acc[tm][tn] = p4;
+      }
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < C::TM16; ++tm) {
+        const int row = wm * C::WTM + tm * 16 + (lane & 15);
+        const bool row_ok = row < m_rows;
+#pragma unroll
+        for (int tn = 0; tn < C::TN16; ++tn) {
+          const int col = wn * C::WTN + tn * 16 + cq;
+          const uint32_t po = (row_ok && col < n_cols) ? (uint32_t)(prow[tm] * ldp + col) * 4u : kOutOfRange;
+          acc[tm][tn] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, po, 0, 0));
+        }
       }
     }
   }
