@@ -85,6 +85,27 @@ def test_broadcast_split_user_phase(Ku):
     assert torch.equal(out, again)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_broadcast_large_tiles_runs_of_users_guard_rows(out_dtype):
+    """Candidate phase on the large tiles (at least 128 tiles of 256 x 256) with candidates in
+    runs of one user, as in the workload, so that most waves gather a single user row of P, and
+    a ragged last tile: integer data, bit-exact against the oracle, and the rows around the
+    output (NaN sentinels) untouched."""
+    rng = np.random.default_rng(12)
+    U, Ku, Kc, N = 7, 64, 72, 1024
+    counts = rng.integers(300, 2500, U)
+    idx = np.repeat(np.arange(U), counts).astype(np.int32)
+    Mc = int(idx.size)
+    assert Mc % 256 != 0 and ptg.describe_config(Mc, N, Kc, wl.B_KN)["BM"] == 256
+    Xu, Xc, W = int_bf16(rng, (U, Ku)), int_bf16(rng, (Mc, Kc)), int_bf16(rng, (Ku + Kc, N))
+    buf = torch.full((Mc + 2, N), float("nan"), dtype=out_dtype, device="cuda")
+    out = buf[1:Mc + 1]
+    ptg.broadcast_gemm(dev_bf16(Xu), dev_bf16(Xc), dev(idx), dev_bf16(W), out=out)
+    v = oracle.broadcast_gemm(Xu, Xc, idx, W, wl.B_KN)
+    exact(out, v, f"broadcast large tiles, runs of users, {out_dtype}")
+    assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[Mc + 1]).all()), "guard rows written"
+
+
 def test_broadcast_check_helper():
     idx = torch.tensor([0, 1, 4, 2], dtype=torch.int32, device="cuda")
     with pytest.raises(ptg.PtgError) as e:

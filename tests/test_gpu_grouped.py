@@ -83,6 +83,26 @@ def test_grouped_equals_per_group_gemm():
             assert torch.equal(out[lo:hi], one)
 
 
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+def test_grouped_tile_boundaries_guard_rows(layout):
+    """Experts of exactly 128 and 256 rows and one more or one less (the split between the
+    half tiles, whose upper consumer waves idle, and the full tiles), an empty expert and a
+    one-row expert: integer data, bit-exact against the oracle, guard rows untouched."""
+    counts = np.array([128, 256, 129, 0, 257, 384, 127, 1])
+    G, K, N = len(counts), 136, 264
+    M = int(counts.sum())
+    rng = np.random.default_rng(9)
+    X = int_bf16(rng, (M, K))
+    W = int_bf16(rng, (G, K, N) if layout == wl.B_KN else (G, N, K))
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    buf = torch.full((M + 2, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[1:M + 1]
+    ptg.grouped_gemm(dev_bf16(X), dev_bf16(W), dev(off), w_layout=layout, out=out)
+    exact(out, oracle.grouped_gemm(X, W, layout, off), f"grouped tile boundaries layout={layout}")
+    assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[M + 1]).all()), "guard rows written"
+
+
 def test_grouped_single_group_is_dense():
     w = wl.grouped(8, 1, 333, 136, 200, counts=np.array([333]))
     out, v = run_grouped(w, torch.float32, wl.EPI_NONE)
