@@ -547,6 +547,8 @@ struct FetchTile {
   int64_t kstride;      // bytes per unit of k along the operand
   int K, nsteps;
   bool has;             // false: no tile, the end marker was published
+  bool dead;            // every row of this producer's share lies past the tile's valid rows
+                        // (m-rows of A, n-rows of B stored N x K): nothing to load or stage
   uint32_t vbase0, vbase1;  // per-lane offsets of this producer's loads 0 and 1
   int32_t vflip0, vflip1;   // byte offset added to load q (parity 0 or 1) when it flips (load_flip)
   int kbase0, kbase1;       // k (within a step) of loads 0 and 1; load q + 2 adds ROWS_A or
@@ -618,6 +620,9 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   const int extent = (int)uni((uint32_t)(opA ? t.info.m_rows : t.info.n_cols));
   f.src = uni64(reinterpret_cast<uint64_t>(opA ? (const void*)t.A : (const void*)t.B));
   const bool kmajor = opA ? C::A_KM : C::B_KN;  // k is the operand's row index
+  // The share's first row (of m or n, when that is the operand's row index).  A share past
+  // the valid rows is read by no consumer: the waves that own those rows idle on this tile.
+  f.dead = !kmajor && (i0 - (opA ? 0 : C::A_INSTR)) * 64 / (opA ? C::CPR_A : C::CPR_B) >= extent;
   if (!kmajor) {
     f.bytes = (uint32_t)((int64_t)(extent - 1) * ld * 2 + (int64_t)f.K * 2);
     f.kstride = 2;
@@ -678,7 +683,7 @@ __device__ __forceinline__ void producer_role_regs(const typename S::Args& args,
   FetchTile f = fetch_tile<C, S>(args, 0, pid, opA, i0, sched_lds, info, guards, abort);
   for (uint32_t g = 0;; ++g) {
     // ---- fetch: issue the loads of step fst of tile fj into R (zeros past K) -----------
-    if (f.has) {
+    if (f.has && !f.dead) {
       const int k0 = fst * C::BK;
       const int64_t kbytes = (int64_t)k0 * f.kstride;
       const __amdgpu_buffer_rsrc_t rs =
@@ -703,9 +708,11 @@ __device__ __forceinline__ void producer_role_regs(const typename S::Args& args,
       lds_bump(&full[s]);  // the end marker's step carries no data
       break;
     }
-    char* dst = ring + s * C::STAGE_BYTES + lds_base;
+    if (!f.dead) {
+      char* dst = ring + s * C::STAGE_BYTES + lds_base;
 #pragma unroll
-    for (int q = 0; q < C::LOADS; ++q) *reinterpret_cast<u32x4*>(dst + q * 1024) = R[q];
+      for (int q = 0; q < C::LOADS; ++q) *reinterpret_cast<u32x4*>(dst + q * 1024) = R[q];
+    }
     // LDS runs one wave's accesses in order: the writes land before the count moves
     lds_bump(&full[s]);
     // ---- advance the fetch side -------------------------------------------------------
