@@ -159,7 +159,9 @@ ptg_status ptg_ikbo_attention(int64_t U, int64_t Mc, int64_t H, int64_t D, int64
  *   ptg_gemm_batch_prepare - validates the host array `problems` (count >= 1), writes the
  *       problem table and its tile prefix into `workspace` (device) and synchronises `stream`
  *       so that `problems` may be freed on return.  Rewrite it whenever a pointer or shape
- *       changes.
+ *       changes.  The table lists the problems with the longest reductions first (stable
+ *       otherwise), so the launch ends on its cheapest tiles; the order of execution is not
+ *       observable, since every problem writes only its own C_p.
  *   ptg_gemm_batch_run - launches the batch recorded in `workspace` (no host work, no sync).
  *   ptg_gemm_batch - prepare followed by run.
  */

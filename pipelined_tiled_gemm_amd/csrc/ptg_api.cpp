@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <exception>
+#include <algorithm>
 #include <vector>
 
 #include "ptg.h"
@@ -302,9 +303,20 @@ ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, pt
       if (a + bytes > hi) hi = a + bytes;
     };
     for (int32_t p = 0; p < count; ++p) {
-      const ptg_problem& q = problems[p];
-      ptg_status st = validate_problem(fn, p, q, epi);
+      ptg_status st = validate_problem(fn, p, problems[p], epi);
       if (st) return st;
+    }
+    // Table order = tile order of the launch, whose workgroups take tiles round-robin: the
+    // problems with the most k-steps per tile go first (stable, so equal costs keep the
+    // caller's order), and the cheapest tiles are the last round's, which then ends evenly.
+    // Every problem writes only its own output, so the order changes no result.
+    std::vector<int32_t> order(count);
+    for (int32_t p = 0; p < count; ++p) order[p] = p;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      return (problems[x].K + 63) / 64 > (problems[y].K + 63) / 64;
+    });
+    for (int32_t p = 0; p < count; ++p) {
+      const ptg_problem& q = problems[order[p]];
       ptg::BatchProblem& r = rec[p];
       r.A = q.A; r.B = q.B; r.C = q.C; r.bias = needs_bias(epi) ? q.bias : nullptr;
       r.lda = q.lda; r.ldb = q.ldb; r.ldc = q.ldc;
