@@ -70,12 +70,19 @@ def to_dev(bits, torch, np):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
-def time_calls(fn, steps, warmup, torch):
-    """Untimed warmup, then `steps` calls between device synchronisations.
+def time_calls(fn, steps, warmup, torch, min_warm_s=0.0):
+    """Untimed warmup (`warmup` calls, continued until at least `min_warm_s` seconds of calls
+    have run), then `steps` calls between device synchronisations.
     Returns (wall seconds per call, event milliseconds per call on the current stream)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if min_warm_s > 0:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < min_warm_s:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -112,10 +119,14 @@ def time_cold(fn, reps, torch, flush_bytes=512 << 20):
             "p90": round(t[min(len(t) - 1, (9 * len(t)) // 10)], 4), "reps": reps}
 
 
-def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
+def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2):
     """Warm-cache throughput (back-to-back calls, as for the headline GEMM) plus per-call cold-cache
-    times (median, min, p90) for each of the memory-relevant workloads."""
+    times (median, min, p90) for each of the memory-relevant workloads.  Each workload's inputs
+    are drawn on the host for several seconds while the GPU idles; its warm timing starts after
+    at least `warm_s` seconds of calls, once the part has come back to its clock under load
+    (the first tens of milliseconds after idling run several percent slower)."""
     out = {}
+
     # grouped: 64 experts, 16384 rows, K=4096, N=1536, Zipf(1.1) routing under both readings
     # of the weights: rank-Zipf (expert e weighted (e+1)^-1.1; every expert gets rows) and
     # Zipf-sampled weights (most experts empty, one or a few take nearly every row)
@@ -125,7 +136,7 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
         X, W, off = to_dev(w.X, torch, np), to_dev(w.W, torch, np), torch.from_numpy(w.offsets).cuda()
         Y = torch.empty((w.M_total, w.N), dtype=torch.bfloat16, device="cuda")
         call = lambda: ptg.grouped_gemm(X, W, off, out=Y)  # noqa: E731
-        _, ms = time_calls(call, steps, warmup, torch)
+        _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
         f, b = wl.grouped_flops(w), wl.grouped_bytes(w)
         out[name] = {
             "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
@@ -139,7 +150,7 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
     dW = torch.empty((w.G, w.K, w.N), dtype=torch.bfloat16, device="cuda")
     wq = torch.empty(ptg.grouped_gemm_wgrad_workspace(), dtype=torch.uint8, device="cuda")
     call = lambda: ptg.grouped_gemm_wgrad(X, dY, off, out=dW, workspace=wq)  # noqa: E731
-    _, ms = time_calls(call, steps, warmup, torch)
+    _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, b = wl.wgrad_flops(w), wl.wgrad_bytes(w)
     out["grouped_wgrad_moe_64x16384x4096x1536"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
@@ -153,7 +164,7 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
     Y = torch.empty((w.Mc, w.N), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(ptg.broadcast_gemm_workspace(w.U, w.N), dtype=torch.uint8, device="cuda")
     call = lambda: ptg.broadcast_gemm(Xu, Xc, idx, W, out=Y, workspace=ws)  # noqa: E731
-    _, ms = time_calls(call, steps, warmup, torch)
+    _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, fm, b = wl.broadcast_flops(w), wl.broadcast_flops_materialised(w), wl.broadcast_bytes(w)
     out["broadcast_ikbo_64users_81403cand"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
@@ -169,7 +180,7 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
     off = torch.from_numpy(w.offsets).cuda()
     O = torch.empty((w.Mc, w.H, w.D), dtype=torch.bfloat16, device="cuda")
     call = lambda: ptg.ikbo_attention(Q, K, V, off, scale=w.scale, out=O)  # noqa: E731
-    _, ms = time_calls(call, steps, warmup, torch)
+    _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, b = wl.attention_flops(w), wl.attention_bytes(w)
     out["ikbo_attention_64users_77801cand_L1024_H4_D128"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
@@ -186,7 +197,7 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20):
     ws = torch.empty(ptg.gemm_batch_workspace(len(probs)), dtype=torch.uint8, device="cuda")
     ptg.gemm_batch_prepare(probs, pl.epi, ws)
     call = lambda: ptg.gemm_batch_run(len(probs), ws, torch.bfloat16, pl.epi)  # noqa: E731
-    _, ms = time_calls(call, steps, warmup, torch)
+    _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, b = wl.problem_list_flops(pl), wl.problem_list_bytes(pl)
     out["batch_recsys_1024_bias_silu"] = {
         "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
@@ -217,10 +228,11 @@ def cpu_baseline(w, np, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The warmup brings the GPU to the clock it holds under sustained load (the first
-    # launches of a cold GPU run measurably slower); 200 timed steps take ~0.2 s.
+    # The warmup brings the GPU to the clock it holds under sustained load (the first tens of
+    # milliseconds of a GPU that was idle run several percent slower): 150 steps take ~0.12 s,
+    # and the 200 timed steps ~0.17 s.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
