@@ -621,7 +621,9 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   f.src = uni64(reinterpret_cast<uint64_t>(opA ? (const void*)t.A : (const void*)t.B));
   const bool kmajor = opA ? C::A_KM : C::B_KN;  // k is the operand's row index
   // The share's first row (of m or n, when that is the operand's row index).  A share past
-  // the valid rows is read by no consumer: the waves that own those rows idle on this tile.
+  // the valid rows feeds only output rows (A) or columns (B stored N x K) past the tile's
+  // valid extent, which are never stored; on the large tile its only readers are the waves
+  // that own those rows, and they idle on this tile.  Its stale LDS contents are harmless.
   f.dead = !kmajor && (i0 - (opA ? 0 : C::A_INSTR)) * 64 / (opA ? C::CPR_A : C::CPR_B) >= extent;
   if (!kmajor) {
     f.bytes = (uint32_t)((int64_t)(extent - 1) * ld * 2 + (int64_t)f.K * 2);
