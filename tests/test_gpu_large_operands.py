@@ -74,3 +74,24 @@ def test_grouped_x_beyond_4gib():
         exact(out[rg], v, f"grouped X beyond 4 GiB, expert {g}")
     del X, out
     torch.cuda.empty_cache()
+
+
+def test_wgrad_reduction_window_just_under_2gib():
+    """Weight gradient at its largest accepted operand: X of 2^31 - 8192 bytes (one tile's
+    descriptor spans an expert's whole row range, so X and dY are bounded by 2 GiB), one expert
+    reducing over 261,143 rows.  Columns of dW[g] depend only on the same columns of X, so the
+    oracle takes the sampled columns of X; integer data, exact in fp32."""
+    K, N = 4096, 256
+    M = (1 << 31) // (K * 2) - 1
+    counts = np.array([M - 1000, 1000])
+    off = np.zeros(len(counts) + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    X = int_bf16_gpu((M, K), 25)
+    dY = int_bf16_gpu((M, N), 26)
+    dW = ptg.grouped_gemm_wgrad(X, dY, dev(off), out_dtype=torch.float32)
+    ks = torch.tensor([0, 1, 255, 256, 2047, 2048, 4095], dtype=torch.int64, device="cuda")
+    v = oracle.grouped_wgrad(host_bits(X[:, ks].contiguous()), host_bits(dY), off)
+    got = dW[:, ks, :].reshape(len(counts) * len(ks), N)
+    exact(got, v, "wgrad reduction over a 2 GiB window")
+    del X, dY, dW
+    torch.cuda.empty_cache()
