@@ -553,6 +553,12 @@ struct FetchTile {
   int32_t vflip0, vflip1;   // byte offset added to load q (parity 0 or 1) when it flips (load_flip)
   int kbase0, kbase1;       // k (within a step) of loads 0 and 1; load q + 2 adds ROWS_A or
                             // ROWS_B k-rows when k is the operand's row index, else nothing
+  // Narrow tile: k is the operand's row index and the tile has fewer valid columns than the
+  // tile width, so loads of columns past `extent` would fetch the next tile's data; they take
+  // an out-of-range offset instead.  col0 and col1 are this lane's first column in loads 0
+  // and 1; a flipped load (load_flip) reads column col ^ 16.
+  bool narrow;
+  int extent, col0, col1;
 };
 
 // The tile a workgroup runs as its j-th.  A static scheduler derives it from j.  A dynamic one
@@ -652,6 +658,10 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   f.vbase1 = (uint32_t)(row1 * ld * 2 + c1 * 16);
   f.vflip0 = kmajor ? ((c0 ^ 2) - c0) * 16 : 0;
   f.vflip1 = kmajor ? ((c1 ^ 2) - c1) * 16 : 0;
+  f.narrow = kmajor && extent < (opA ? C::BM : C::BN);
+  f.extent = extent;
+  f.col0 = c0 * 8;
+  f.col1 = c1 * 8;
   f.kbase0 = kmajor ? row0 : c0 * 8;  // k of the chunk's first element
   f.kbase1 = kmajor ? row1 : c1 * 8;
   f.rstep = (uint32_t)(ld * 2 * (opA ? C::ROWS_A : C::ROWS_B));
@@ -690,16 +700,20 @@ __device__ __forceinline__ void producer_role_regs(const typename S::Args& args,
       const int64_t kbytes = (int64_t)k0 * f.kstride;
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(reinterpret_cast<const void*>(f.src + kbytes), f.bytes - (uint32_t)kbytes);
-      if (k0 + C::BK <= f.K) {
+      if (k0 + C::BK <= f.K && !f.narrow) {
 #pragma unroll
         for (int q = 0; q < C::LOADS; ++q)
           R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, load_off<C>(f, q, opA), 0, 0);
       } else {
+        // the last, partial k-step, or a narrow tile: k past K and columns past the tile's
+        // valid ones take an out-of-range offset (zeros, no memory access)
 #pragma unroll
         for (int q = 0; q < C::LOADS; ++q) {
           const int kpos = ((q & 1) ? f.kbase1 : f.kbase0) + (q >> 1) * kq;
-          const uint32_t vo = load_off<C>(f, q, opA);
-          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, k0 + kpos < f.K ? vo : kOutOfRange, 0, 0);
+          const bool flip = opA ? row_flip<C::ROWS_A>(q) : row_flip<C::ROWS_B>(q);
+          const int col = ((q & 1) ? f.col1 : f.col0) ^ (flip ? 16 : 0);
+          const bool ok = k0 + kpos < f.K && (!f.narrow || col < f.extent);
+          R[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? load_off<C>(f, q, opA) : kOutOfRange, 0, 0);
         }
       }
     }

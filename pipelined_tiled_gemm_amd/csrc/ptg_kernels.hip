@@ -169,6 +169,14 @@ __device__ __forceinline__ int upper_index(const int32_t* pre, int n, int64_t x)
 // none at the end.  Within a group, full tiles come in bands of group_m m-tiles walked column
 // by column: the workgroups of one XCD, which take consecutive tiles, then share both the
 // band's rows of X and a few column strips of W_g in their L2.
+//
+// The full tiles of a last round that leaves workgroups idle are split by columns: each
+// becomes two units of BN / 2 columns on two workgroups.  A unit has half the tile's matrix
+// work, and the workgroups would otherwise idle.  Half tiles stay whole: a unit of one would
+// issue as many load instructions as the whole tile (its other columns are only masked) and
+// load the X rows twice, and measured slower.  Every output element keeps its k-sequence, so
+// results do not change.  The tile count is known only on the device, so each workgroup works
+// this out from the prefix sums.
 struct GroupedSched {
   struct Args {
     const __bf16* X;
@@ -182,8 +190,10 @@ struct GroupedSched {
     Guards guard;
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
-  // offsets[G + 1], full-tile prefix[G + 1], half-tile prefix[G + 1], scan scratch
-  static constexpr int LDS_BYTES = 3 * (kMaxGroups + 1) * 4 + 20 * 4;
+  // offsets[G + 1], full-tile prefix[G + 1], half-tile prefix[G + 1], scan scratch, then the
+  // first tile of the last round and the number of its full tiles that are split by columns
+  static constexpr int kScratchInts = 20;
+  static constexpr int LDS_BYTES = 3 * (kMaxGroups + 1) * 4 + kScratchInts * 4 + 2 * 4;
   static constexpr bool kDynamic = false;
 
   // full (more than BM/2 valid rows) and half m-tiles of a group of cnt rows
@@ -214,6 +224,18 @@ struct GroupedSched {
       const int cnt = off[g + 1] - off[g];
       return cnt > 0 ? half_mtiles<C>(cnt) * tn : 0;
     }, pre_half, scratch);
+    static_assert(C::NT / 64 + 1 <= kScratchInts, "scan scratch holds one sum per wave and the total");
+    if (threadIdx.x == 0) {
+      // pre_full[G] and pre_half[G] were written by this thread
+      const int64_t n_full = pre_full[a.G];
+      const int64_t T = n_full + pre_half[a.G];
+      const int64_t grid = gridDim.x;
+      const int64_t last = (T / grid) * grid, rem = T - last;  // the last round's tiles
+      const int64_t nf = n_full > last ? min(rem, n_full - last) : 0;  // its full tiles
+      const bool split = nf > 0 && rem + nf <= grid && a.N % C::BN == 0 && C::BN % 128 == 0;
+      scratch[kScratchInts] = (int32_t)(split ? last : T);
+      scratch[kScratchInts + 1] = (int32_t)(split ? nf : 0);
+    }
   }
 
   template <class C>
@@ -221,8 +243,22 @@ struct GroupedSched {
     const int32_t* off = reinterpret_cast<const int32_t*>(lds);
     const int32_t* pre_full = off + kMaxGroups + 1;
     const int32_t* pre_half = pre_full + kMaxGroups + 1;
+    const int64_t split_from = (pre_half + kMaxGroups + 1)[kScratchInts];
+    const int64_t split_nf = (pre_half + kMaxGroups + 1)[kScratchInts + 1];
     const int r = (int)xcd_rank(blockIdx.x, gridDim.x);
-    const int64_t L = (int64_t)j * gridDim.x + ((j & 1) ? (int64_t)gridDim.x - 1 - r : r);
+    int64_t L = (int64_t)j * gridDim.x + ((j & 1) ? (int64_t)gridDim.x - 1 - r : r);
+    int part = -1;  // column half of a split tile
+    if (split_nf > 0 && L >= split_from) {
+      // units 0 .. 2 nf - 1 are the halves of the round's full tiles, then its half tiles;
+      // past the last tile there is no unit (below)
+      const int64_t u = L - split_from;
+      if (u < 2 * split_nf) {
+        part = (int)(u & 1);
+        L = split_from + u / 2;
+      } else {
+        L = split_from + split_nf + (u - 2 * split_nf);
+      }
+    }
     const int64_t n_full = pre_full[a.G];
     int g, mt, nt;
     if (L < n_full) {
@@ -243,7 +279,8 @@ struct GroupedSched {
       nt = (int)(L2 - pre_half[g]);
     }
     const int row0 = off[g], cnt = off[g + 1] - off[g];  // cnt > 0: the group has tiles
-    const int64_t m0 = (int64_t)row0 + (int64_t)mt * C::BM, n0 = (int64_t)nt * C::BN;
+    const int64_t m0 = (int64_t)row0 + (int64_t)mt * C::BM;
+    const int64_t n0 = (int64_t)nt * C::BN + (part > 0 ? C::BN / 2 : 0);
     const int64_t wsize = (int64_t)a.K * a.N;
     t.A = a.X + m0 * a.K;
     t.lda = a.K;
@@ -252,7 +289,7 @@ struct GroupedSched {
     t.info.tag = 0;  // set by the producer when it publishes the slot
     t.info.K = a.K;
     t.info.m_rows = min(C::BM, cnt - mt * C::BM);
-    t.info.n_cols = (int)min((int64_t)C::BN, (int64_t)a.N - n0);
+    t.info.n_cols = (int)min((int64_t)(part >= 0 ? C::BN / 2 : C::BN), (int64_t)a.N - n0);
     t.info.C = (uint64_t)(a.Y + (m0 * a.N + n0) * a.out_bytes);
     t.info.ldc = a.N;
     t.info.bias = a.bias ? (uint64_t)(a.bias + (int64_t)g * a.N + n0) : 0;

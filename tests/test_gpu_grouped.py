@@ -103,6 +103,26 @@ def test_grouped_tile_boundaries_guard_rows(layout):
     assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[M + 1]).all()), "guard rows written"
 
 
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+def test_grouped_last_round_split_by_columns(layout):
+    """A last round with idle workgroups: its full tiles run as two column halves on two
+    workgroups (on an MI355X, 328 tiles on 256 workgroups: 64 full tiles split into 128 units,
+    then 8 half tiles).  Integer data, bit-exact against the oracle, guard rows untouched."""
+    counts = np.array([40 * 256, 100])
+    G, K, N = len(counts), 72, 2048
+    M = int(counts.sum())
+    rng = np.random.default_rng(13)
+    X = int_bf16(rng, (M, K))
+    W = int_bf16(rng, (G, K, N) if layout == wl.B_KN else (G, N, K))
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    buf = torch.full((M + 2, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[1:M + 1]
+    ptg.grouped_gemm(dev_bf16(X), dev_bf16(W), dev(off), w_layout=layout, out=out)
+    exact(out, oracle.grouped_gemm(X, W, layout, off), f"grouped last round split, layout={layout}")
+    assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[M + 1]).all()), "guard rows written"
+
+
 def test_grouped_single_group_is_dense():
     w = wl.grouped(8, 1, 333, 136, 200, counts=np.array([333]))
     out, v = run_grouped(w, torch.float32, wl.EPI_NONE)
