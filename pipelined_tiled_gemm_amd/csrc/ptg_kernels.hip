@@ -50,6 +50,9 @@ struct DenseSched {
     int32_t epi, out_f32, out_bytes;
     int32_t splits;              // split-K: splits of k_chunk each, outputs c_split apart
     int64_t k_chunk, c_split;
+    // units from split_from on are column halves of the last round's tiles (two per tile);
+    // split_from at or past the tile count: no split (see launch_dense_cfg)
+    int64_t split_from;
     Guards guard;
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
@@ -61,7 +64,12 @@ struct DenseSched {
 
   template <class C>
   __device__ static bool tile(const Args& a, int j, TileSrc& t, char*) {
-    const int64_t L0 = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
+    int64_t L0 = (int64_t)j * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
+    int part = -1;  // column half of a split tile
+    if (L0 >= a.split_from) {
+      part = (int)((L0 - a.split_from) & 1);
+      L0 = a.split_from + (L0 - a.split_from) / 2;
+    }
     const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
     if (L0 >= ntiles * a.splits) return false;
     const int64_t split = L0 / ntiles, L = L0 % ntiles;
@@ -72,7 +80,7 @@ struct DenseSched {
     const int first_m = (int)(grp * a.group_m);
     const int gm = min(a.tiles_m - first_m, a.group_m);
     const int tm = first_m + (int)(in % gm), tn = (int)(in / gm);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN + (part > 0 ? C::BN / 2 : 0);
     t.A = a.A + m0 * a.lda + k0;
     t.lda = a.lda;
     t.B = C::B_KN ? a.B + k0 * a.ldb + n0 : a.B + n0 * a.ldb + k0;
@@ -80,7 +88,7 @@ struct DenseSched {
     t.info.tag = 0;  // set by the producer when it publishes the slot
     t.info.K = (int)min(a.k_chunk, (int64_t)a.K - k0);
     t.info.m_rows = (int)min((int64_t)C::BM, a.M - m0);
-    t.info.n_cols = (int)min((int64_t)C::BN, a.N - n0);
+    t.info.n_cols = (int)min((int64_t)(part >= 0 ? C::BN / 2 : C::BN), a.N - n0);
     t.info.C = (uint64_t)(a.C + (split * a.c_split + m0 * a.ldc + n0) * a.out_bytes);
     t.info.ldc = a.ldc;
     t.info.bias = a.bias ? (uint64_t)(a.bias + n0) : 0;
@@ -594,6 +602,16 @@ static hipError_t launch_dense_cfg(const DenseLaunch& d, hipStream_t stream) {
   a.splits = d.splits > 1 ? d.splits : 1;
   a.k_chunk = d.splits > 1 ? d.k_chunk : d.K;
   a.c_split = d.splits > 1 ? d.c_split : 0;
+  {
+    // A last round that leaves at least half the workgroups idle runs its tiles as column
+    // halves on two workgroups each (every tile full width, so no half is empty).
+    const int64_t total = (int64_t)a.tiles_m * a.tiles_n * a.splits;
+    const int cus = device_cus();
+    const int64_t grid = total < cus ? total : cus;
+    const int64_t last = grid > 0 ? (total / grid) * grid : 0, rem = total - last;
+    const bool split = grid > 0 && rem > 0 && 2 * rem <= grid && d.N % C::BN == 0 && C::BN % 128 == 0;
+    a.split_from = split ? last : total;
+  }
   Guards& g = a.guard;
   span(d.A, mat_bytes(d.M, d.K, d.lda, 2), g.a_lo, g.a_hi);
   span(d.B, d.b_kn ? mat_bytes(d.K, d.N, d.ldb, 2) : mat_bytes(d.N, d.K, d.ldb, 2), g.b_lo, g.b_hi);

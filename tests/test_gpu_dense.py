@@ -72,6 +72,24 @@ def test_medium_tiles_both_consumer_groups(shape):
 
 
 @pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+@pytest.mark.parametrize("shape", [(4352, 4352, 72), (2304, 2304, 72)])
+def test_last_round_split_by_columns(shape, layout):
+    """Tile counts that leave most workgroups idle in the last round, whose tiles then run as
+    column halves on two workgroups (on an MI355X: 289 large tiles, the last 33 split; 324
+    medium tiles, the last 68 split).  Integer data, bit-exact against the oracle, guard rows
+    untouched."""
+    M, N, K = shape
+    rng = np.random.default_rng(M + K)
+    A = int_bf16(rng, (M, K))
+    B = int_bf16(rng, (K, N) if layout == wl.B_KN else (N, K))
+    buf = torch.full((M + 2, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[1:M + 1]
+    ptg.gemm(dev_bf16(A), dev_bf16(B), b_layout=layout, out=out)
+    exact(out, oracle.gemm(A, B, layout), f"dense last round split {shape} layout={layout}")
+    assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[M + 1]).all()), "guard rows written"
+
+
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
 @pytest.mark.parametrize("epi", [wl.EPI_NONE, wl.EPI_BIAS_SILU])
 def test_large_tiles_ragged(layout, epi):
     """Large-tile path (>= 128 tiles of 256 x 256) with ragged M, N and K; sampled rows."""
