@@ -123,6 +123,22 @@ def test_grouped_last_round_split_by_columns(layout):
     assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[M + 1]).all()), "guard rows written"
 
 
+def test_grouped_every_tile_split_when_the_grid_exceeds_the_tiles():
+    """The grid is sized from an upper bound on the tile count (every group may add a partial
+    m-tile), so a small problem can have fewer tiles than workgroups: then every full tile runs
+    as two column halves (here 4 tiles, 8 units).  Integer data, bit-exact."""
+    counts = np.array([512, 0, 0, 0, 0, 0, 0, 0])
+    G, K, N = len(counts), 72, 512
+    M = int(counts.sum())
+    rng = np.random.default_rng(14)
+    X = int_bf16(rng, (M, K))
+    W = int_bf16(rng, (G, K, N))
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    out = ptg.grouped_gemm(dev_bf16(X), dev_bf16(W), dev(off), out_dtype=torch.float32)
+    exact(out, oracle.grouped_gemm(X, W, wl.B_KN, off), "grouped, every tile split")
+
+
 def test_grouped_single_group_is_dense():
     w = wl.grouped(8, 1, 333, 136, 200, counts=np.array([333]))
     out, v = run_grouped(w, torch.float32, wl.EPI_NONE)
