@@ -38,13 +38,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_8192_nk_bf16.txt")
 
 
 def kernel_sources_digest() -> str:
+    """sha256 over the kernel sources and the build script that holds their compile flags."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "pipelined_tiled_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    pkg = os.path.join(ROOT, "pipelined_tiled_gemm_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))
+             if n.endswith((".hip", ".hpp", ".h", ".cpp"))]
+    for path in files + [os.path.join(pkg, "build.py")]:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
     return h.hexdigest()
 
 

@@ -464,8 +464,12 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
 ptg_status ptg_watchdog(uint32_t* value, int32_t clear) {
   PTG_TRY({
     if (!value) return fail(PTG_ERR_INVALID_ARG, "ptg_watchdog: value is NULL");
-    hipError_t e = ptg::read_watchdog(value, clear);
+    uint32_t gemm = 0;
+    uint32_t attention = 0;
+    hipError_t e = ptg::read_watchdog(&gemm, clear);
+    if (e == hipSuccess) e = ptg::read_attention_watchdog(&attention, clear);
     if (e != hipSuccess) return hip_fail(e, "ptg_watchdog");
+    *value = gemm | attention;
     return PTG_OK;
   })
 }

@@ -22,8 +22,7 @@
 //     maximum is lazy (it moves only when a score passes it by more than 2^8 in weight), so O
 //     is rescaled on few steps.
 //   - The epilogue divides by the softmax sum and stores runs of 16 bytes.
-// Included by ptg_kernels.hip (one translation unit: the watchdog word and the XCD-aware tile
-// order are shared).
+// Compiled as its own translation unit (ptg_attention.hip), with its own watchdog word.
 #pragma once
 #include <hip/hip_runtime.h>
 

@@ -272,7 +272,16 @@ __device__ __forceinline__ void lds_put64(uint64_t* p, uint64_t v) {
   if (lane_id() == 0) __asm__ volatile("ds_write_b64 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
 }
 
-extern __device__ uint32_t g_watchdog;
+// One watchdog word per translation unit (each .hip file is its own code object, so the word
+// has internal linkage and each file reads its own back through read_watchdog*).
+static __device__ uint32_t g_watchdog = 0;
+
+// MI300-class parts hand workgroups of one dispatch to their XCDs round-robin (8 XCDs
+// on MI355X).  Renumbering so that consecutive tile indices land on one XCD lets tiles that
+// share A rows or B columns meet in that XCD's L2.
+__device__ __forceinline__ int64_t xcd_rank(int w, int grid) {
+  return (grid % 8 == 0) ? (int64_t)(w % 8) * (grid / 8) + w / 8 : (int64_t)w;
+}
 
 // Stop the workgroup: raise its abort word (every wait returns at once) and record `why`
 // in the device watchdog word (1: a wait timed out, 2: inconsistent tile metadata, 4: a DMA

@@ -23,15 +23,6 @@
 
 namespace ptg {
 
-__device__ uint32_t g_watchdog = 0;
-
-// MI300-class parts hand workgroups of one dispatch to their XCDs round-robin (8 XCDs
-// on MI355X).  Renumbering so that consecutive tile indices land on one XCD lets tiles that
-// share A rows or B columns meet in that XCD's L2.
-__device__ __forceinline__ int64_t xcd_rank(int w, int grid) {
-  return (grid % 8 == 0) ? (int64_t)(w % 8) * (grid / 8) + w / 8 : (int64_t)w;
-}
-
 // ---------------------------------------------------------------------------------------
 // Dense scheduler
 // ---------------------------------------------------------------------------------------
@@ -826,4 +817,3 @@ hipError_t read_watchdog(uint32_t* value, int clear) {
 
 }  // namespace ptg
 
-#include "ptg_attention.hpp"

@@ -136,7 +136,9 @@ hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hip
 hipError_t check_index(const int32_t* idx, int64_t n, int64_t U, hipStream_t stream, int* bad);
 // The dense path's tile configuration for a problem: BM, BN, BK, stages, consumers, producers.
 void dense_config(int64_t M, int64_t N, int64_t K, int b_kn, int32_t cfg[6]);
-// Watchdog word of the bounded waits (nonzero if a wait ever gave up).
+// Watchdog words of the bounded waits (nonzero if a wait ever gave up): the GEMM kernels'
+// word and the attention kernel's word.
 hipError_t read_watchdog(uint32_t* value, int clear);
+hipError_t read_attention_watchdog(uint32_t* value, int clear);
 
 }  // namespace ptg

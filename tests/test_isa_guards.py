@@ -29,15 +29,21 @@ hipcc_missing = shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "k.s"
-    cmd = [build.hipcc(), *build.compile_flags(), "-S", "--cuda-device-only",
-           os.path.join(build.CSRC, "ptg_kernels.hip"), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True)
-    return out.read_text()
+    # every device source, each with the flags the library is built with
+    d = tmp_path_factory.mktemp("isa")
+    text = []
+    for src in build.DEVICE_SOURCES:
+        out = d / (src + ".s")
+        cmd = [build.hipcc(), *build.compile_flags(source=src), "-S", "--cuda-device-only",
+               os.path.join(build.CSRC, src), "-o", str(out)]
+        subprocess.run(cmd, check=True, capture_output=True)
+        text.append(out.read_text())
+    return "\n".join(text)
 
 
 def kernels(asm_text):
-    for m in re.finditer(r"\n(_ZN3ptg10ptg_kernel\S+):", asm_text):
+    # the pipelined GEMM kernels and the attention kernel
+    for m in re.finditer(r"\n(_ZN3ptg(?:10ptg_kernel|4attn16attention_kernel)\S+):", asm_text):
         start = m.start()
         end = asm_text.index(".Lfunc_end", start)
         yield m.group(1), asm_text[start:end].split("\n")

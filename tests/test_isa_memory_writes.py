@@ -23,11 +23,13 @@ SCALAR_WRITES = re.compile(
 
 @pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
 def test_no_scalar_memory_writes(tmp_path):
-    out = tmp_path / "k.s"
-    subprocess.run([build.hipcc(), *build.compile_flags(), "-S", "--cuda-device-only",
-                    os.path.join(build.CSRC, "ptg_kernels.hip"), "-o", str(out)],
-                   check=True, capture_output=True)
-    text = out.read_text()
+    text = ""
+    for src in build.DEVICE_SOURCES:
+        out = tmp_path / (src + ".s")
+        subprocess.run([build.hipcc(), *build.compile_flags(source=src), "-S", "--cuda-device-only",
+                        os.path.join(build.CSRC, src), "-o", str(out)],
+                       check=True, capture_output=True)
+        text += out.read_text() + "\n"
     bad = [line.strip() for line in text.split("\n") if SCALAR_WRITES.match(line)]
     assert not bad, bad[:5]
     # the atomics that exist are vector ones
