@@ -10,7 +10,7 @@ import re
 
 import pytest
 
-from pipelined_tiled_gemm_amd import _ffi
+from pipelined_tiled_gemm_amd import _ffi, build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
@@ -188,3 +188,17 @@ def test_describe_config(L):
     assert L.ptg_describe_config(256, 256, 256, 0, cfg) == OK
     assert list(cfg)[:2] == [128, 128]
     assert L.ptg_describe_config(1, 1, 1, 0, None) == INVALID
+
+
+def test_build_compiles_every_source_with_its_flags():
+    # every source under csrc/ that is a translation unit is built, and only the GEMM kernels
+    # take the max-ilp scheduler (the attention kernel keeps the default one)
+    units = sorted(f for f in os.listdir(build.CSRC) if f.endswith((".hip", ".cpp")))
+    assert units == sorted(build.SOURCES)
+    ilp = "-amdgpu-sched-strategy=max-ilp"
+    assert ilp in build.compile_flags(source="ptg_kernels.hip")
+    assert ilp not in build.compile_flags(source="ptg_attention.hip")
+    assert ilp not in build.compile_flags()
+    for src in build.SOURCES:
+        flags = build.compile_flags(source=src)
+        assert "--offload-arch=gfx950" in flags and "-packed-fp32-ops" in flags
