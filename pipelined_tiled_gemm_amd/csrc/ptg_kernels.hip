@@ -632,14 +632,16 @@ __global__ __launch_bounds__(64) void reduce_splits_kernel(float* out, const flo
   const int64_t quads = count / 4;  // count and n are multiples of 8
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (int64_t)gridDim.x * blockDim.x) {
     f4 acc = reinterpret_cast<const f4*>(parts)[q];
-    // eight partials in flight at a time, added in split order
-    for (int32_t s0 = 1; s0 < splits; s0 += 8) {
-      f4 v[8];
+    // up to 32 partials in flight at a time (the user phase makes at most 32), added in split
+    // order: one round trip to memory per quad instead of four
+    constexpr int kInFlight = 32;
+    for (int32_t s0 = 1; s0 < splits; s0 += kInFlight) {
+      f4 v[kInFlight];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kInFlight; ++i)
         v[i] = s0 + i < splits ? reinterpret_cast<const f4*>(parts + (s0 + i) * count)[q] : f4{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kInFlight; ++i)
         if (s0 + i < splits) acc += v[i];
     }
     if (bias) acc += reinterpret_cast<const f4*>(bias)[(q * 4 % n) / 4];
