@@ -19,20 +19,33 @@
  *     The second operand is either "KN" (K x N row-major, the plain B of C = A.B) or "NK"
  *     (N x K row-major, i.e. B transposed).
  *   - Memory: every matrix/vector pointer is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or retains it past the call's completion on the stream.
- *     Host pointers are only the ptg_problem arrays, read during the call.  Scratch memory
- *     is supplied by the caller (see the *_workspace queries).
+ *     library never allocates device memory, and never frees or retains a caller's pointer
+ *     past the call's completion on the stream.  Host pointers are only the ptg_problem
+ *     arrays, read during the call.  Scratch memory is supplied by the caller (see the
+ *     *_workspace queries).
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
  *     call only enqueues work and returns; results are ready when the stream reaches them.
  *   - Alignment: device pointers must be 16-byte aligned, K and N multiples of 8 and
  *     leading dimensions multiples of 8 elements (16 bytes), else PTG_ERR_UNSUPPORTED.
  *   - Sizes: M = 0 or N = 0 is a valid no-op.  K = 0 is rejected (PTG_ERR_UNSUPPORTED).
+ *     The kernels address one tile of every operand (256 rows), the output included, with
+ *     31-bit byte offsets: a call whose operand or output tile would need more (for the
+ *     output: ((255 * ldc + 256) * element size) >= 2^31) is rejected with
+ *     PTG_ERR_UNSUPPORTED before anything runs.
  *   - Errors are returned, never thrown; ptg_last_error() holds a thread-local message for
  *     the last failing call on the calling thread.  Preconditions on device-resident data
  *     (group offsets, user indices) are not read by the host; violating them is undefined
  *     unless checked with the *_check helpers below.
- *   - Calls are reentrant; the library keeps no state between calls apart from the per-
- *     thread error text and a per-device cache of device properties.
+ *   - Calls are reentrant and may run on several streams and threads at once.  State kept
+ *     between calls: the per-thread error text, a per-device cache of device properties,
+ *     the watchdog words (see ptg_watchdog), the *_check helpers' result words (one per
+ *     check in flight, handed out under a lock) and the pinned host staging buffers of
+ *     ptg_grouped_gemm_ptr_array (see there).
+ *   - Kernel-side faults: every pipeline wait is bounded and every address range is
+ *     checked on the device; a launch that trips one finishes without hanging, sets a
+ *     watchdog bit and leaves its output incomplete.  The enqueueing call has already
+ *     returned PTG_OK by then: ptg_watchdog() reports it, and the *_check helpers return
+ *     PTG_ERR_DEVICE_CHECK while the current device's watchdog word is nonzero.
  */
 #ifndef PTG_H_
 #define PTG_H_
@@ -97,8 +110,12 @@ ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K,
                             void* Y, ptg_dtype y_dtype,
                             const float* bias, ptg_epilogue epi, void* stream);
 
-/* ptg_grouped_gemm_check - validates group_offsets on the device (0 at both ends as stated,
- * nondecreasing), synchronises `stream`, and returns PTG_OK or PTG_ERR_DEVICE_CHECK. */
+/* ptg_grouped_gemm_check - validates group_offsets on the device (offsets[0] = 0,
+ * nondecreasing, offsets[G] = M_total), synchronises `stream`, and returns PTG_OK, or
+ * PTG_ERR_DEVICE_CHECK when the offsets break the precondition or the device's watchdog
+ * word is set (a fault of an earlier launch).  Checks on different streams or threads run
+ * concurrently, each with a result word of its own; up to 256 may be in flight at once
+ * (beyond that PTG_ERR_UNSUPPORTED). */
 ptg_status ptg_grouped_gemm_check(int32_t G, int64_t M_total, const int32_t* group_offsets,
                                   void* stream);
 
@@ -151,36 +168,51 @@ ptg_status ptg_ikbo_attention(int64_t U, int64_t Mc, int64_t H, int64_t D, int64
                               const int32_t* user_offsets, void* O, ptg_dtype o_dtype, void* stream);
 
 /*
- * Batch of independent GEMMs in one persistent launch (the pointer-array form of the grouped
- * GEMM): problem p computes C_p = epi(A_p . B_p + bias_p) with B_p stored K x N (KN).
- * Short problems keep the pipeline full across problem boundaries ("Case Study 2", final
- * stage: stages share circular buffers without draining the pipeline).
- *   ptg_gemm_batch_workspace(count) - bytes of device workspace needed for `count` problems.
- *   ptg_gemm_batch_prepare - validates the host array `problems` (count >= 1), writes the
- *       problem table and its tile prefix into `workspace` (device) and synchronises `stream`
- *       so that `problems` may be freed on return.  Rewrite it whenever a pointer or shape
- *       changes.  The table lists the problems with the longest reductions first (stable
- *       otherwise), so the launch ends on its cheapest tiles; the order of execution is not
- *       observable, since every problem writes only its own C_p.
- *   ptg_gemm_batch_run - launches the batch recorded in `workspace` (no host work, no sync).
- *   ptg_gemm_batch - prepare followed by run.
+ * Pointer-array grouped GEMM: independent problems, each with its own pointers, shapes and
+ * leading dimensions, in one persistent launch ("Case Study 3: Distributed Grouped GEMM for
+ * LLM Pretraining": grouped matrix products; "Case Study 2", final stage of the linear-
+ * compression kernel: short problems keep the pipeline full across problem boundaries).
+ * Problem p computes C_p = epi(A_p . B_p + bias_p), B_p stored K x N (KN).
+ *   ptg_grouped_gemm_ptr_array_workspace(count) - bytes of DEVICE workspace for `count`
+ *       problems (0 for count <= 0): a 256-byte header, the tile prefix and 80 bytes per problem.
+ *   ptg_grouped_gemm_ptr_array(count, problems, c_dtype, epi, workspace, ws_bytes, stream) -
+ *       validates the HOST array `problems` (1 <= count <= 2048), writes the problem table into
+ *       `workspace` with an asynchronous copy on `stream`, and launches the batch after it.
+ *       `problems` may be freed or reused as soon as the call returns: the table is staged in a
+ *       pinned host buffer of the library's own (a small per-device pool, allocated on first
+ *       use and kept until exit; a buffer is reused once the copy that read it has completed,
+ *       and the call waits on the host only if every buffer of the pool is still in flight).
+ *       There is no host synchronisation of `stream`.  Each C_p must be of `c_dtype`.
+ *   ptg_grouped_gemm_ptr_array_prepare / _run - the same call in two halves, so that a table
+ *       written once can be launched many times: prepare validates and writes the table (it
+ *       records c_dtype and epi in the table); run launches the batch recorded in `workspace`
+ *       and does no host work.  run with a c_dtype, epi or count that differs from the
+ *       table's is refused on the device: the kernel compares them with the table header
+ *       before it touches any operand, writes nothing, and sets watchdog bit 2.
+ * The table lists the problems with the longest reductions first (stable otherwise), so the
+ * launch ends on its cheapest tiles; the order of execution is not observable, since every
+ * problem writes only its own C_p.  Rewrite the table whenever a pointer or shape changes.
+ * Calls that run at the same time must not share a workspace.
+ * Errors: per problem as ptg_gemm (the failing problem's index is in ptg_last_error), plus
+ * PTG_ERR_WORKSPACE; PTG_ERR_UNSUPPORTED also when a problem's output tile of 256 rows
+ * cannot be addressed with 31-bit byte offsets (((255 * ldc + 256) * element size) >= 2^31).
  */
 typedef struct {
     int64_t M, N, K;          /* M >= 0, N and K multiples of 8, K > 0 */
     const void* A;            /* bf16 [M x K], row stride lda */
     const void* B;            /* bf16 [K x N], row stride ldb (KN layout) */
-    void* C;                  /* [M x N] of the batch's c_dtype, row stride ldc */
+    void* C;                  /* [M x N] of the call's c_dtype, row stride ldc */
     const float* bias;        /* float32 [N] (BIAS epilogues) or NULL */
     int64_t lda, ldb, ldc;
 } ptg_problem;
 
-size_t ptg_gemm_batch_workspace(int32_t count);
-ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, ptg_epilogue epi,
-                                  void* workspace, size_t ws_bytes, void* stream);
-ptg_status ptg_gemm_batch_run(int32_t count, const void* workspace, size_t ws_bytes,
-                              ptg_dtype c_dtype, ptg_epilogue epi, void* stream);
-ptg_status ptg_gemm_batch(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype,
-                          ptg_epilogue epi, void* workspace, size_t ws_bytes, void* stream);
+size_t ptg_grouped_gemm_ptr_array_workspace(int32_t count);
+ptg_status ptg_grouped_gemm_ptr_array(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype,
+                                      ptg_epilogue epi, void* workspace, size_t ws_bytes, void* stream);
+ptg_status ptg_grouped_gemm_ptr_array_prepare(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype,
+                                              ptg_epilogue epi, void* workspace, size_t ws_bytes, void* stream);
+ptg_status ptg_grouped_gemm_ptr_array_run(int32_t count, const void* workspace, size_t ws_bytes,
+                                          ptg_dtype c_dtype, ptg_epilogue epi, void* stream);
 
 /*
  * ptg_broadcast_gemm - in-kernel broadcast linear compression ("Case Study 2: In-Kernel
@@ -203,6 +235,8 @@ ptg_status ptg_gemm_batch(int32_t count, const ptg_problem* problems, ptg_dtype 
  * slice order (results do not depend on timing).  The workspace query returns
  * U * N * 4 * (1 + S) bytes, S the slice count for U x N (a function of U and N only, at most
  * 32; S = 1 needs no partials: U * N * 4 bytes).
+ * Errors: as ptg_gemm, plus PTG_ERR_WORKSPACE; PTG_ERR_UNSUPPORTED also when U * N * 4 >= 2^31
+ * (the gather addresses P with 31-bit byte offsets).
  */
 size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N);
 ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N,
@@ -213,7 +247,8 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
                               void* workspace, size_t ws_bytes, void* stream);
 
 /* ptg_broadcast_gemm_check - validates 0 <= user_idx[r] < U on the device, synchronises
- * `stream`, returns PTG_OK or PTG_ERR_DEVICE_CHECK. */
+ * `stream`, returns PTG_OK or PTG_ERR_DEVICE_CHECK (also when the device's watchdog word is
+ * set); concurrent as ptg_grouped_gemm_check. */
 ptg_status ptg_broadcast_gemm_check(int64_t U, int64_t Mc, const int32_t* user_idx, void* stream);
 
 /* Text of a status code (static storage), and the calling thread's last error detail. */

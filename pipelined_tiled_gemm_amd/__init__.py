@@ -21,9 +21,8 @@ from . import _ffi
 __all__ = [
     "PtgError", "B_KN", "B_NK", "EPI_NONE", "EPI_BIAS", "EPI_SILU", "EPI_BIAS_SILU",
     "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace", "ikbo_attention",
-    "gemm_batch_workspace",
-    "gemm_batch_prepare",
-    "gemm_batch_run", "gemm_batch", "broadcast_gemm_workspace", "broadcast_gemm",
+    "grouped_gemm_ptr_array_workspace", "grouped_gemm_ptr_array", "grouped_gemm_ptr_array_prepare",
+    "grouped_gemm_ptr_array_run", "broadcast_gemm_workspace", "broadcast_gemm",
     "broadcast_gemm_check", "watchdog", "version", "describe_config", "status_string",
     "last_error", "library_path",
 ]
@@ -100,6 +99,19 @@ def _rowmajor_ld(t: torch.Tensor, name: str) -> int:
     return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
 
 
+def _bias_for(bias: Optional[torch.Tensor], epi: int, n: int, name: str, dims: int = 1):
+    """The bias an epilogue reads (float32, on the GPU, contiguous, at least n entries), or
+    None when the epilogue reads none."""
+    if epi not in (EPI_BIAS, EPI_BIAS_SILU):
+        return None
+    if bias is None:
+        raise ValueError(f"the epilogue needs a {name}")
+    _need(bias, name, torch.float32, dims)
+    if not bias.is_contiguous() or bias.numel() < n:
+        raise ValueError(f"{name} must be contiguous with at least {n} entries")
+    return bias
+
+
 def describe_config(M: int, N: int, K: int, b_layout: int = B_KN):
     cfg = (ctypes.c_int32 * 6)()
     _check(_lib().ptg_describe_config(M, N, K, b_layout, cfg))
@@ -129,8 +141,7 @@ def gemm(A: torch.Tensor, B: torch.Tensor, *, b_layout: int = B_KN, out: Optiona
     _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must be [{M}, {N}]")
-    if bias is not None:
-        _need(bias, "bias", torch.float32, 1)
+    bias = _bias_for(bias, epi, N, "bias")
     _check(_lib().ptg_gemm(M, N, K, _ptr(A), _rowmajor_ld(A, "A"), _ptr(B), _rowmajor_ld(B, "B"),
                            b_layout, _ptr(out), _rowmajor_ld(out, "out"), _dtype_code(out.dtype),
                            _ptr(bias), epi, _stream(stream)))
@@ -156,8 +167,9 @@ def grouped_gemm(X: torch.Tensor, W: torch.Tensor, group_offsets: torch.Tensor, 
         out = torch.empty((M, N), dtype=out_dtype, device=X.device)
     if not out.is_contiguous() or tuple(out.shape) != (M, N):
         raise ValueError(f"out must be a contiguous [{M}, {N}] tensor")
-    if bias is not None:
-        _need(bias, "bias", torch.float32, 2)
+    if bias is not None and epi in (EPI_BIAS, EPI_BIAS_SILU) and tuple(bias.shape) != (G, N):
+        raise ValueError(f"bias must be [{G}, {N}]")
+    bias = _bias_for(bias, epi, G * N, "bias", dims=2)
     _check(_lib().ptg_grouped_gemm(G, M, N, K, _ptr(X), _ptr(W), w_layout, _ptr(group_offsets),
                                    _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi, _stream(stream)))
     return out
@@ -231,53 +243,81 @@ def grouped_gemm_check(group_offsets: torch.Tensor, M_total: int, stream=None) -
                                          _stream(stream)))
 
 
-def gemm_batch_workspace(count: int) -> int:
-    return int(_lib().ptg_gemm_batch_workspace(count))
+def grouped_gemm_ptr_array_workspace(count: int) -> int:
+    return int(_lib().ptg_grouped_gemm_ptr_array_workspace(count))
 
 
-def _problem_array(problems: Sequence):
+def _problem_array(problems: Sequence, epi: int):
+    """The ptg_problem array of [(A, B, C[, bias]), ...] (B stored K x N) and the one output
+    dtype every C shares."""
+    if len(problems) == 0:
+        raise ValueError("at least one problem is needed")
     arr = (_ffi.ProblemStruct * len(problems))()
+    out_dtype = None
     for i, pr in enumerate(problems):
         A, B, C = pr[0], pr[1], pr[2]
         bias = pr[3] if len(pr) > 3 else None
         _need(A, f"A[{i}]", torch.bfloat16, 2)
         _need(B, f"B[{i}]", torch.bfloat16, 2)
-        if C.dim() != 2 or C.device.type != "cuda":
+        if not isinstance(C, torch.Tensor) or C.dim() != 2 or C.device.type != "cuda":
             raise ValueError(f"C[{i}] must be a 2-D GPU tensor")
+        if out_dtype is None:
+            out_dtype = C.dtype
+        elif C.dtype != out_dtype:
+            raise TypeError(f"C[{i}] is {C.dtype}, but C[0] is {out_dtype}: every output of a batch "
+                            "must have one dtype")
+        _dtype_code(C.dtype)
         M, K = A.shape
-        if B.shape[0] != K or tuple(C.shape) != (M, B.shape[1]):
+        N = B.shape[1]
+        if B.shape[0] != K or tuple(C.shape) != (M, N):
             raise ValueError(f"problem {i}: shapes do not match")
+        if epi in (EPI_BIAS, EPI_BIAS_SILU):
+            if bias is None:
+                raise ValueError(f"problem {i}: the epilogue needs a bias")
+            _need(bias, f"bias[{i}]", torch.float32, 1)
+            if not bias.is_contiguous() or bias.numel() < N:
+                raise ValueError(f"bias[{i}] must be contiguous with at least N = {N} entries")
+        else:
+            bias = None
         s = arr[i]
-        s.M, s.N, s.K = M, B.shape[1], K
+        s.M, s.N, s.K = M, N, K
         s.A, s.B, s.C, s.bias = _ptr(A), _ptr(B), _ptr(C), _ptr(bias)
         s.lda, s.ldb, s.ldc = _rowmajor_ld(A, "A"), _rowmajor_ld(B, "B"), _rowmajor_ld(C, "C")
-    return arr
+    return arr, out_dtype
 
 
-def gemm_batch_prepare(problems: Sequence, epi: int, workspace: torch.Tensor, stream=None) -> None:
-    """Record problems [(A, B, C[, bias]), ...] (B stored K x N) in a device workspace."""
-    arr = _problem_array(problems)
-    _check(_lib().ptg_gemm_batch_prepare(len(problems), arr, epi, _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+def _workspace_bytes(workspace: torch.Tensor) -> int:
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.numel() * workspace.element_size()
 
 
-def gemm_batch_run(count: int, workspace: torch.Tensor, out_dtype: torch.dtype, epi: int,
-                   stream=None) -> None:
-    _check(_lib().ptg_gemm_batch_run(count, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _dtype_code(out_dtype), epi, _stream(stream)))
-
-
-def gemm_batch(problems: Sequence, epi: int, workspace: Optional[torch.Tensor] = None,
-               stream=None) -> torch.Tensor:
-    """Prepare and run a batch in one call; returns the workspace used."""
+def grouped_gemm_ptr_array(problems: Sequence, epi: int = EPI_NONE, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """C_p = epi(A_p . B_p + bias_p) for problems [(A, B, C[, bias]), ...] (B stored K x N, every C
+    of one dtype) in one persistent launch; returns the workspace used."""
+    arr, out_dtype = _problem_array(problems, epi)
     if workspace is None:
-        dev = problems[0][0].device
-        workspace = torch.empty(gemm_batch_workspace(len(problems)), dtype=torch.uint8, device=dev)
-    arr = _problem_array(problems)
-    out_dtype = problems[0][2].dtype
-    _check(_lib().ptg_gemm_batch(len(problems), arr, _dtype_code(out_dtype), epi, _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+        workspace = torch.empty(grouped_gemm_ptr_array_workspace(len(problems)), dtype=torch.uint8,
+                                device=problems[0][0].device)
+    _check(_lib().ptg_grouped_gemm_ptr_array(len(problems), arr, _dtype_code(out_dtype), epi, _ptr(workspace),
+                                             _workspace_bytes(workspace), _stream(stream)))
     return workspace
+
+
+def grouped_gemm_ptr_array_prepare(problems: Sequence, epi: int, workspace: torch.Tensor, stream=None) -> None:
+    """Write the table of problems [(A, B, C[, bias]), ...] into a device workspace."""
+    arr, out_dtype = _problem_array(problems, epi)
+    _check(_lib().ptg_grouped_gemm_ptr_array_prepare(len(problems), arr, _dtype_code(out_dtype), epi,
+                                                     _ptr(workspace), _workspace_bytes(workspace),
+                                                     _stream(stream)))
+
+
+def grouped_gemm_ptr_array_run(count: int, workspace: torch.Tensor, out_dtype: torch.dtype, epi: int,
+                               stream=None) -> None:
+    """Launch the batch whose table `workspace` holds (written by grouped_gemm_ptr_array_prepare)."""
+    _check(_lib().ptg_grouped_gemm_ptr_array_run(count, _ptr(workspace), _workspace_bytes(workspace),
+                                                 _dtype_code(out_dtype), epi, _stream(stream)))
 
 
 def broadcast_gemm_workspace(U: int, N: int) -> int:
@@ -312,8 +352,7 @@ def broadcast_gemm(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W
     if workspace is None:
         workspace = torch.empty(max(broadcast_gemm_workspace(U, N), 16), dtype=torch.uint8,
                                 device=Xc.device)
-    if bias is not None:
-        _need(bias, "bias", torch.float32, 1)
+    bias = _bias_for(bias, epi, N, "bias")
     _check(_lib().ptg_broadcast_gemm(U, Mc, Ku, Kc, N, _ptr(Xu), _ptr(Xc), _ptr(user_idx), _ptr(W),
                                      w_layout, _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi,
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),

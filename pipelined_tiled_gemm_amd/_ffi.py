@@ -24,7 +24,8 @@ STATUS_NAMES = {
 EXPORTS = (
     "ptg_gemm", "ptg_grouped_gemm", "ptg_grouped_gemm_check", "ptg_grouped_gemm_wgrad",
     "ptg_grouped_gemm_wgrad_workspace", "ptg_ikbo_attention",
-    "ptg_gemm_batch_workspace", "ptg_gemm_batch_prepare", "ptg_gemm_batch_run", "ptg_gemm_batch",
+    "ptg_grouped_gemm_ptr_array_workspace", "ptg_grouped_gemm_ptr_array",
+    "ptg_grouped_gemm_ptr_array_prepare", "ptg_grouped_gemm_ptr_array_run",
     "ptg_broadcast_gemm_workspace", "ptg_broadcast_gemm", "ptg_broadcast_gemm_check",
     "ptg_status_string", "ptg_last_error", "ptg_watchdog", "ptg_version", "ptg_describe_config",
 )
@@ -48,9 +49,16 @@ def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str):
+    """A declared handle on a build of the library at `path` (the product build, or a
+    test build of the same sources); raises if the file is missing."""
     if not os.path.exists(path):
         raise ImportError(
-            f"libptg.so not found at {path}: build it with "
+            f"{os.path.basename(path)} not found at {path}: build it with "
             "`python -m pipelined_tiled_gemm_amd.build` (hipcc, gfx950)")
     L = ctypes.CDLL(path)
     i64, i32, p, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
@@ -62,18 +70,18 @@ def load(path: str = LIB_PATH):
     L.ptg_ikbo_attention.argtypes = [i64, i64, i64, i64, i64, ctypes.c_float, p, p, p, p, p, e, p]
     L.ptg_grouped_gemm_wgrad_workspace.argtypes = []
     L.ptg_grouped_gemm_wgrad_workspace.restype = sz
-    L.ptg_gemm_batch_workspace.argtypes = [i32]
-    L.ptg_gemm_batch_workspace.restype = sz
-    L.ptg_gemm_batch_prepare.argtypes = [i32, ctypes.POINTER(ProblemStruct), e, p, sz, p]
-    L.ptg_gemm_batch_run.argtypes = [i32, p, sz, e, e, p]
-    L.ptg_gemm_batch.argtypes = [i32, ctypes.POINTER(ProblemStruct), e, e, p, sz, p]
+    L.ptg_grouped_gemm_ptr_array_workspace.argtypes = [i32]
+    L.ptg_grouped_gemm_ptr_array_workspace.restype = sz
+    L.ptg_grouped_gemm_ptr_array.argtypes = [i32, ctypes.POINTER(ProblemStruct), e, e, p, sz, p]
+    L.ptg_grouped_gemm_ptr_array_prepare.argtypes = [i32, ctypes.POINTER(ProblemStruct), e, e, p, sz, p]
+    L.ptg_grouped_gemm_ptr_array_run.argtypes = [i32, p, sz, e, e, p]
     L.ptg_broadcast_gemm_workspace.argtypes = [i64, i64]
     L.ptg_broadcast_gemm_workspace.restype = sz
     L.ptg_broadcast_gemm.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, e, p, e, p, e, p, sz, p]
     L.ptg_broadcast_gemm_check.argtypes = [i64, i64, p, p]
     for f in (L.ptg_gemm, L.ptg_grouped_gemm, L.ptg_grouped_gemm_check, L.ptg_grouped_gemm_wgrad, L.ptg_ikbo_attention,
-              L.ptg_gemm_batch_prepare,
-              L.ptg_gemm_batch_run, L.ptg_gemm_batch, L.ptg_broadcast_gemm,
+              L.ptg_grouped_gemm_ptr_array, L.ptg_grouped_gemm_ptr_array_prepare,
+              L.ptg_grouped_gemm_ptr_array_run, L.ptg_broadcast_gemm,
               L.ptg_broadcast_gemm_check):
         f.restype = e
     L.ptg_status_string.argtypes = [e]
@@ -86,5 +94,4 @@ def load(path: str = LIB_PATH):
     L.ptg_version.restype = i32
     L.ptg_describe_config.argtypes = [i64, i64, i64, e, ctypes.POINTER(ctypes.c_int32)]
     L.ptg_describe_config.restype = e
-    _lib = L
     return L

@@ -8,6 +8,8 @@
 #include <cstring>
 #include <exception>
 #include <algorithm>
+#include <memory>
+#include <mutex>
 #include <vector>
 
 #include "ptg.h"
@@ -67,6 +69,25 @@ bool fits31(int64_t rows, int64_t ld, int64_t cols) {
   return bytes < ((int64_t)1 << 31);
 }
 
+// The epilogue addresses an output tile of up to 256 rows and 256 columns (elements of
+// `osz` bytes, row stride ldc) with 31-bit byte offsets, and takes ldc as a 32-bit value.
+bool out_fits(int64_t ldc, int64_t osz) {
+  return ldc < ((int64_t)1 << 31) && (255 * ldc + 256) * osz < ((int64_t)1 << 31);
+}
+
+// After a synchronising check: a set watchdog word (a kernel of an earlier launch tripped a
+// bounded wait or a range check, and its output is incomplete) is reported as a failed check.
+ptg_status watchdog_status(const char* fn) {
+  uint32_t gemm = 0, attention = 0;
+  hipError_t e = ptg::read_watchdog(&gemm, 0);
+  if (e == hipSuccess) e = ptg::read_attention_watchdog(&attention, 0);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (gemm | attention)
+    return fail(PTG_ERR_DEVICE_CHECK, "%s: the device's watchdog word is 0x%x (an earlier launch stopped early)",
+                fn, gemm | attention);
+  return PTG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,8 +134,9 @@ ptg_status ptg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (bias && !aligned16(bias)))
       return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned", fn);
     const bool kn = b_layout == PTG_B_KN;
-    if (!fits31(256, lda, K) || !(kn ? fits31(K, ldb, 256) : fits31(256, ldb, K)) || !fits31(512, ldc, 2 * N))
-      return fail(PTG_ERR_UNSUPPORTED, "%s: operand tile exceeds 2 GiB of addressing", fn);
+    if (!fits31(256, lda, K) || !(kn ? fits31(K, ldb, 256) : fits31(256, ldb, K)) ||
+        !out_fits(ldc, c_dtype == PTG_F32 ? 4 : 2))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand or output tile exceeds 2 GiB of addressing", fn);
     ptg::DenseLaunch d{};
     d.A = A; d.B = B; d.C = C; d.bias = needs_bias(epi) ? bias : nullptr;
     d.lda = lda; d.ldb = ldb; d.ldc = ldc;
@@ -147,8 +169,9 @@ ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, co
         (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
       return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (offsets 4-byte)", fn);
     const bool kn = w_layout == PTG_B_KN;
-    if (!fits31(256, K, K) || !(kn ? fits31(K, N, 256) : fits31(256, K, K)))
-      return fail(PTG_ERR_UNSUPPORTED, "%s: operand tile exceeds 2 GiB of addressing", fn);
+    if (!fits31(256, K, K) || !(kn ? fits31(K, N, 256) : fits31(256, K, K)) ||
+        !out_fits(N, y_dtype == PTG_F32 ? 4 : 2))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand or output tile exceeds 2 GiB of addressing", fn);
     ptg::GroupedLaunch g{};
     g.X = X; g.W = W; g.Y = Y; g.bias = needs_bias(epi) ? bias : nullptr; g.offsets = group_offsets;
     g.M_total = M_total; g.N = N; g.K = K; g.G = G;
@@ -234,10 +257,12 @@ ptg_status ptg_grouped_gemm_check(int32_t G, int64_t M_total, const int32_t* gro
     const char* fn = "ptg_grouped_gemm_check";
     if (G <= 0 || M_total < 0 || !group_offsets) return fail(PTG_ERR_INVALID_ARG, "%s: bad arguments", fn);
     int bad = 0;
-    hipError_t e = ptg::check_offsets(group_offsets, G, M_total, reinterpret_cast<hipStream_t>(stream), &bad);
+    int busy = 0;
+    hipError_t e = ptg::check_offsets(group_offsets, G, M_total, reinterpret_cast<hipStream_t>(stream), &bad, &busy);
     if (e != hipSuccess) return hip_fail(e, fn);
+    if (busy) return fail(PTG_ERR_UNSUPPORTED, "%s: %d checks already in flight", fn, ptg::kCheckWords);
     if (bad) return fail(PTG_ERR_DEVICE_CHECK, "%s: group offsets violate the precondition", fn);
-    return PTG_OK;
+    return watchdog_status(fn);
   })
 }
 
@@ -245,21 +270,27 @@ ptg_status ptg_broadcast_gemm_check(int64_t U, int64_t Mc, const int32_t* user_i
   PTG_TRY({
     const char* fn = "ptg_broadcast_gemm_check";
     if (U <= 0 || Mc < 0 || (Mc > 0 && !user_idx)) return fail(PTG_ERR_INVALID_ARG, "%s: bad arguments", fn);
-    if (Mc == 0) return PTG_OK;
+    if (Mc == 0) return watchdog_status(fn);
     int bad = 0;
-    hipError_t e = ptg::check_index(user_idx, Mc, U, reinterpret_cast<hipStream_t>(stream), &bad);
+    int busy = 0;
+    hipError_t e = ptg::check_index(user_idx, Mc, U, reinterpret_cast<hipStream_t>(stream), &bad, &busy);
     if (e != hipSuccess) return hip_fail(e, fn);
+    if (busy) return fail(PTG_ERR_UNSUPPORTED, "%s: %d checks already in flight", fn, ptg::kCheckWords);
     if (bad) return fail(PTG_ERR_DEVICE_CHECK, "%s: a user index is outside [0, U)", fn);
-    return PTG_OK;
+    return watchdog_status(fn);
   })
 }
 
-size_t ptg_gemm_batch_workspace(int32_t count) {
+size_t ptg_grouped_gemm_ptr_array_workspace(int32_t count) {
   if (count <= 0) return 0;
   return ptg::batch_workspace_bytes(count);
 }
 
-static ptg_status validate_problem(const char* fn, int32_t p, const ptg_problem& q, ptg_epilogue epi) {
+}  // extern "C"
+
+namespace {
+
+ptg_status validate_problem(const char* fn, int32_t p, const ptg_problem& q, ptg_dtype c_dtype, ptg_epilogue epi) {
   if (q.M < 0 || q.N < 0 || q.K < 0) return fail(PTG_ERR_INVALID_ARG, "%s: problem %d: negative size", fn, p);
   if (q.K == 0) return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: K = 0", fn, p);
   if (q.K % 8 || q.N % 8) return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: N and K must be multiples of 8", fn, p);
@@ -272,40 +303,110 @@ static ptg_status validate_problem(const char* fn, int32_t p, const ptg_problem&
   if (q.lda % 8 || q.ldb % 8 || q.ldc % 8) return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: leading dimensions must be multiples of 8", fn, p);
   if (!aligned16(q.A) || !aligned16(q.B) || !aligned16(q.C) || (q.bias && !aligned16(q.bias)))
     return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: pointers must be 16-byte aligned", fn, p);
-  if (!fits31(256, q.lda, q.K) || !fits31(q.K, q.ldb, 256))
-    return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: operand tile exceeds 2 GiB of addressing", fn, p);
+  if (!fits31(256, q.lda, q.K) || !fits31(q.K, q.ldb, 256) || !out_fits(q.ldc, c_dtype == PTG_F32 ? 4 : 2))
+    return fail(PTG_ERR_UNSUPPORTED, "%s: problem %d: operand or output tile exceeds 2 GiB of addressing", fn, p);
   return PTG_OK;
 }
 
-ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, ptg_epilogue epi,
-                                  void* workspace, size_t ws_bytes, void* stream) {
+// Pinned host buffers that stage a problem table on its way to the device, per device.  A
+// buffer is handed out again once the copy that read it has completed (its event), so a
+// call returns as soon as the copy is enqueued and the caller's array may be freed at once.
+struct StagingBuffer {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;   // recorded on the stream after the copy
+};
+struct StagingPool {
+  std::mutex mu;
+  std::vector<StagingBuffer> bufs;
+  size_t next = 0;             // the buffer waited for when all are in flight (round robin)
+};
+constexpr size_t kStagingBuffers = 8;
+
+StagingPool& staging_pool(int dev) {
+  static std::mutex mu;
+  static std::vector<std::unique_ptr<StagingPool>> pools;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)pools.size() <= dev) pools.resize(dev + 1);
+  if (!pools[dev]) pools[dev].reset(new StagingPool);
+  return *pools[dev];
+}
+
+// Copies `bytes` from `fill` (a function writing the table into a host buffer) to the device
+// pointer `dst` on `stream` through a pinned staging buffer.
+template <class Fill>
+hipError_t staged_copy(void* dst, size_t bytes, hipStream_t stream, Fill fill) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  StagingPool& pool = staging_pool(dev);
+  std::lock_guard<std::mutex> lock(pool.mu);
+  StagingBuffer* b = nullptr;
+  for (StagingBuffer& c : pool.bufs) {
+    if (c.cap >= bytes && hipEventQuery(c.done) == hipSuccess) {
+      b = &c;
+      break;
+    }
+  }
+  if (!b && pool.bufs.size() < kStagingBuffers) {
+    pool.bufs.emplace_back();
+    b = &pool.bufs.back();
+    e = hipEventCreateWithFlags(&b->done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      pool.bufs.pop_back();
+      return e;
+    }
+  }
+  if (!b) {
+    // every buffer is in flight (or too small): wait for the oldest one handed out
+    b = &pool.bufs[pool.next % pool.bufs.size()];
+    pool.next++;
+    e = hipEventSynchronize(b->done);
+    if (e != hipSuccess) return e;
+  }
+  if (b->cap < bytes) {
+    if (b->host) {
+      e = hipEventSynchronize(b->done);
+      if (e != hipSuccess) return e;
+      (void)hipHostFree(b->host);
+      b->host = nullptr;
+      b->cap = 0;
+    }
+    const size_t cap = std::max<size_t>(bytes, 64 << 10);
+    e = hipHostMalloc(&b->host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      b->host = nullptr;
+      return e;
+    }
+    b->cap = cap;
+  }
+  fill(static_cast<char*>(b->host));
+  e = hipMemcpyAsync(dst, b->host, bytes, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipEventRecord(b->done, stream);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+ptg_status ptg_grouped_gemm_ptr_array_prepare(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype,
+                                              ptg_epilogue epi, void* workspace, size_t ws_bytes, void* stream) {
   PTG_TRY({
-    const char* fn = "ptg_gemm_batch_prepare";
+    const char* fn = "ptg_grouped_gemm_ptr_array_prepare";
     if (count <= 0 || !problems) return fail(PTG_ERR_INVALID_ARG, "%s: count must be positive and problems non-null", fn);
     if (count > ptg::kMaxBatch) return fail(PTG_ERR_UNSUPPORTED, "%s: count exceeds %d", fn, ptg::kMaxBatch);
+    if (c_dtype != PTG_BF16 && c_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
     if (!valid_epi(epi)) return fail(PTG_ERR_UNSUPPORTED, "%s: bad epilogue", fn);
     const size_t need = ptg::batch_workspace_bytes(count);
     if (!workspace || ws_bytes < need)
       return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
-    std::vector<char> host(need, 0);
-    auto* hdr = reinterpret_cast<ptg::BatchHeader*>(host.data());
-    auto* pre = reinterpret_cast<int32_t*>(host.data() + sizeof(ptg::BatchHeader));
-    auto* rec = reinterpret_cast<ptg::BatchProblem*>(host.data() + sizeof(ptg::BatchHeader) +
-                                                     ptg::batch_prefix_bytes(count));
-    int64_t total = 0;
-    ptg::Guards& gu = hdr->guard;
-    gu.a_lo = gu.b_lo = gu.c_lo = gu.bias_lo = UINT64_MAX;
-    gu.a_hi = gu.b_hi = gu.c_hi = gu.bias_hi = 0;
-    auto widen = [](uint64_t& lo, uint64_t& hi, const void* p, uint64_t bytes) {
-      const uint64_t a = reinterpret_cast<uint64_t>(p);
-      if (a < lo) lo = a;
-      if (a + bytes > hi) hi = a + bytes;
-    };
     for (int32_t p = 0; p < count; ++p) {
-      ptg_status st = validate_problem(fn, p, problems[p], epi);
+      ptg_status st = validate_problem(fn, p, problems[p], c_dtype, epi);
       if (st) return st;
     }
+    const int64_t osz = c_dtype == PTG_F32 ? 4 : 2;
     // Table order = tile order of the launch, whose workgroups take tiles round-robin: the
     // problems with the most k-steps per tile go first (stable, so equal costs keep the
     // caller's order), and the cheapest tiles are the last round's, which then ends evenly.
@@ -315,48 +416,67 @@ ptg_status ptg_gemm_batch_prepare(int32_t count, const ptg_problem* problems, pt
     std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
       return (problems[x].K + 63) / 64 > (problems[y].K + 63) / 64;
     });
+    int64_t total = 0;
     for (int32_t p = 0; p < count; ++p) {
-      const ptg_problem& q = problems[order[p]];
-      ptg::BatchProblem& r = rec[p];
-      r.A = q.A; r.B = q.B; r.C = q.C; r.bias = needs_bias(epi) ? q.bias : nullptr;
-      r.lda = q.lda; r.ldb = q.ldb; r.ldc = q.ldc;
-      r.M = (int32_t)q.M; r.N = (int32_t)q.N; r.K = (int32_t)q.K;
-      const bool empty = q.M == 0 || q.N == 0;
-      r.tiles_m = empty ? 0 : (int32_t)((q.M + ptg::kBatchBM - 1) / ptg::kBatchBM);
-      r.tiles_n = empty ? 0 : (int32_t)((q.N + ptg::kBatchBN - 1) / ptg::kBatchBN);
-      if (!empty) {
-        widen(gu.a_lo, gu.a_hi, q.A, (uint64_t)(((q.M - 1) * q.lda + q.K) * 2));
-        widen(gu.b_lo, gu.b_hi, q.B, (uint64_t)(((q.K - 1) * q.ldb + q.N) * 2));
-        widen(gu.c_lo, gu.c_hi, q.C, (uint64_t)(((q.M - 1) * q.ldc + q.N) * 4));
-        if (r.bias) widen(gu.bias_lo, gu.bias_hi, r.bias, (uint64_t)q.N * 4);
-      }
-      pre[p] = (int32_t)total;
-      total += (int64_t)r.tiles_m * r.tiles_n;
-      if (total >= ((int64_t)1 << 31)) return fail(PTG_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+      const ptg_problem& q = problems[p];
+      if (q.M > 0 && q.N > 0) total += ((q.M + ptg::kBatchBM - 1) / ptg::kBatchBM) * ((q.N + ptg::kBatchBN - 1) / ptg::kBatchBN);
     }
-    pre[count] = (int32_t)total;
-    if (gu.a_lo > gu.a_hi) gu.a_lo = gu.a_hi = 0;
-    if (gu.b_lo > gu.b_hi) gu.b_lo = gu.b_hi = 0;
-    if (gu.c_lo > gu.c_hi) gu.c_lo = gu.c_hi = 0;
-    if (gu.bias_lo > gu.bias_hi) gu.bias_lo = gu.bias_hi = 0;
-    hdr->magic = ptg::kBatchMagic;
-    hdr->count = count;
-    hdr->total_tiles = (int32_t)total;
-    hdr->bm = ptg::kBatchBM;
-    hdr->bn = ptg::kBatchBN;
-    hdr->epi = epi;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (total >= ((int64_t)1 << 31)) return fail(PTG_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    auto fill = [&](char* host) {
+      std::memset(host, 0, need);
+      auto* hdr = reinterpret_cast<ptg::BatchHeader*>(host);
+      auto* pre = reinterpret_cast<int32_t*>(host + sizeof(ptg::BatchHeader));
+      auto* rec = reinterpret_cast<ptg::BatchProblem*>(host + sizeof(ptg::BatchHeader) + ptg::batch_prefix_bytes(count));
+      ptg::Guards& gu = hdr->guard;
+      gu.a_lo = gu.b_lo = gu.c_lo = gu.bias_lo = UINT64_MAX;
+      gu.a_hi = gu.b_hi = gu.c_hi = gu.bias_hi = 0;
+      auto widen = [](uint64_t& lo, uint64_t& hi, const void* ptr, uint64_t bytes) {
+        const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+        if (a < lo) lo = a;
+        if (a + bytes > hi) hi = a + bytes;
+      };
+      int64_t run = 0;
+      for (int32_t p = 0; p < count; ++p) {
+        const ptg_problem& q = problems[order[p]];
+        ptg::BatchProblem& r = rec[p];
+        r.A = q.A; r.B = q.B; r.C = q.C; r.bias = needs_bias(epi) ? q.bias : nullptr;
+        r.lda = q.lda; r.ldb = q.ldb; r.ldc = q.ldc;
+        r.M = (int32_t)q.M; r.N = (int32_t)q.N; r.K = (int32_t)q.K;
+        const bool empty = q.M == 0 || q.N == 0;
+        r.tiles_m = empty ? 0 : (int32_t)((q.M + ptg::kBatchBM - 1) / ptg::kBatchBM);
+        r.tiles_n = empty ? 0 : (int32_t)((q.N + ptg::kBatchBN - 1) / ptg::kBatchBN);
+        if (!empty) {
+          widen(gu.a_lo, gu.a_hi, q.A, (uint64_t)(((q.M - 1) * q.lda + q.K) * 2));
+          widen(gu.b_lo, gu.b_hi, q.B, (uint64_t)(((q.K - 1) * q.ldb + q.N) * 2));
+          widen(gu.c_lo, gu.c_hi, q.C, (uint64_t)(((q.M - 1) * q.ldc + q.N) * osz));
+          if (r.bias) widen(gu.bias_lo, gu.bias_hi, r.bias, (uint64_t)q.N * 4);
+        }
+        pre[p] = (int32_t)run;
+        run += (int64_t)r.tiles_m * r.tiles_n;
+      }
+      pre[count] = (int32_t)run;
+      if (gu.a_lo > gu.a_hi) gu.a_lo = gu.a_hi = 0;
+      if (gu.b_lo > gu.b_hi) gu.b_lo = gu.b_hi = 0;
+      if (gu.c_lo > gu.c_hi) gu.c_lo = gu.c_hi = 0;
+      if (gu.bias_lo > gu.bias_hi) gu.bias_lo = gu.bias_hi = 0;
+      hdr->magic = ptg::kBatchMagic;
+      hdr->count = count;
+      hdr->total_tiles = (int32_t)run;
+      hdr->bm = ptg::kBatchBM;
+      hdr->bn = ptg::kBatchBN;
+      hdr->epi = epi;
+      hdr->out_f32 = c_dtype == PTG_F32;
+    };
+    hipError_t e = staged_copy(workspace, need, reinterpret_cast<hipStream_t>(stream), fill);
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
   })
 }
 
-ptg_status ptg_gemm_batch_run(int32_t count, const void* workspace, size_t ws_bytes, ptg_dtype c_dtype,
-                              ptg_epilogue epi, void* stream) {
+ptg_status ptg_grouped_gemm_ptr_array_run(int32_t count, const void* workspace, size_t ws_bytes, ptg_dtype c_dtype,
+                                          ptg_epilogue epi, void* stream) {
   PTG_TRY({
-    const char* fn = "ptg_gemm_batch_run";
+    const char* fn = "ptg_grouped_gemm_ptr_array_run";
     if (count <= 0) return fail(PTG_ERR_INVALID_ARG, "%s: count must be positive", fn);
     if (count > ptg::kMaxBatch) return fail(PTG_ERR_UNSUPPORTED, "%s: count exceeds %d", fn, ptg::kMaxBatch);
     if (c_dtype != PTG_BF16 && c_dtype != PTG_F32) return fail(PTG_ERR_UNSUPPORTED, "%s: bad output dtype", fn);
@@ -364,6 +484,7 @@ ptg_status ptg_gemm_batch_run(int32_t count, const void* workspace, size_t ws_by
     const size_t need = ptg::batch_workspace_bytes(count);
     if (!workspace || ws_bytes < need)
       return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
     ptg::BatchLaunch b{};
     b.workspace = workspace; b.count = count; b.epi = epi; b.out_f32 = c_dtype == PTG_F32;
     hipError_t e = ptg::launch_batch(b, reinterpret_cast<hipStream_t>(stream));
@@ -372,11 +493,11 @@ ptg_status ptg_gemm_batch_run(int32_t count, const void* workspace, size_t ws_by
   })
 }
 
-ptg_status ptg_gemm_batch(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype, ptg_epilogue epi,
-                          void* workspace, size_t ws_bytes, void* stream) {
-  ptg_status st = ptg_gemm_batch_prepare(count, problems, epi, workspace, ws_bytes, stream);
+ptg_status ptg_grouped_gemm_ptr_array(int32_t count, const ptg_problem* problems, ptg_dtype c_dtype,
+                                      ptg_epilogue epi, void* workspace, size_t ws_bytes, void* stream) {
+  ptg_status st = ptg_grouped_gemm_ptr_array_prepare(count, problems, c_dtype, epi, workspace, ws_bytes, stream);
   if (st) return st;
-  return ptg_gemm_batch_run(count, workspace, ws_bytes, c_dtype, epi, stream);
+  return ptg_grouped_gemm_ptr_array_run(count, workspace, ws_bytes, c_dtype, epi, stream);
 }
 
 size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N) {
@@ -412,8 +533,11 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
       return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (indices 4-byte)", fn);
     const int64_t Kt = Ku + Kc;
     const bool kn = w_layout == PTG_B_KN;
-    if (!fits31(256, Ku, Ku) || !fits31(256, Kc, Kc) || !(kn ? fits31(Kt, N, 256) : fits31(256, Kt, Kt)))
-      return fail(PTG_ERR_UNSUPPORTED, "%s: operand tile exceeds 2 GiB of addressing", fn);
+    if (!fits31(256, Ku, Ku) || !fits31(256, Kc, Kc) || !(kn ? fits31(Kt, N, 256) : fits31(256, Kt, Kt)) ||
+        !out_fits(N, y_dtype == PTG_F32 ? 4 : 2))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: operand or output tile exceeds 2 GiB of addressing", fn);
+    if (U * N * 4 >= ((int64_t)1 << 31))
+      return fail(PTG_ERR_UNSUPPORTED, "%s: P (U x N fp32) exceeds 2 GiB of addressing", fn);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* P = reinterpret_cast<float*>(workspace);
     // Matmul decomposition: the user half of W meets each user's features once ...

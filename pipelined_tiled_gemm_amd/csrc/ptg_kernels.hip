@@ -446,6 +446,7 @@ __global__ void arm_queue_kernel(uint32_t* queue) {
 // ---------------------------------------------------------------------------------------
 struct BatchSched {
   struct Args {
+    const BatchHeader* hdr;       // table header (workspace)
     const int32_t* prefix;        // [count + 1] tile prefix (workspace)
     const BatchProblem* probs;    // [count]
     int32_t count;
@@ -456,10 +457,22 @@ struct BatchSched {
   static constexpr int LDS_BYTES = (kMaxBatch + 1) * 4 + 16;
   static constexpr bool kDynamic = false;
 
+  // The launch runs only the table it was asked for: a header whose magic, count, epilogue
+  // or output type differs from the launch's arguments (a table written for another call)
+  // gives a prefix with no tiles, so the workgroups publish the end marker at once and touch
+  // no operand; watchdog bit 2 records it.
   template <class C>
   __device__ static void init(const Args& a, char* lds) {
     int32_t* pre = reinterpret_cast<int32_t*>(lds);
-    for (int i = threadIdx.x; i <= a.count; i += C::NT) pre[i] = a.prefix[i];
+    const BatchHeader& h = *a.hdr;
+    const bool ok = h.magic == kBatchMagic && h.count == a.count && h.epi == a.epi &&
+                    h.out_f32 == a.out_f32 && h.bm == C::BM && h.bn == C::BN;
+    if (ok) {
+      for (int i = threadIdx.x; i <= a.count; i += C::NT) pre[i] = a.prefix[i];
+    } else {
+      for (int i = threadIdx.x; i <= a.count; i += C::NT) pre[i] = 0;
+      if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(&g_watchdog, 2u);
+    }
   }
 
   // The problem record is read with scalar loads (constant address space, wave-uniform index):
@@ -747,6 +760,7 @@ hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream) {
   static_assert(C::BM == kBatchBM && C::BN == kBatchBN, "batch prefix tile shape");
   const char* ws = reinterpret_cast<const char*>(b.workspace);
   BatchSched::Args a;
+  a.hdr = reinterpret_cast<const BatchHeader*>(ws);
   a.prefix = reinterpret_cast<const int32_t*>(ws + sizeof(BatchHeader));
   a.probs = reinterpret_cast<const BatchProblem*>(ws + sizeof(BatchHeader) + batch_prefix_bytes(b.count));
   a.count = b.count;
@@ -761,50 +775,97 @@ hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream) {
 // ---------------------------------------------------------------------------------------
 // Validation kernels for device-resident preconditions
 // ---------------------------------------------------------------------------------------
-// Flag word of the check kernels (one per device, no allocation).
-__device__ int32_t g_check_flag = 0;
+// Result words of the check kernels (one per check in flight; no allocation).  A check claims
+// a free word under a lock and releases it after its stream has been synchronised.
+__device__ int32_t g_check_words[kCheckWords];
 
-__global__ void check_offsets_kernel(const int32_t* off, int32_t G, int64_t M_total) {
+namespace {
+std::mutex g_check_mu;
+bool g_check_busy[kCheckWords];
+std::vector<int32_t*> g_check_base;  // per device: device address of g_check_words
+}  // namespace
+
+__global__ void clear_word_kernel(int32_t* w) {
+  if (threadIdx.x == 0) *w = 0;
+}
+
+__global__ void check_offsets_kernel(const int32_t* off, int32_t G, int64_t M_total, int32_t* flag) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i > G) return;
   bool bad = false;
   if (i == 0 && off[0] != 0) bad = true;
   if (i == G && (int64_t)off[G] != M_total) bad = true;
   if (i < G && off[i + 1] < off[i]) bad = true;
-  if (bad) atomicOr(&g_check_flag, 1);
+  if (bad) atomicOr(flag, 1);
 }
 
-__global__ void check_index_kernel(const int32_t* idx, int64_t n, int64_t U) {
+__global__ void check_index_kernel(const int32_t* idx, int64_t n, int64_t U, int32_t* flag) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int32_t v = idx[i];
-  if (v < 0 || (int64_t)v >= U) atomicOr(&g_check_flag, 1);
+  if (v < 0 || (int64_t)v >= U) atomicOr(flag, 1);
 }
 
 template <class Launch>
-static hipError_t run_check(hipStream_t stream, int* bad, Launch launch) {
+static hipError_t run_check(hipStream_t stream, int* bad, int* busy, Launch launch) {
+  *bad = 0;
+  *busy = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int slot = -1;
+  int32_t* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_check_mu);
+    if ((int)g_check_base.size() <= dev) g_check_base.resize(dev + 1, nullptr);
+    if (!g_check_base[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_check_words));
+      if (e != hipSuccess) return e;
+      g_check_base[dev] = static_cast<int32_t*>(p);
+    }
+    base = g_check_base[dev];
+    for (int i = 0; i < kCheckWords; ++i) {
+      if (!g_check_busy[i]) {
+        g_check_busy[i] = true;
+        slot = i;
+        break;
+      }
+    }
+  }
+  if (slot < 0) {
+    *busy = 1;
+    return hipSuccess;
+  }
+  int32_t* flag = base + slot;
   int32_t h = 0;
-  hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_check_flag), &h, sizeof h, 0, hipMemcpyHostToDevice, stream);
-  if (e == hipSuccess) e = launch();
-  if (e == hipSuccess) e = hipMemcpyFromSymbolAsync(&h, HIP_SYMBOL(g_check_flag), sizeof h, 0, hipMemcpyDeviceToHost, stream);
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, flag);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = launch(flag);
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, flag, sizeof h, hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   *bad = (e == hipSuccess && h != 0) ? 1 : 0;
+  {
+    std::lock_guard<std::mutex> lock(g_check_mu);
+    g_check_busy[slot] = false;
+  }
   return e;
 }
 
-hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hipStream_t stream, int* bad) {
-  return run_check(stream, bad, [&]() {
+hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hipStream_t stream, int* bad,
+                         int* busy) {
+  return run_check(stream, bad, busy, [&](int32_t* flag) {
     const int64_t n = (int64_t)G + 1;
     hipLaunchKernelGGL(check_offsets_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       offsets, G, M_total);
+                       offsets, G, M_total, flag);
     return hipGetLastError();
   });
 }
 
-hipError_t check_index(const int32_t* idx, int64_t n, int64_t U, hipStream_t stream, int* bad) {
-  return run_check(stream, bad, [&]() {
+hipError_t check_index(const int32_t* idx, int64_t n, int64_t U, hipStream_t stream, int* bad, int* busy) {
+  return run_check(stream, bad, busy, [&](int32_t* flag) {
     hipLaunchKernelGGL(check_index_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       idx, n, U);
+                       idx, n, U, flag);
     return hipGetLastError();
   });
 }

@@ -78,7 +78,8 @@ struct BatchHeader {
   int32_t total_tiles;
   int32_t bm, bn;
   int32_t epi;
-  int32_t reserved0[2];
+  int32_t out_f32;              // output element type the table was written for (C ranges)
+  int32_t reserved0;
   Guards guard;                 // union of the problems' operand ranges
   int32_t reserved[32];
 };
@@ -95,7 +96,7 @@ inline size_t batch_workspace_bytes(int32_t count) {
 struct BatchLaunch {
   const void* workspace;
   int32_t count;
-  int epi, out_f32;
+  int epi, out_f32;             // compared with the table header on the device
 };
 
 // Limits enforced by the ABI layer.
@@ -130,10 +131,15 @@ struct AttentionLaunch {
 };
 hipError_t launch_attention(const AttentionLaunch& p, hipStream_t stream);
 // Validation of device-resident preconditions: runs a check kernel on `stream`, waits for
-// it, and sets *bad to 1 if the data violates the precondition (0 otherwise).
+// it, and sets *bad to 1 if the data violates the precondition (0 otherwise).  Each check
+// takes a result word of its own from a small device array (claimed under a lock, released
+// after the wait), so checks on several streams or threads do not share one; *busy is set
+// when every word is in use (nothing then runs).
+constexpr int kCheckWords = 256;
 hipError_t check_offsets(const int32_t* offsets, int32_t G, int64_t M_total, hipStream_t stream,
-                         int* bad);
-hipError_t check_index(const int32_t* idx, int64_t n, int64_t U, hipStream_t stream, int* bad);
+                         int* bad, int* busy);
+hipError_t check_index(const int32_t* idx, int64_t n, int64_t U, hipStream_t stream, int* bad,
+                       int* busy);
 // The dense path's tile configuration for a problem: BM, BN, BK, stages, consumers, producers.
 void dense_config(int64_t M, int64_t N, int64_t K, int b_kn, int32_t cfg[6]);
 // Watchdog words of the bounded waits (nonzero if a wait ever gave up): the GEMM kernels'

@@ -91,29 +91,83 @@ def test_grouped_validation(L):
     assert g(M=0, X=None, W=None, Y=None, off=None) == OK
 
 
-def test_batch_validation(L):
-    n = 3
-    need = L.ptg_gemm_batch_workspace(n)
-    assert need >= 256 + 16 + n * 80
+def _problems(n, dtype_rows=64):
     arr = (_ffi.ProblemStruct * n)()
     for i in range(n):
         s = arr[i]
         s.M, s.N, s.K = 64, 64, 64
         s.A = s.B = s.C = P
         s.lda = s.ldb = s.ldc = 64
-    assert L.ptg_gemm_batch_prepare(0, arr, 0, P, need, None) == INVALID
-    assert L.ptg_gemm_batch_prepare(n, arr, 0, P, need - 1, None) == WORKSPACE
-    assert L.ptg_gemm_batch_prepare(n, arr, 0, None, need, None) == WORKSPACE
+    return arr
+
+
+def test_ptr_array_validation(L):
+    n = 3
+    need = L.ptg_grouped_gemm_ptr_array_workspace(n)
+    assert need >= 256 + 16 + n * 80
+    assert L.ptg_grouped_gemm_ptr_array_workspace(0) == 0
+    arr = _problems(n)
+    for fn in (L.ptg_grouped_gemm_ptr_array_prepare, L.ptg_grouped_gemm_ptr_array):
+        assert fn(0, arr, 0, 0, P, need, None) == INVALID
+        assert fn(n, None, 0, 0, P, need, None) == INVALID
+        assert fn(2049, arr, 0, 0, P, 1 << 30, None) == UNSUPPORTED
+        assert fn(n, arr, 0, 0, P, need - 1, None) == WORKSPACE
+        assert fn(n, arr, 0, 0, None, need, None) == WORKSPACE
+        assert fn(n, arr, 0, 0, P + 8, need, None) == UNSUPPORTED
+        assert fn(n, arr, 5, 0, P, need, None) == UNSUPPORTED       # bad output dtype
+        assert fn(n, arr, 0, 4, P, need, None) == UNSUPPORTED       # bad epilogue
+        arr[1].K = 12
+        assert fn(n, arr, 0, 0, P, need, None) == UNSUPPORTED
+        assert "problem 1" in L.ptg_last_error().decode()
+        arr[1].K = 64
+        arr[2].lda = 8
+        assert fn(n, arr, 0, 0, P, need, None) == INVALID
+        arr[2].lda = 64
+        assert fn(n, arr, 0, 1, P, need, None) == INVALID           # bias missing
+    assert L.ptg_grouped_gemm_ptr_array_run(n, P, need - 1, 0, 0, None) == WORKSPACE
+    assert L.ptg_grouped_gemm_ptr_array_run(n, P, need, 5, 0, None) == UNSUPPORTED
+    assert L.ptg_grouped_gemm_ptr_array_run(n, P, need, 0, 9, None) == UNSUPPORTED
+    assert L.ptg_grouped_gemm_ptr_array_run(0, P, need, 0, 0, None) == INVALID
+    assert L.ptg_grouped_gemm_ptr_array_run(2049, P, 1 << 30, 0, 0, None) == UNSUPPORTED
+
+
+def test_ptr_array_output_extent(L):
+    """An output row stride whose 256-row tile needs 2^31 bytes or more is refused; the limit
+    depends on the output element size (fp32 rows are twice as wide)."""
+    n = 2
+    need = L.ptg_grouped_gemm_ptr_array_workspace(n)
+    arr = _problems(n)
+    # bf16: (255 * ldc + 256) * 2 < 2^31  <=>  ldc <= 4210751 (as a multiple of 8: 4210744).  At the limit
+    # problem 0 passes, and the call stops at problem 1, made invalid so that nothing runs.
     arr[1].K = 12
-    assert L.ptg_gemm_batch_prepare(n, arr, 0, P, need, None) == UNSUPPORTED
+    arr[0].ldc = 4210744
+    assert L.ptg_grouped_gemm_ptr_array_prepare(n, arr, 0, 0, P, need, None) == UNSUPPORTED
+    assert "problem 1" in L.ptg_last_error().decode()
+    arr[0].ldc = 4210752
+    assert L.ptg_grouped_gemm_ptr_array_prepare(n, arr, 0, 0, P, need, None) == UNSUPPORTED
+    assert "problem 0" in L.ptg_last_error().decode()
     arr[1].K = 64
-    arr[2].lda = 8
-    assert L.ptg_gemm_batch_prepare(n, arr, 0, P, need, None) == INVALID
-    arr[2].lda = 64
-    assert L.ptg_gemm_batch_prepare(n, arr, 1, P, need, None) == INVALID   # bias missing
-    assert L.ptg_gemm_batch_run(n, P, need - 1, 0, 0, None) == WORKSPACE
-    assert L.ptg_gemm_batch_run(n, P, need, 5, 0, None) == UNSUPPORTED
-    assert L.ptg_gemm_batch_run(2049, P, 1 << 30, 0, 0, None) == UNSUPPORTED
+    assert L.ptg_grouped_gemm_ptr_array_prepare(n, arr, 0, 0, P, need, None) == UNSUPPORTED
+    arr[0].ldc = 2105376                                           # fp32: at most 2105368
+    assert L.ptg_grouped_gemm_ptr_array_prepare(n, arr, 1, 0, P, need, None) == UNSUPPORTED
+    arr[0].ldc = 1 << 31                                           # 32-bit ldc
+    assert L.ptg_grouped_gemm_ptr_array_prepare(n, arr, 0, 0, P, need, None) == UNSUPPORTED
+
+
+def test_gemm_output_extent(L):
+    # the output tile bound of ptg_gemm, per element size
+    assert gemm(L, N=64, ldc=4210752) == UNSUPPORTED
+    assert gemm(L, N=64, ldc=2105376, dtype=1) == UNSUPPORTED
+    assert gemm(L, N=64, ldc=1 << 31) == UNSUPPORTED
+
+
+def test_grouped_output_extent(L):
+    def g(N, dtype):
+        return L.ptg_grouped_gemm(4, 64, N, 64, P, P, 0, P, P, dtype, None, 0, None)
+    # Y is dense (ld = N): the output tile bound caps N; W's K x N tile is checked too, so the
+    # output check is what fails for the fp32 output at an N that passes for bf16 W
+    assert g(2105376, 1) == UNSUPPORTED
+    assert "output" in L.ptg_last_error().decode()
 
 
 def test_broadcast_validation(L):
@@ -135,6 +189,10 @@ def test_broadcast_validation(L):
     assert b(wsb=need - 4) == WORKSPACE
     assert b(ws=None) == WORKSPACE
     assert b(Mc=0, Xu=None, Xc=None, idx=None, W=None, Y=None, ws=None, wsb=0) == OK
+    # P (U x N fp32) is addressed with 31-bit offsets: U * N * 4 >= 2^31 is refused
+    bigU, bigN = 1 << 17, 4096
+    assert b(U=bigU, N=bigN, wsb=1 << 62) == UNSUPPORTED
+    assert "P (U x N fp32)" in L.ptg_last_error().decode()
 
 
 def test_wgrad_validation(L):

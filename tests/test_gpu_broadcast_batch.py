@@ -1,4 +1,5 @@
-"""GPU parity of the in-kernel broadcast GEMM and of the batched (pointer-array) GEMM."""
+"""GPU parity of the in-kernel broadcast GEMM and of the pointer-array grouped GEMM (a batch of
+independent problems in one launch)."""
 import numpy as np
 import pytest
 import torch
@@ -138,7 +139,7 @@ def run_batch(pl: wl.ProblemList, out_dtype, rows_per=None):
         C = torch.empty((p.M, p.N), dtype=out_dtype, device="cuda")
         probs.append((dev_bf16(p.A), dev_bf16(p.B), C, dev(p.bias)))
         outs.append(C)
-    ptg.gemm_batch(probs, pl.epi)
+    ptg.grouped_gemm_ptr_array(probs, pl.epi)
     vs = oracle.problem_list(pl.problems, pl.epi, rows_per)
     return outs, vs
 
@@ -160,13 +161,13 @@ def test_batch_prepare_once_run_twice():
         C = torch.empty((p.M, p.N), dtype=torch.float32, device="cuda")
         probs.append((dev_bf16(p.A), dev_bf16(p.B), C, dev(p.bias)))
         outs.append(C)
-    ws = torch.empty(ptg.gemm_batch_workspace(len(probs)), dtype=torch.uint8, device="cuda")
-    ptg.gemm_batch_prepare(probs, pl.epi, ws)
-    ptg.gemm_batch_run(len(probs), ws, torch.float32, pl.epi)
+    ws = torch.empty(ptg.grouped_gemm_ptr_array_workspace(len(probs)), dtype=torch.uint8, device="cuda")
+    ptg.grouped_gemm_ptr_array_prepare(probs, pl.epi, ws)
+    ptg.grouped_gemm_ptr_array_run(len(probs), ws, torch.float32, pl.epi)
     first = [o.clone() for o in outs]
     for o in outs:
         o.zero_()
-    ptg.gemm_batch_run(len(probs), ws, torch.float32, pl.epi)
+    ptg.grouped_gemm_ptr_array_run(len(probs), ws, torch.float32, pl.epi)
     for a, b in zip(first, outs):
         assert torch.equal(a, b)
     vs = oracle.problem_list(pl.problems, pl.epi)
@@ -180,7 +181,7 @@ def test_batch_each_equals_standalone_gemm():
     for p in pl.problems:
         probs.append((dev_bf16(p.A), dev_bf16(p.B), torch.empty((p.M, p.N), dtype=torch.float32,
                       device="cuda"), dev(p.bias)))
-    ptg.gemm_batch(probs, pl.epi)
+    ptg.grouped_gemm_ptr_array(probs, pl.epi)
     for A, B, C, bias in probs:
         one = ptg.gemm(A, B, out_dtype=torch.float32, bias=bias, epi=pl.epi)
         assert torch.allclose(C, one, rtol=0, atol=0) or torch.equal(C, one)
@@ -198,6 +199,97 @@ def test_config5_recsys_batch_sampled():
             C = torch.empty((p.M, p.N), dtype=out_dtype, device="cuda")
             probs.append((dev_bf16(p.A), dev_bf16(p.B), C, dev(p.bias)))
             outs.append(C)
-        ptg.gemm_batch(probs, pl.epi)
+        ptg.grouped_gemm_ptr_array(probs, pl.epi)
         for i, (o, v) in enumerate(zip(outs, vs)):
             check(o[torch.from_numpy(rows_per[i]).cuda()], v, pl.problems[i].K, f"config5 problem {i}")
+
+
+def _small_batch(seed, n, out_dtype=torch.float32, epi=wl.EPI_BIAS_SILU):
+    pl = wl.problem_list(seed, n, mmin=1, mmax=300, nk_choices=(8, 136, 256), epi=epi)
+    probs, outs = [], []
+    for p in pl.problems:
+        C = torch.full((p.M, p.N), float("nan"), dtype=out_dtype, device="cuda")
+        probs.append((dev_bf16(p.A), dev_bf16(p.B), C, dev(p.bias)))
+        outs.append(C)
+    return pl, probs, outs
+
+
+def test_ptr_array_caller_array_reused_at_once():
+    """The host problem array may be overwritten as soon as the call returns: the table was
+    staged before the call returned, and the launch reads the staged copy."""
+    import ctypes
+    from pipelined_tiled_gemm_amd import _ffi
+    pl, probs, outs = _small_batch(61, 7)
+    arr, _ = ptg._problem_array(probs, pl.epi)
+    ws = torch.empty(ptg.grouped_gemm_ptr_array_workspace(len(probs)), dtype=torch.uint8, device="cuda")
+    L = _ffi.load()
+    st = L.ptg_grouped_gemm_ptr_array(len(probs), arr, 1, pl.epi, ws.data_ptr(), ws.numel(),
+                                      torch.cuda.current_stream().cuda_stream)
+    assert st == 0, ptg.last_error()
+    ctypes.memset(arr, 0xFF, ctypes.sizeof(arr))      # garbage, before the stream has run
+    torch.cuda.synchronize()
+    vs = oracle.problem_list(pl.problems, pl.epi)
+    for i, (o, v) in enumerate(zip(outs, vs)):
+        check(o, v, pl.problems[i].K, f"problem {i}")
+
+
+def test_ptr_array_many_calls_in_flight():
+    """More back-to-back calls than the library keeps staging buffers (8), each with its own
+    workspace, without a synchronisation between them: every call's table stays intact."""
+    batches = [_small_batch(70 + k, 3 + k % 4) for k in range(20)]
+    for pl, probs, _ in batches:
+        ptg.grouped_gemm_ptr_array(probs, pl.epi)
+    torch.cuda.synchronize()
+    for k, (pl, probs, outs) in enumerate(batches):
+        vs = oracle.problem_list(pl.problems, pl.epi)
+        for i, (o, v) in enumerate(zip(outs, vs)):
+            check(o, v, pl.problems[i].K, f"batch {k} problem {i}")
+
+
+@pytest.mark.parametrize("change", ["epi", "dtype", "count"])
+def test_ptr_array_run_with_another_table_is_refused_on_device(change):
+    """A run whose epilogue, output type or count differs from what its table was written for
+    writes nothing (the outputs keep their NaN fill) and sets watchdog bit 2."""
+    pl, probs, outs = _small_batch(81, 5, epi=wl.EPI_NONE)
+    ws = torch.empty(ptg.grouped_gemm_ptr_array_workspace(len(probs) + 1), dtype=torch.uint8, device="cuda")
+    ptg.grouped_gemm_ptr_array_prepare(probs, wl.EPI_NONE, ws)
+    torch.cuda.synchronize()
+    epi = wl.EPI_SILU if change == "epi" else wl.EPI_NONE
+    dtype = torch.bfloat16 if change == "dtype" else torch.float32
+    count = len(probs) + 1 if change == "count" else len(probs)
+    ptg.grouped_gemm_ptr_array_run(count, ws, dtype, epi)
+    torch.cuda.synchronize()
+    assert ptg.watchdog(clear=True) == 2
+    for o in outs:
+        assert bool(torch.isnan(o).all()), "a refused launch wrote output"
+    # the same table with matching arguments runs
+    ptg.grouped_gemm_ptr_array_run(len(probs), ws, torch.float32, wl.EPI_NONE)
+    vs = oracle.problem_list(pl.problems, wl.EPI_NONE)
+    for i, (o, v) in enumerate(zip(outs, vs)):
+        check(o, v, pl.problems[i].K, f"problem {i}")
+
+
+def test_ptr_array_outputs_of_one_dtype():
+    pl, probs, outs = _small_batch(91, 3)
+    probs[1] = (probs[1][0], probs[1][1], probs[1][2].to(torch.bfloat16), probs[1][3])
+    with pytest.raises(TypeError):
+        ptg.grouped_gemm_ptr_array(probs, pl.epi)
+    probs[1] = (probs[1][0], probs[1][1], outs[1], probs[1][3][:-8])
+    with pytest.raises(ValueError):
+        ptg.grouped_gemm_ptr_array(probs, pl.epi)     # bias shorter than N
+
+
+def test_checks_concurrent_streams_and_watchdog():
+    """The device-data checks on two streams at once each see their own result, and a set
+    watchdog word makes a check fail."""
+    good = torch.tensor([0, 3, 3, 10], dtype=torch.int32, device="cuda")
+    bad = torch.tensor([0, 5, 3, 10], dtype=torch.int32, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(20):
+        ptg.grouped_gemm_check(good, 10, stream=s1)
+        with pytest.raises(ptg.PtgError):
+            ptg.grouped_gemm_check(bad, 10, stream=s2)
+    idx = torch.tensor([0, 1, 2, 1], dtype=torch.int32, device="cuda")
+    ptg.broadcast_gemm_check(3, idx, stream=s1)
+    with pytest.raises(ptg.PtgError):
+        ptg.broadcast_gemm_check(2, idx, stream=s2)
