@@ -7,6 +7,14 @@ accumulation error.  The tests allow 2^-8 max|V| per element for fp32 output; bf
 be within one bf16 step of the correctly rounded oracle value or within that same bound.
 Exact cases: zero keys (uniform weights 1.0) with integer values and a power-of-two context
 length give the mean of the values exactly; one overwhelming key returns its value row exactly.
+
+Norm check.  The weight errors are independent, at most 2^-9 relative each, so the error of
+an output row is about 2^-9 / sqrt(3) of sqrt(sum_j p_j^2 v_j^2) / l, which is also the size of
+the row itself when the values have random signs: the relative Frobenius error over a case is
+about 1.1e-3.  The tests require at most 2^-8 (fp32 output) and 2^-8 + 2^-9 (bf16 output, whose
+rounding adds at most 2^-9 relative).  A dropped, repeated or stale key block moves a row by
+about 1/L of a value, several percent of a typical row at L = 1024, and fails it, where the
+per-element bound alone would not notice.
 """
 import numpy as np
 import pytest
@@ -32,6 +40,13 @@ def bound(V):
     return 2.0 ** -8 * float(np.abs(wl.bf16_bits_to_f32(V)).max())
 
 
+def check_norm(got, v, limit, what):
+    nv = float(np.linalg.norm(v))
+    if nv > 0:
+        rel = float(np.linalg.norm(got - v)) / nv
+        assert rel <= limit, f"{what}: relative Frobenius error {rel:.3e} > {limit:.3e}"
+
+
 def check_attn(out, v, V, what):
     tol = bound(V)
     if out.dtype == torch.float32:
@@ -39,6 +54,7 @@ def check_attn(out, v, V, what):
         assert np.all(np.isfinite(got)), what
         err = float(np.abs(got - v).max())
         assert err <= tol, f"{what}: max error {err:.3e} > {tol:.3e}"
+        check_norm(got, v, 2.0 ** -8, what)
     else:
         got = host_bits(out).reshape(v.shape)
         ref = oracle.round_bf16(v)
@@ -47,6 +63,7 @@ def check_attn(out, v, V, what):
         near = np.abs(wl.bf16_bits_to_f32(got).astype(np.float64) - v) <= tol
         bad = ~((step <= 1) | near)
         assert not bad.any(), f"{what}: {int(bad.sum())} elements out of bound"
+        check_norm(wl.bf16_bits_to_f32(got).astype(np.float64), v, 2.0 ** -8 + 2.0 ** -9, what)
 
 
 def run(w, out_dtype, rows=None, guard=0):

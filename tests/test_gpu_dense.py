@@ -36,10 +36,6 @@ def run_dense(w: wl.Dense, out_dtype=torch.float32, epi=None, rows=None):
     return out, v
 
 
-@pytest.mark.skip(reason="kept off the GPU for now: this case faulted the GPU twice, and the one "
-                         "run that tested a guessed fix faulted again; the cause, a sign-extended "
-                         "buffer-descriptor base, was then shown on the CPU and fixed "
-                         "(test_isa_guards pins the compiled code against it)")
 def test_config1_single_gemm_256():
     """256^3, U(-1,1) bf16, fp32 output, no epilogue: every element against the oracle."""
     w = wl.config1()
@@ -108,16 +104,34 @@ def test_large_tiles_ragged(layout, epi):
 @pytest.mark.parametrize("shape", [(1000, 1032, 1096), (4096, 4096, 1024)])
 def test_integer_exact(layout, shape):
     """Integer entries: any summation order is exact in fp32, so the result is bit-exact.
-    Pins the whole pipeline: no k-step lost, repeated or read from a stale ring slot."""
+    Pins the whole pipeline: no k-step lost, repeated or read from a stale ring slot.  Every
+    element is compared."""
     M, N, K = shape
     rng = np.random.default_rng(M + K + layout)
     A = int_bf16(rng, (M, K))
     Bkn = int_bf16(rng, (K, N))
     B = Bkn if layout == wl.B_KN else np.ascontiguousarray(Bkn.T)
     out = ptg.gemm(dev_bf16(A), dev_bf16(B), b_layout=layout, out_dtype=torch.float32)
-    rows = sample_rows(M, 128, 2)
-    v = oracle.gemm(A, B, layout, rows=rows)
-    exact(out[torch.from_numpy(rows).cuda()], v, f"integer {shape}")
+    exact(out, oracle.gemm(A, B, layout), f"integer {shape}")
+
+
+def test_integer_exact_8192_full():
+    """The headline shape and launch configuration (8192^3, B stored N x K, large tiles) on
+    integer entries in [-4, 4]: every partial sum is an integer below 2^24, exact in fp32 in
+    any order, so the whole 8192 x 8192 output must equal the oracle bit for bit (fp32
+    output), and the bf16 output must be its correct rounding."""
+    M = N = K = 8192
+    rng = np.random.default_rng(8192)
+    A = int_bf16(rng, (M, K))
+    B = int_bf16(rng, (N, K))
+    assert ptg.describe_config(M, N, K, wl.B_NK)["BM"] == 256
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    out = ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.float32)
+    out16 = ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.bfloat16)
+    del dA, dB
+    v = oracle.gemm(A, B, wl.B_NK)
+    exact(out, v, "integer 8192^3 fp32")
+    exact(out16, v, "integer 8192^3 bf16")
 
 
 @pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])

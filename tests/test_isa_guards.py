@@ -1,9 +1,10 @@
 """Checks on the gfx950 assembly of the kernels (CPU only: hipcc cross-compiles).
 
-- Every buffer-to-LDS DMA takes a zero scalar offset.  The k-step offset is carried by the
-  descriptor base: gfx950 buffer-to-LDS loads are not used with a nonzero scalar offset,
-  and a kernel that used one faulted (its DMAs wrote outside their ring slots and reached
-  the tile metadata that holds the output pointer).
+- Every buffer-to-LDS DMA takes a zero scalar offset; the k-step offset is carried by the
+  descriptor base, the form AMD's own libraries use for these loads on gfx950.  (An earlier
+  kernel with a nonzero scalar offset faulted, but it also carried the sign-extension bug
+  below, which its compiled code shows and which is the cause; the zero offset is kept as
+  the documented form, not as the fix.)
 - No kernel spills to scratch, and none needs a waterfall loop around a DMA (a descriptor
   or offset the compiler believes divergent).
 - No scalar sign-extension of a 32-bit word into 64 bits (s_bfe_i64 with width 32).  A
@@ -136,3 +137,18 @@ def test_wide_output_stores_take_distinct_registers(asm):
                     srcs[dst] = src
             assert len(srcs) < 4 or len(set(srcs.values())) > 1, f"{name}: broadcast store {line.strip()}"
     assert n > 0
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_stress_pauses_only_in_the_test_build(asm, tmp_path):
+    """The product kernels read no cycle counter (the ring-stress pauses are compiled out);
+    the stress build's GEMM kernels do, at their handoffs."""
+    def memtimes(text):
+        return sum(1 for _, body in kernels(text) for l in body if l.strip().startswith("s_memtime"))
+    assert memtimes(asm) == 0
+    out = tmp_path / "delay.s"
+    src = "ptg_kernels.hip"
+    cmd = [build.hipcc(), *build.compile_flags(build.VARIANTS["delay"], source=src), "-S",
+           "--cuda-device-only", os.path.join(build.CSRC, src), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    assert memtimes(out.read_text()) > 0
