@@ -27,6 +27,14 @@ SOURCES = {
     "ptg_api.cpp": [],
 }
 DEVICE_SOURCES = [s for s in SOURCES if s.endswith(".hip")]
+# Test builds of the same sources, each a library of its own next to libptg.so (never loaded
+# by the package): "delay" pauses pseudo-randomly at every ring handoff (PTG_DELAY_INJECT),
+# for the ring stress tests.
+VARIANTS = {"delay": ["-DPTG_DELAY_INJECT=1"]}
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(HERE, f"libptg_{name}.so")
 
 
 def hipcc() -> str:
@@ -44,10 +52,14 @@ def compile_flags(extra=(), source=None):
             "-I", os.path.join(ROOT, "include"), *own, *extra]
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), variant: str = None) -> str:
+    """Builds libptg.so, or with `variant` the test build libptg_<variant>.so."""
     cc = hipcc()
     objs = []
-    tmpdir = os.path.join(HERE, "_build")
+    tmpdir = os.path.join(HERE, "_build", variant or "")
+    out = variant_path(variant) if variant else LIB
+    if variant:
+        extra = (*VARIANTS[variant], *extra)
     os.makedirs(tmpdir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(tmpdir, src + ".o")
@@ -58,14 +70,20 @@ def build(verbose: bool = False, extra=()) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
         objs.append(obj)
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build_all(verbose: bool = False) -> list:
+    """The library and every test build."""
+    return [build(verbose)] + [build(verbose, variant=v) for v in VARIANTS]
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    for path in build_all(verbose="-v" in sys.argv):
+        print(path)

@@ -253,7 +253,26 @@ __device__ __forceinline__ uint32_t lds_peek(const uint32_t* p) {
   return v;
 }
 
+// Ring stress build (compiled with PTG_DELAY_INJECT=1 into a separate test library, never
+// into the product): every handoff, each release or fill signal and each wait, first pauses
+// for a pseudo-random 0 to 8192 shader cycles (a hash of the cycle counter, the same on
+// every lane of the wave), so producers and consumers meet the ring in orders a natural run
+// rarely produces.  The handoff rule must hold under any timing; results stay bit-identical.
+#ifndef PTG_DELAY_INJECT
+#define PTG_DELAY_INJECT 0
+#endif
+__device__ __forceinline__ void stress_pause() {
+#if PTG_DELAY_INJECT
+  const uint64_t t = __builtin_amdgcn_s_memtime();
+  uint32_t h = (uint32_t)t * 2654435761u ^ (uint32_t)(t >> 9);
+  h ^= h >> 15;
+  const uint32_t r = (h >> 8) & 15u;
+  for (uint32_t i = 8; i < r + 1; ++i) __builtin_amdgcn_s_sleep(16);  // r >= 8: 1 to 8 x 1024 cycles
+#endif
+}
+
 __device__ __forceinline__ void lds_bump(uint32_t* p) {
+  stress_pause();
   __asm__ volatile("" ::: "memory");
   if (lane_id() == 0) {
     const uint32_t one = 1;
@@ -296,6 +315,7 @@ __device__ __forceinline__ void raise_abort(uint32_t* abort, uint32_t why) {
 
 // Wait until a monotone LDS counter reaches `target`; bounded (see kSpinLimit).
 __device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t target, uint32_t* abort) {
+  stress_pause();
   uint32_t polls = 0;
   while ((uint32_t)__builtin_amdgcn_readfirstlane(lds_peek(p)) < target) {
     __builtin_amdgcn_s_sleep(1);
@@ -847,7 +867,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::TM][C::TN], int wm, in
   const int half = lane >> 5;
   const int osz = f32out ? 4 : 2;
   const __amdgpu_buffer_rsrc_t rc =
-      make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)(((m_rows - 1) * ldc + n_cols) * osz));
+      make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)(((int64_t)(m_rows - 1) * ldc + n_cols) * osz));
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm) {
     const int row = wm * C::WTM + tm * 32 + (lane & 31);
@@ -1061,7 +1081,7 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
       raise_abort(abort, 2u);
       break;
     }
-    const uint64_t c_bytes = (uint64_t)((m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
+    const uint64_t c_bytes = (uint64_t)((int64_t)(m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
     if (!inside(Cp, c_bytes, uni64(guards->c_lo), uni64(guards->c_hi))) {
       raise_abort(abort, 8u);
       break;
@@ -1208,7 +1228,7 @@ __device__ __forceinline__ void epilogue16(f32x4 (&acc)[C::TM16][C::TN16], int w
   const int grp = lane >> 4;
   const int osz = f32out ? 4 : 2;
   const __amdgpu_buffer_rsrc_t rc =
-      make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)(((m_rows - 1) * ldc + n_cols) * osz));
+      make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)(((int64_t)(m_rows - 1) * ldc + n_cols) * osz));
 #pragma unroll
   for (int tm = 0; tm < C::TM16; ++tm) {
     const int row = wm * C::WTM + tm * 16 + (lane & 15);
@@ -1452,7 +1472,7 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
       raise_abort(abort, 2u);
       break;
     }
-    const uint64_t c_bytes = (uint64_t)((m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
+    const uint64_t c_bytes = (uint64_t)((int64_t)(m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
     if (!inside(Cp, c_bytes, uni64(guards->c_lo), uni64(guards->c_hi))) {
       raise_abort(abort, 8u);
       break;

@@ -13,11 +13,13 @@ def pytest_configure(config):
 
 def pytest_sessionstart(session):
     """Build what is missing (never rebuild what is there): the oracle's shared library and,
-    when the HIP toolchain is present, libptg.so."""
+    when the HIP toolchain is present, libptg.so and its test builds."""
     import importlib
     oracle = importlib.import_module("oracle")
     oracle.build(force=False)
-    lib = os.path.join(ROOT, "pipelined_tiled_gemm_amd", "libptg.so")
-    if not os.path.exists(lib):
-        from pipelined_tiled_gemm_amd import build
+    from pipelined_tiled_gemm_amd import build
+    if not os.path.exists(build.LIB):
         build.build()
+    for v in build.VARIANTS:
+        if not os.path.exists(build.variant_path(v)):
+            build.build(variant=v)
