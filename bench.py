@@ -6,8 +6,9 @@
 A step is one call of the pipelined GEMM on the headline workload: C = A.B with
 M = N = K = 8192, A row-major bf16, B stored transposed (N x K) bf16, entries N(0,1)/sqrt(K),
 fp32 accumulation, bf16 output (seeded synthetic data, resident in HBM before timing).
-W untimed steps, then exactly K timed steps between two device synchronisations; one JSON
-line is printed.
+W untimed steps (continued until at least --warm-s seconds of calls have run, so that the part
+is at its clock under load), then exactly K timed steps between two device synchronisations;
+one JSON line is printed.
 
 value            whole-job TFLOP/s over the timed steps (algorithmic 2 M N K flops per step)
 roofline         the GEMM kernel against MI355X's dense bf16 MFMA peak (2500 TFLOP/s); its
@@ -16,10 +17,12 @@ roofline         the GEMM kernel against MI355X's dense bf16 MFMA peak (2500 TFL
                  a summary for the current kernel sources exists under profiles/, else null
 cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload (some output
                  rows), on all host cores it uses, in the same unit
-secondary        grouped (mixture-of-experts) forward and weight gradient, broadcast, IKBO
-                 attention and batched workloads, timed the same way (TFLOP/s, % of peak, GB/s of
-                 compulsory traffic), plus per-call
-                 cold-cache times (median, min, p90) with a 512 MB scratch write between calls
+secondary        the 256^3 single GEMM (per-call latency in microseconds), grouped (mixture-of-
+                 experts) forward and weight gradient, broadcast, IKBO attention and batched
+                 workloads: TFLOP/s, % of peak, GB/s of compulsory traffic from per-call
+                 cold-cache times (median, min, p90; a 512 MB scratch write before every call)
+                 as the primary figures of the memory-relevant workloads, warm back-to-back
+                 figures beside them (labelled), and the oracle timed on a sample of each
 """
 import argparse
 import hashlib
@@ -99,6 +102,23 @@ def time_calls(fn, steps, warmup, torch, min_warm_s=0.0):
     return (t1 - t0) / steps, e0.elapsed_time(e1) / steps
 
 
+def time_each(fn, reps, torch):
+    """Per-call durations of back-to-back calls (an event pair around each call on the current
+    stream).  Returns {median, min, p90} in milliseconds."""
+    stream = torch.cuda.current_stream()
+    pairs = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in pairs)
+    return {"median": t[len(t) // 2], "min": t[0], "p90": t[min(len(t) - 1, (9 * len(t)) // 10)], "reps": reps}
+
+
 def time_cold(fn, reps, torch, flush_bytes=512 << 20):
     """Per-call durations with the caches cold: before each call a 512 MB scratch buffer is
     written (outside the event pair), which evicts the 256 MB last-level cache and the L2s.
@@ -122,13 +142,91 @@ def time_cold(fn, reps, torch, flush_bytes=512 << 20):
             "p90": round(t[min(len(t) - 1, (9 * len(t)) // 10)], 4), "reps": reps}
 
 
-def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2):
-    """Warm-cache throughput (back-to-back calls, as for the headline GEMM) plus per-call cold-cache
-    times (median, min, p90) for each of the memory-relevant workloads.  Each workload's inputs
-    are drawn on the host for several seconds while the GPU idles; its warm timing starts after
-    at least `warm_s` seconds of calls, once the part has come back to its clock under load
-    (the first tens of milliseconds after idling run several percent slower)."""
+def figures(f, b, ms):
+    """TFLOP/s, % of the MFMA peak, GB/s of compulsory traffic and % of HBM peak at `ms`."""
+    return {"ms": round(ms, 4), "tflops": round(f / ms / 1e9, 2),
+            "pct_peak": round(100 * f / ms / 1e9 / PEAK_TFLOPS, 2),
+            "gbs": round(b / ms / 1e6, 1), "pct_hbm": round(100 * b / ms / 1e6 / PEAK_GBS, 2)}
+
+
+def entry(f, b, warm_ms, cold, primary="cold", **extra):
+    """One workload's line.  The top-level figures are the primary ones: cold-cache (median
+    of per-call times after a cache flush) for the memory-relevant workloads, warm (back-to-back
+    calls) otherwise; the other set follows, labelled."""
+    e = {"primary": primary}
+    e.update(figures(f, b, cold["median"] if primary == "cold" else warm_ms))
+    e["cold_ms"] = cold
+    e["warm"] = figures(f, b, warm_ms)
+    e.update(extra)
+    return e
+
+
+def oracle_timed(make_sample, n_all, budget_s, threads=None):
+    """The CPU oracle, untuned, on a bounded sample: `make_sample(n)` runs it on n units (rows
+    or problems) of a workload of `n_all`; a probe of a few units sizes the timed sample to
+    about `budget_s` seconds.  Returns (units, seconds, threads used)."""
+    import oracle
+    oracle.build(force=False)
+    prev = oracle.max_threads()
+    if threads:
+        oracle.set_threads(threads)
+    try:
+        make_sample(min(n_all, 2))                       # thread pool and page-in
+        n = min(n_all, 8)
+        t0 = time.perf_counter()
+        make_sample(n)
+        dt = time.perf_counter() - t0
+        n = int(max(n, min(n_all, n * budget_s / max(dt, 1e-4))))
+        t0 = time.perf_counter()
+        make_sample(n)
+        dt = time.perf_counter() - t0
+        cores = oracle.max_threads()
+    finally:
+        oracle.set_threads(prev)
+    return n, dt, cores
+
+
+def cpu_entry(n, dt, cores, unit_flops, what):
+    return {"value": round(n * unit_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3), "sample": what}
+
+
+def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2, cpu=True, cpu_budget_s=2.0):
+    """Each secondary workload: warm-cache throughput (back-to-back calls, as for the headline
+    GEMM) and per-call cold-cache times (median, min, p90) with a cache flush before every
+    call; the cold figures are the primary ones for the memory-relevant workloads.  Each
+    workload's inputs are drawn on the host for several seconds while the GPU idles; its warm
+    timing starts after at least `warm_s` seconds of calls, once the part has come back to its
+    clock under load (the first tens of milliseconds after idling run several percent slower).
+    With `cpu`, the oracle is timed on a bounded sample of the same workload."""
+    import oracle
     out = {}
+
+    # the 256^3 single GEMM (fp32 out): launch-latency bound, so per-call times in microseconds
+    w = wl.config1()
+    A, B = to_dev(w.A, torch, np), to_dev(w.B, torch, np)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    call = lambda: ptg.gemm(A, B, b_layout=w.b_layout, out=C)  # noqa: E731
+    time_calls(call, 10, 10, torch, min_warm_s=warm_s)
+    warm = time_each(call, 200, torch)
+    cold = time_cold(call, cold_reps, torch)
+    f, b = wl.dense_flops(w.M, w.N, w.K), wl.dense_bytes(w.M, w.N, w.K, "f32")
+    e = {"primary": "warm per-call latency",
+         "us_median": round(1e3 * warm["median"], 2), "us_min": round(1e3 * warm["min"], 2),
+         "us_p90": round(1e3 * warm["p90"], 2), "calls": warm["reps"],
+         "tflops": round(f / warm["median"] / 1e9, 3), "gbs": round(b / warm["median"] / 1e6, 1),
+         "cold_us": {k: (round(1e3 * v, 2) if k != "reps" else v) for k, v in cold.items()},
+         "roofline": "not meaningful: launch-latency bound (0.013 us of MFMA work, 0.07 us of HBM traffic)"}
+    if cpu:
+        # the whole GEMM, repeated: unit r is the r-th call on all 256 rows
+        def whole(n):
+            for _ in range(n):
+                oracle.gemm(w.A, w.B, w.b_layout)
+        for threads, key in ((None, "cpu_baseline"), (1, "cpu_baseline_1core")):
+            n, dt, cores = oracle_timed(whole, 1 << 20, 0.5, threads=threads)
+            e[key] = cpu_entry(n, dt, cores, f, f"{n} calls of the whole 256^3 GEMM ({1e6 * dt / n:.0f} us each)")
+    out["config1_gemm_256_f32"] = e
+    del A, B, C, w
 
     # grouped: 64 experts, 16384 rows, K=4096, N=1536, Zipf(1.1) routing under both readings
     # of the weights: rank-Zipf (expert e weighted (e+1)^-1.1; every expert gets rows) and
@@ -141,12 +239,15 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2):
         call = lambda: ptg.grouped_gemm(X, W, off, out=Y)  # noqa: E731
         _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
         f, b = wl.grouped_flops(w), wl.grouped_bytes(w)
-        out[name] = {
-            "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-            "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
-            "live_groups": int((w.counts > 0).sum()),
-            "cold_ms": time_cold(call, cold_reps, torch)}
-        del X, W, off, Y, w
+        e = entry(f, b, ms, time_cold(call, cold_reps, torch), live_groups=int((w.counts > 0).sum()))
+        if cpu and reading == "rank":
+            rows = np.random.default_rng(0).permutation(w.M_total)
+            n, dt, cores = oracle_timed(lambda n: oracle.grouped_gemm(
+                w.X, w.W, w.w_layout, w.offsets, rows=np.sort(rows[:n])), w.M_total, cpu_budget_s)
+            e["cpu_baseline"] = cpu_entry(n, dt, cores, 2.0 * w.N * w.K,
+                                          f"{n} random rows of {w.M_total} (all {w.N} columns)")
+        out[name] = e
+        del X, W, off, Y
     # weight gradient of the same MoE layer: dW_g = X_g^T . dY_g, 64 x 4096 x 1536 bf16
     w = wl.moe_wgrad()
     X, dY, off = to_dev(w.X, torch, np), to_dev(w.dY, torch, np), torch.from_numpy(w.offsets).cuda()
@@ -155,10 +256,16 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2):
     call = lambda: ptg.grouped_gemm_wgrad(X, dY, off, out=dW, workspace=wq)  # noqa: E731
     _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, b = wl.wgrad_flops(w), wl.wgrad_bytes(w)
-    out["grouped_wgrad_moe_64x16384x4096x1536"] = {
-        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
-        "cold_ms": time_cold(call, cold_reps, torch)}
+    e = entry(f, b, ms, time_cold(call, cold_reps, torch))
+    if cpu:
+        rows = np.random.default_rng(0).permutation(w.G * w.K)
+        n, dt, cores = oracle_timed(lambda n: oracle.grouped_wgrad(
+            w.X, w.dY, w.offsets, rows=np.sort(rows[:n])), w.G * w.K, cpu_budget_s)
+        # a row g*K + i of dW costs 2 * count_g * N flops; over random rows the mean is
+        # 2 * N * M_total / G
+        e["cpu_baseline"] = cpu_entry(n, dt, cores, 2.0 * w.M_total * w.N / w.G,
+                                      f"{n} random rows of the {w.G * w.K} rows of dW (flops at the mean row cost)")
+    out["grouped_wgrad_moe_64x16384x4096x1536"] = e
     del X, dY, off, dW, wq, w
     # broadcast: 64 users, sum C_u = 81403 candidates, [2048 | 512] -> 1024
     w = wl.config4()
@@ -169,12 +276,18 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2):
     call = lambda: ptg.broadcast_gemm(Xu, Xc, idx, W, out=Y, workspace=ws)  # noqa: E731
     _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, fm, b = wl.broadcast_flops(w), wl.broadcast_flops_materialised(w), wl.broadcast_bytes(w)
-    out["broadcast_ikbo_64users_81403cand"] = {
-        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-        "effective_tflops_materialised_equivalent": fm / ms / 1e9,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
-        "cold_ms": time_cold(call, cold_reps, torch)}
-    del Xu, Xc, idx, W, Y, ws, w
+    cold = time_cold(call, cold_reps, torch)
+    e = entry(f, b, ms, cold, effective_tflops_materialised_equivalent=round(fm / cold["median"] / 1e9, 1))
+    if cpu:
+        rows = np.random.default_rng(0).permutation(w.Mc)
+        n, dt, cores = oracle_timed(lambda n: oracle.broadcast_gemm(
+            w.Xu, w.Xc, w.idx, w.W, w.w_layout, rows=np.sort(rows[:n])), w.Mc, cpu_budget_s)
+        # the oracle computes the materialised definition: (Ku + Kc) per output element
+        e["cpu_baseline"] = cpu_entry(n, dt, cores, 2.0 * (w.Ku + w.Kc) * w.N,
+                                      f"{n} random candidate rows of {w.Mc}, materialised [Xu[idx] | Xc] . W "
+                                      f"(flops as computed)")
+    out["broadcast_ikbo_64users_81403cand"] = e
+    del Xu, Xc, idx, W, Y, ws
     # IKBO attention: 64 users (C_u ~ U{256..2048}), context of 1024 keys, 4 heads of 128
     w = wl.ikbo_attention_workload()
     Q, K, V = (to_dev(w.Q.reshape(w.Mc, -1), torch, np).view(w.Mc, w.H, w.D),
@@ -185,10 +298,14 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2):
     call = lambda: ptg.ikbo_attention(Q, K, V, off, scale=w.scale, out=O)  # noqa: E731
     _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, b = wl.attention_flops(w), wl.attention_bytes(w)
-    out["ikbo_attention_64users_77801cand_L1024_H4_D128"] = {
-        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
-        "cold_ms": time_cold(call, cold_reps, torch)}
+    e = entry(f, b, ms, time_cold(call, cold_reps, torch), primary="warm")
+    if cpu:
+        rows = np.random.default_rng(0).permutation(w.Mc)
+        n, dt, cores = oracle_timed(lambda n: oracle.ikbo_attention(
+            w.Q, w.K, w.V, w.offsets, w.scale, rows=np.sort(rows[:n])), w.Mc, cpu_budget_s)
+        e["cpu_baseline"] = cpu_entry(n, dt, cores, 4.0 * w.H * w.L * w.D,
+                                      f"{n} random candidates of {w.Mc} (all heads)")
+    out["ikbo_attention_64users_77801cand_L1024_H4_D128"] = e
     del Q, K, V, off, O, w
     # batch: 1024 independent GEMMs with fused bias + SiLU, one persistent launch
     pl = wl.config5()
@@ -197,15 +314,27 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2):
         probs.append((to_dev(p.A, torch, np), to_dev(p.B, torch, np),
                       torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda"),
                       torch.from_numpy(p.bias).cuda()))
-    ws = torch.empty(ptg.gemm_batch_workspace(len(probs)), dtype=torch.uint8, device="cuda")
-    ptg.gemm_batch_prepare(probs, pl.epi, ws)
-    call = lambda: ptg.gemm_batch_run(len(probs), ws, torch.bfloat16, pl.epi)  # noqa: E731
+    ws = torch.empty(ptg.grouped_gemm_ptr_array_workspace(len(probs)), dtype=torch.uint8, device="cuda")
+    ptg.grouped_gemm_ptr_array_prepare(probs, pl.epi, ws)
+    call = lambda: ptg.grouped_gemm_ptr_array_run(len(probs), ws, torch.bfloat16, pl.epi)  # noqa: E731
     _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
     f, b = wl.problem_list_flops(pl), wl.problem_list_bytes(pl)
-    out["batch_recsys_1024_bias_silu"] = {
-        "ms": ms, "tflops": f / ms / 1e9, "pct_peak": 100 * f / ms / 1e9 / PEAK_TFLOPS,
-        "gbs": b / ms / 1e6, "pct_hbm": 100 * b / ms / 1e6 / PEAK_GBS,
-        "cold_ms": time_cold(call, cold_reps, torch)}
+    e = entry(f, b, ms, time_cold(call, cold_reps, torch))
+    if cpu:
+        order = np.random.default_rng(0).permutation(len(pl.problems))
+        pf = [2.0 * p.M * p.N * p.K for p in pl.problems]
+
+        def run(n):
+            for i in order[:n]:
+                q = pl.problems[i]
+                oracle.gemm(q.A, q.B, wl.B_KN, q.bias, pl.epi)
+        for threads, key in ((None, "cpu_baseline"), (1, "cpu_baseline_1core")):
+            n, dt, cores = oracle_timed(run, len(pl.problems), cpu_budget_s, threads=threads)
+            fl = sum(pf[i] for i in order[:n])
+            e[key] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                      "seconds": round(dt, 3),
+                      "sample": f"{n} random problems of {len(pl.problems)}, whole (every row)"}
+    out["batch_recsys_1024_bias_silu"] = e
     return out
 
 
@@ -236,6 +365,8 @@ def main():
     # and the 200 timed steps ~0.17 s.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
+    # ... and, whatever the step count, at least this many seconds of untimed calls
+    ap.add_argument("--warm-s", type=float, default=0.5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -258,7 +389,7 @@ def main():
     flops = wl.dense_flops(w.M, w.N, w.K)
     ptg.watchdog(clear=True)
     step = lambda: ptg.gemm(A, B, b_layout=wl.B_NK, out=C)  # noqa: E731
-    wall_s, ev_ms = time_calls(step, args.steps, args.warmup, torch)
+    wall_s, ev_ms = time_calls(step, args.steps, args.warmup, torch, min_warm_s=args.warm_s)
     if ptg.watchdog(clear=True) != 0:
         raise RuntimeError("a pipeline wait timed out during the benchmark")
     value = flops / wall_s / 1e12
@@ -271,6 +402,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warm_s": args.warm_s,
         "ms_per_step": round(wall_s * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -296,7 +428,8 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     if not args.no_secondary:
-        line["secondary"] = secondary(torch, np, ptg, wl, max(5, args.steps // 2), max(3, args.warmup))
+        line["secondary"] = secondary(torch, np, ptg, wl, max(50, args.steps // 2), max(3, args.warmup),
+                                      cpu=not args.no_cpu)
         if ptg.watchdog(clear=True) != 0:
             raise RuntimeError("a pipeline wait timed out during the secondary workloads")
     if not args.no_cpu:
