@@ -246,6 +246,25 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
                               const float* bias, ptg_epilogue epi,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * ptg_broadcast_gemm_noalloc - ptg_broadcast_gemm for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and errors as ptg_broadcast_gemm, without the workspace: P and the
+ * user phase's partial products live in a file-scope device array of the library, 16 MiB per
+ * GPU (16,777,216 bytes), held until the process ends.  A call whose workspace query
+ * ptg_broadcast_gemm_workspace(U, N) exceeds 16 MiB is refused with PTG_ERR_UNSUPPORTED.  The
+ * call allocates nothing (no hipMalloc, no allocating library routine); on its first use on a
+ * device it looks up that device's copy of the array.  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents (every call overwrites what it reads, so
+ * nothing needs clearing): calls that overlap on one GPU (on different streams, or from
+ * different threads) race and must not be issued.
+ */
+ptg_status ptg_broadcast_gemm_noalloc(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N,
+                                      const void* Xu, const void* Xc, const int32_t* user_idx,
+                                      const void* W, ptg_layout w_layout,
+                                      void* Y, ptg_dtype y_dtype,
+                                      const float* bias, ptg_epilogue epi, void* stream);
+
 /* ptg_broadcast_gemm_check - validates 0 <= user_idx[r] < U on the device, synchronises
  * `stream`, returns PTG_OK or PTG_ERR_DEVICE_CHECK (also when the device's watchdog word is
  * set); concurrent as ptg_grouped_gemm_check. */

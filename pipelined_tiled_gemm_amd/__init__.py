@@ -22,7 +22,7 @@ __all__ = [
     "PtgError", "B_KN", "B_NK", "EPI_NONE", "EPI_BIAS", "EPI_SILU", "EPI_BIAS_SILU",
     "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace", "ikbo_attention",
     "grouped_gemm_ptr_array_workspace", "grouped_gemm_ptr_array", "grouped_gemm_ptr_array_prepare",
-    "grouped_gemm_ptr_array_run", "broadcast_gemm_workspace", "broadcast_gemm",
+    "grouped_gemm_ptr_array_run", "broadcast_gemm_workspace", "broadcast_gemm", "broadcast_gemm_noalloc",
     "broadcast_gemm_check", "watchdog", "version", "describe_config", "status_string",
     "last_error", "library_path",
 ]
@@ -324,12 +324,7 @@ def broadcast_gemm_workspace(U: int, N: int) -> int:
     return int(_lib().ptg_broadcast_gemm_workspace(U, N))
 
 
-def broadcast_gemm(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W: torch.Tensor, *,
-                   w_layout: int = B_KN, out: Optional[torch.Tensor] = None,
-                   out_dtype: torch.dtype = torch.bfloat16, bias: Optional[torch.Tensor] = None,
-                   epi: int = EPI_NONE, workspace: Optional[torch.Tensor] = None,
-                   stream=None) -> torch.Tensor:
-    """Y[r] = epi([Xu[user_idx[r]] | Xc[r]].W + bias) without materialising Xu[user_idx]."""
+def _broadcast_args(Xu, Xc, user_idx, W, w_layout, out, out_dtype, bias, epi):
     _need(Xu, "Xu", torch.bfloat16, 2)
     _need(Xc, "Xc", torch.bfloat16, 2)
     _need(W, "W", torch.bfloat16, 2)
@@ -349,14 +344,36 @@ def broadcast_gemm(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W
         out = torch.empty((Mc, N), dtype=out_dtype, device=Xc.device)
     if not out.is_contiguous() or tuple(out.shape) != (Mc, N):
         raise ValueError(f"out must be a contiguous [{Mc}, {N}] tensor")
+    bias = _bias_for(bias, epi, N, "bias")
+    return (U, Mc, Ku, Kc, N, _ptr(Xu), _ptr(Xc), _ptr(user_idx), _ptr(W), w_layout, _ptr(out),
+            _dtype_code(out.dtype), _ptr(bias), epi), out
+
+
+def broadcast_gemm(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W: torch.Tensor, *,
+                   w_layout: int = B_KN, out: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.bfloat16, bias: Optional[torch.Tensor] = None,
+                   epi: int = EPI_NONE, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Y[r] = epi([Xu[user_idx[r]] | Xc[r]].W + bias) without materialising Xu[user_idx]."""
+    args, out = _broadcast_args(Xu, Xc, user_idx, W, w_layout, out, out_dtype, bias, epi)
+    U, N = args[0], args[4]
     if workspace is None:
         workspace = torch.empty(max(broadcast_gemm_workspace(U, N), 16), dtype=torch.uint8,
                                 device=Xc.device)
-    bias = _bias_for(bias, epi, N, "bias")
-    _check(_lib().ptg_broadcast_gemm(U, Mc, Ku, Kc, N, _ptr(Xu), _ptr(Xc), _ptr(user_idx), _ptr(W),
-                                     w_layout, _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi,
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+    _check(_lib().ptg_broadcast_gemm(*args, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+    return out
+
+
+def broadcast_gemm_noalloc(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W: torch.Tensor, *,
+                           out: torch.Tensor, w_layout: int = B_KN, bias: Optional[torch.Tensor] = None,
+                           epi: int = EPI_NONE, stream=None) -> torch.Tensor:
+    """broadcast_gemm without a workspace and without any allocation (the caller passes `out`):
+    the library's own per-GPU scratch array holds P (calls overlapping on one GPU race)."""
+    if out is None:
+        raise ValueError("out is required: this call allocates nothing")
+    args, out = _broadcast_args(Xu, Xc, user_idx, W, w_layout, out, out.dtype, bias, epi)
+    _check(_lib().ptg_broadcast_gemm_noalloc(*args, _stream(stream)))
     return out
 
 

@@ -507,12 +507,19 @@ size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N) {
   return (size_t)U * (size_t)N * sizeof(float) * (splits > 1 ? 1 + (size_t)splits : 1);
 }
 
-ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
-                              const void* Xc, const int32_t* user_idx, const void* W, ptg_layout w_layout,
-                              void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
-                              void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The broadcast GEMM behind both entry points.  `scratch(need, &ws, &bytes)` supplies the
+// workspace once every host-checkable argument has passed (the caller's, or the library's
+// static array), or returns an error status.
+template <class Scratch>
+ptg_status broadcast_call(const char* fn, int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
+                          const void* Xc, const int32_t* user_idx, const void* W, ptg_layout w_layout,
+                          void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                          Scratch scratch, void* stream) {
   PTG_TRY({
-    const char* fn = "ptg_broadcast_gemm";
+    ptg_status st = PTG_OK;
     if (U <= 0 || Mc < 0 || Ku < 0 || Kc < 0 || N < 0)
       return fail(PTG_ERR_INVALID_ARG, "%s: bad sizes (U must be positive)", fn);
     if (Ku == 0 || Kc == 0) return fail(PTG_ERR_UNSUPPORTED, "%s: Ku and Kc must be positive", fn);
@@ -525,10 +532,7 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
     if (Mc == 0 || N == 0) return PTG_OK;
     if (!Xu || !Xc || !user_idx || !W || !Y) return fail(PTG_ERR_INVALID_ARG, "%s: null operand", fn);
     if (needs_bias(epi) && !bias) return fail(PTG_ERR_INVALID_ARG, "%s: epilogue needs a bias", fn);
-    const size_t need = ptg_broadcast_gemm_workspace(U, N);
-    if (!workspace || ws_bytes < need)
-      return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
-    if (!aligned16(Xu) || !aligned16(Xc) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace) ||
+    if (!aligned16(Xu) || !aligned16(Xc) || !aligned16(W) || !aligned16(Y) ||
         (bias && !aligned16(bias)) || (reinterpret_cast<uintptr_t>(user_idx) & 3u))
       return fail(PTG_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (indices 4-byte)", fn);
     const int64_t Kt = Ku + Kc;
@@ -538,6 +542,14 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
       return fail(PTG_ERR_UNSUPPORTED, "%s: operand or output tile exceeds 2 GiB of addressing", fn);
     if (U * N * 4 >= ((int64_t)1 << 31))
       return fail(PTG_ERR_UNSUPPORTED, "%s: P (U x N fp32) exceeds 2 GiB of addressing", fn);
+    void* workspace = nullptr;
+    size_t ws_bytes = 0;
+    const size_t need = ptg_broadcast_gemm_workspace(U, N);
+    st = scratch(need, &workspace, &ws_bytes);
+    if (st) return st;
+    if (!workspace || ws_bytes < need)
+      return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* P = reinterpret_cast<float*>(workspace);
     // Matmul decomposition: the user half of W meets each user's features once ...
@@ -583,6 +595,62 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
   })
+}
+
+
+// Scratch of ptg_broadcast_gemm_noalloc: one array per GPU, held until the process ends.  In
+// host code `g_noalloc_scratch` names a host-side stand-in; the device address of each GPU's
+// copy comes from hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+__device__ __attribute__((aligned(256))) char g_noalloc_scratch[kNoAllocScratchBytes];
+
+ptg_status noalloc_scratch(const char* fn, void** ptr) {
+  static std::mutex mu;
+  static std::vector<void*> addr;  // per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_noalloc_scratch));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return PTG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
+                              const void* Xc, const int32_t* user_idx, const void* W, ptg_layout w_layout,
+                              void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return broadcast_call("ptg_broadcast_gemm", U, Mc, Ku, Kc, N, Xu, Xc, user_idx, W, w_layout, Y, y_dtype, bias,
+                        epi, [&](size_t, void** ws, size_t* bytes) {
+                          *ws = workspace;
+                          *bytes = ws_bytes;
+                          return PTG_OK;
+                        }, stream);
+}
+
+ptg_status ptg_broadcast_gemm_noalloc(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
+                                      const void* Xc, const int32_t* user_idx, const void* W, ptg_layout w_layout,
+                                      void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                                      void* stream) {
+  const char* fn = "ptg_broadcast_gemm_noalloc";
+  return broadcast_call(fn, U, Mc, Ku, Kc, N, Xu, Xc, user_idx, W, w_layout, Y, y_dtype, bias, epi,
+                        [&](size_t need, void** ws, size_t* bytes) {
+                          if (need > kNoAllocScratchBytes)
+                            return fail(PTG_ERR_UNSUPPORTED, "%s: %zu bytes of scratch needed, at most %zu available",
+                                        fn, need, kNoAllocScratchBytes);
+                          *bytes = kNoAllocScratchBytes;
+                          return noalloc_scratch(fn, ws);
+                        }, stream);
 }
 
 ptg_status ptg_watchdog(uint32_t* value, int32_t clear) {

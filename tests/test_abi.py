@@ -260,3 +260,19 @@ def test_build_compiles_every_source_with_its_flags():
     for src in build.SOURCES:
         flags = build.compile_flags(source=src)
         assert "--offload-arch=gfx950" in flags and "-packed-fp32-ops" in flags
+
+
+def test_broadcast_noalloc_validation(L):
+    """Host-side refusals of the entry point that allocates nothing: the usual argument checks,
+    and a workspace need beyond its 16 MiB scratch array."""
+    def b(U=4, Mc=100, Ku=64, Kc=32, N=64, Xu=P, Xc=P, idx=P, W=P, layout=0, Y=P, dtype=0, bias=None, epi=0):
+        return L.ptg_broadcast_gemm_noalloc(U, Mc, Ku, Kc, N, Xu, Xc, idx, W, layout, Y, dtype, bias, epi, None)
+    assert b(U=0) == INVALID
+    assert b(Kc=0) == UNSUPPORTED
+    assert b(idx=None) == INVALID
+    assert b(epi=1) == INVALID                      # bias missing
+    assert b(Mc=0, Xu=None, Xc=None, idx=None, W=None, Y=None) == OK
+    U, N = 256, 4096
+    assert L.ptg_broadcast_gemm_workspace(U, N) > 16 << 20
+    assert b(U=U, N=N) == UNSUPPORTED
+    assert "16777216" in L.ptg_last_error().decode()
