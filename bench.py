@@ -236,10 +236,13 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2, cpu=T
         w = wl.config3(reading)
         X, W, off = to_dev(w.X, torch, np), to_dev(w.W, torch, np), torch.from_numpy(w.offsets).cuda()
         Y = torch.empty((w.M_total, w.N), dtype=torch.bfloat16, device="cuda")
-        call = lambda: ptg.grouped_gemm(X, W, off, out=Y)  # noqa: E731
+        # with the split workspace: a last round of idle workgroups runs its tiles as two units
+        gws = torch.empty(ptg.grouped_gemm_split_workspace(), dtype=torch.uint8, device="cuda")
+        call = lambda: ptg.grouped_gemm(X, W, off, out=Y, workspace=gws)  # noqa: E731
         _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
         f, b = wl.grouped_flops(w), wl.grouped_bytes(w)
-        e = entry(f, b, ms, time_cold(call, cold_reps, torch), live_groups=int((w.counts > 0).sum()))
+        e = entry(f, b, ms, time_cold(call, cold_reps, torch), live_groups=int((w.counts > 0).sum()),
+                  entry_point="ptg_grouped_gemm_split")
         if cpu and reading == "rank":
             rows = np.random.default_rng(0).permutation(w.M_total)
             n, dt, cores = oracle_timed(lambda n: oracle.grouped_gemm(
@@ -247,7 +250,7 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2, cpu=T
             e["cpu_baseline"] = cpu_entry(n, dt, cores, 2.0 * w.N * w.K,
                                           f"{n} random rows of {w.M_total} (all {w.N} columns)")
         out[name] = e
-        del X, W, off, Y
+        del X, W, off, Y, gws
     # weight gradient of the same MoE layer: dW_g = X_g^T . dY_g, 64 x 4096 x 1536 bf16
     w = wl.moe_wgrad()
     X, dY, off = to_dev(w.X, torch, np), to_dev(w.dY, torch, np), torch.from_numpy(w.offsets).cuda()

@@ -110,6 +110,31 @@ ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K,
                             void* Y, ptg_dtype y_dtype,
                             const float* bias, ptg_epilogue epi, void* stream);
 
+/*
+ * ptg_grouped_gemm_split - ptg_grouped_gemm with a workspace that lets the last round of tiles
+ * use otherwise idle workgroups: when that round fills at most half the workgroups, each of its
+ * tiles runs as two units, a full tile by columns (128 each), any other tile by reduction (each
+ * unit takes half of the k-steps; the two fp32 partial sums are added in the workspace by the
+ * unit that finishes second, which then runs the epilogue).  Same arguments, results and
+ * errors as ptg_grouped_gemm, plus:
+ *   workspace  DEVICE, 16-byte aligned, ws_bytes >= ptg_grouped_gemm_split_workspace() (for the
+ *              current device: a 128-byte sync block and a 256 KB partial image per possible
+ *              split tile, half the device's compute units; 32 MiB and 16 KiB on a 256-CU
+ *              MI355X).  Its content on entry does not matter and needs no clearing: the sync
+ *              words carry a per-call epoch.  Calls that run at the same time must not share it.
+ * A tile split by reduction sums its two halves of k separately, so its elements may differ
+ * from ptg_grouped_gemm's in the last bits (the same fp32 accumulation tolerance holds); the
+ * result does not depend on which unit finishes first.
+ * ptg_grouped_gemm_split_workspace returns 0 when no device is available.
+ */
+size_t ptg_grouped_gemm_split_workspace(void);
+ptg_status ptg_grouped_gemm_split(int32_t G, int64_t M_total, int64_t N, int64_t K,
+                                  const void* X, const void* W, ptg_layout w_layout,
+                                  const int32_t* group_offsets,
+                                  void* Y, ptg_dtype y_dtype,
+                                  const float* bias, ptg_epilogue epi,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
 /* ptg_grouped_gemm_check - validates group_offsets on the device (offsets[0] = 0,
  * nondecreasing, offsets[G] = M_total), synchronises `stream`, and returns PTG_OK, or
  * PTG_ERR_DEVICE_CHECK when the offsets break the precondition or the device's watchdog

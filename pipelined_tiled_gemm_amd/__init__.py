@@ -20,7 +20,7 @@ from . import _ffi
 
 __all__ = [
     "PtgError", "B_KN", "B_NK", "EPI_NONE", "EPI_BIAS", "EPI_SILU", "EPI_BIAS_SILU",
-    "gemm", "grouped_gemm", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace", "ikbo_attention",
+    "gemm", "grouped_gemm", "grouped_gemm_split_workspace", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace", "ikbo_attention",
     "grouped_gemm_ptr_array_workspace", "grouped_gemm_ptr_array", "grouped_gemm_ptr_array_prepare",
     "grouped_gemm_ptr_array_run", "broadcast_gemm_workspace", "broadcast_gemm", "broadcast_gemm_noalloc",
     "broadcast_gemm_check", "watchdog", "version", "describe_config", "status_string",
@@ -148,11 +148,18 @@ def gemm(A: torch.Tensor, B: torch.Tensor, *, b_layout: int = B_KN, out: Optiona
     return out
 
 
+def grouped_gemm_split_workspace() -> int:
+    return int(_lib().ptg_grouped_gemm_split_workspace())
+
+
 def grouped_gemm(X: torch.Tensor, W: torch.Tensor, group_offsets: torch.Tensor, *,
                  w_layout: int = B_KN, out: Optional[torch.Tensor] = None,
                  out_dtype: torch.dtype = torch.bfloat16, bias: Optional[torch.Tensor] = None,
-                 epi: int = EPI_NONE, stream=None) -> torch.Tensor:
-    """Y[r] = epi(X[r].W[g] + bias[g]) for offsets[g] <= r < offsets[g+1] (offsets on device)."""
+                 epi: int = EPI_NONE, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Y[r] = epi(X[r].W[g] + bias[g]) for offsets[g] <= r < offsets[g+1] (offsets on device).
+    With `workspace` (uint8, device, at least grouped_gemm_split_workspace() bytes) the call is
+    ptg_grouped_gemm_split: the last round of tiles may run as two units per tile."""
     _need(X, "X", torch.bfloat16, 2)
     _need(W, "W", torch.bfloat16, 3)
     _need(group_offsets, "group_offsets", torch.int32, 1)
@@ -170,8 +177,13 @@ def grouped_gemm(X: torch.Tensor, W: torch.Tensor, group_offsets: torch.Tensor, 
     if bias is not None and epi in (EPI_BIAS, EPI_BIAS_SILU) and tuple(bias.shape) != (G, N):
         raise ValueError(f"bias must be [{G}, {N}]")
     bias = _bias_for(bias, epi, G * N, "bias", dims=2)
-    _check(_lib().ptg_grouped_gemm(G, M, N, K, _ptr(X), _ptr(W), w_layout, _ptr(group_offsets),
-                                   _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi, _stream(stream)))
+    if workspace is None:
+        _check(_lib().ptg_grouped_gemm(G, M, N, K, _ptr(X), _ptr(W), w_layout, _ptr(group_offsets),
+                                       _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi, _stream(stream)))
+    else:
+        _check(_lib().ptg_grouped_gemm_split(G, M, N, K, _ptr(X), _ptr(W), w_layout, _ptr(group_offsets),
+                                             _ptr(out), _dtype_code(out.dtype), _ptr(bias), epi,
+                                             _ptr(workspace), _workspace_bytes(workspace), _stream(stream)))
     return out
 
 

@@ -22,7 +22,8 @@ STATUS_NAMES = {
 
 # Every symbol include/ptg.h declares (checked by the CPU tests).
 EXPORTS = (
-    "ptg_gemm", "ptg_grouped_gemm", "ptg_grouped_gemm_check", "ptg_grouped_gemm_wgrad",
+    "ptg_gemm", "ptg_grouped_gemm", "ptg_grouped_gemm_split", "ptg_grouped_gemm_split_workspace",
+    "ptg_grouped_gemm_check", "ptg_grouped_gemm_wgrad",
     "ptg_grouped_gemm_wgrad_workspace", "ptg_ikbo_attention",
     "ptg_grouped_gemm_ptr_array_workspace", "ptg_grouped_gemm_ptr_array",
     "ptg_grouped_gemm_ptr_array_prepare", "ptg_grouped_gemm_ptr_array_run",
@@ -67,6 +68,9 @@ def open_library(path: str):
     L.ptg_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, e, p, i64, e, p, e, p]
     L.ptg_grouped_gemm.argtypes = [i32, i64, i64, i64, p, p, e, p, p, e, p, e, p]
     L.ptg_grouped_gemm_check.argtypes = [i32, i64, p, p]
+    L.ptg_grouped_gemm_split.argtypes = [i32, i64, i64, i64, p, p, e, p, p, e, p, e, p, sz, p]
+    L.ptg_grouped_gemm_split_workspace.argtypes = []
+    L.ptg_grouped_gemm_split_workspace.restype = sz
     L.ptg_grouped_gemm_wgrad.argtypes = [i32, i64, i64, i64, p, p, p, p, e, p, sz, p]
     L.ptg_ikbo_attention.argtypes = [i64, i64, i64, i64, i64, ctypes.c_float, p, p, p, p, p, e, p]
     L.ptg_grouped_gemm_wgrad_workspace.argtypes = []
@@ -81,7 +85,7 @@ def open_library(path: str):
     L.ptg_broadcast_gemm.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, e, p, e, p, e, p, sz, p]
     L.ptg_broadcast_gemm_check.argtypes = [i64, i64, p, p]
     L.ptg_broadcast_gemm_noalloc.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, e, p, e, p, e, p]
-    for f in (L.ptg_gemm, L.ptg_grouped_gemm, L.ptg_grouped_gemm_check, L.ptg_grouped_gemm_wgrad, L.ptg_ikbo_attention,
+    for f in (L.ptg_gemm, L.ptg_grouped_gemm, L.ptg_grouped_gemm_split, L.ptg_grouped_gemm_check, L.ptg_grouped_gemm_wgrad, L.ptg_ikbo_attention,
               L.ptg_grouped_gemm_ptr_array, L.ptg_grouped_gemm_ptr_array_prepare,
               L.ptg_grouped_gemm_ptr_array_run, L.ptg_broadcast_gemm, L.ptg_broadcast_gemm_noalloc,
               L.ptg_broadcast_gemm_check):

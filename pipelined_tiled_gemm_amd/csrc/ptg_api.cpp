@@ -8,6 +8,7 @@
 #include <cstring>
 #include <exception>
 #include <algorithm>
+#include <atomic>
 #include <memory>
 #include <mutex>
 #include <vector>
@@ -148,12 +149,24 @@ ptg_status ptg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
   })
 }
 
-ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, const void* X,
-                            const void* W, ptg_layout w_layout, const int32_t* group_offsets,
-                            void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+std::atomic<uint32_t> g_epoch{0};
+
+// A value that no earlier launch of this process used (skipping 0, the value of zeroed memory).
+uint32_t next_epoch() {
+  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
+ptg_status grouped_call(const char* fn, int32_t G, int64_t M_total, int64_t N, int64_t K, const void* X,
+                        const void* W, ptg_layout w_layout, const int32_t* group_offsets, void* Y,
+                        ptg_dtype y_dtype, const float* bias, ptg_epilogue epi, void* workspace, size_t ws_bytes,
+                        bool with_ws, void* stream) {
   PTG_TRY({
-    const char* fn = "ptg_grouped_gemm";
     if (G <= 0) return fail(PTG_ERR_INVALID_ARG, "%s: G must be positive", fn);
     if (G > ptg::kMaxGroups) return fail(PTG_ERR_UNSUPPORTED, "%s: G exceeds %d", fn, ptg::kMaxGroups);
     ptg_status st = check_mnk(fn, M_total, N, K);
@@ -173,6 +186,16 @@ ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, co
         !out_fits(N, y_dtype == PTG_F32 ? 4 : 2))
       return fail(PTG_ERR_UNSUPPORTED, "%s: operand or output tile exceeds 2 GiB of addressing", fn);
     ptg::GroupedLaunch g{};
+    if (with_ws) {
+      if (!workspace) return fail(PTG_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+      if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
+      const size_t need = ptg::grouped_split_workspace_bytes(ptg::device_compute_units());
+      if (ws_bytes < need)
+        return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+      g.workspace = workspace;
+      g.ws_bytes = ws_bytes;
+      g.epoch = next_epoch();
+    }
     g.X = X; g.W = W; g.Y = Y; g.bias = needs_bias(epi) ? bias : nullptr; g.offsets = group_offsets;
     g.M_total = M_total; g.N = N; g.K = K; g.G = G;
     g.b_kn = kn; g.epi = epi; g.out_f32 = y_dtype == PTG_F32;
@@ -180,6 +203,31 @@ ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, co
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
   })
+}
+
+}  // namespace
+
+extern "C" {
+
+ptg_status ptg_grouped_gemm(int32_t G, int64_t M_total, int64_t N, int64_t K, const void* X,
+                            const void* W, ptg_layout w_layout, const int32_t* group_offsets,
+                            void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                            void* stream) {
+  return grouped_call("ptg_grouped_gemm", G, M_total, N, K, X, W, w_layout, group_offsets, Y, y_dtype, bias, epi,
+                      nullptr, 0, false, stream);
+}
+
+size_t ptg_grouped_gemm_split_workspace(void) {
+  const int cus = ptg::device_compute_units();
+  return cus > 0 ? ptg::grouped_split_workspace_bytes(cus) : 0;
+}
+
+ptg_status ptg_grouped_gemm_split(int32_t G, int64_t M_total, int64_t N, int64_t K, const void* X,
+                                  const void* W, ptg_layout w_layout, const int32_t* group_offsets,
+                                  void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  return grouped_call("ptg_grouped_gemm_split", G, M_total, N, K, X, W, w_layout, group_offsets, Y, y_dtype, bias,
+                      epi, workspace, ws_bytes, true, stream);
 }
 
 size_t ptg_grouped_gemm_wgrad_workspace(void) { return ptg::kWgradWorkspace; }

@@ -190,8 +190,16 @@ struct TileInfo {            // 16 dwords
   uint64_t P;                // address of P[0][n0] (broadcast gather) or 0
   int32_t ldp;               // row stride of P in elements
   uint32_t p_bytes;          // bytes of P from P[0][n0] on (bounds of the gather)
+  // Reduction split (grouped GEMM, last round): 0 for a whole tile; 1 or 2 for the unit that
+  // reduces the first or second part of k of a tile split in two.  The two units' fp32
+  // partial sums meet in the workspace (combine_split16).
+  uint32_t mode;
+  uint32_t epoch;            // the launch's epoch: sync words left by other launches never match
+  uint64_t part;             // workspace: the tile's partial image (32 KB per consumer wave)
+  uint64_t sync;             // workspace: per consumer wave, a 64-bit arrival word, then a 32-bit ready word
+  uint64_t pad;
 };
-static_assert(sizeof(TileInfo) == 64, "TileInfo is 16 dwords");
+static_assert(sizeof(TileInfo) == 96, "TileInfo is 24 dwords");
 
 // Tags of a metadata slot.  The consumer checks the tag of the slot it expects before it
 // uses any address from it: a slot that is not exactly what the producer published stops
@@ -989,6 +997,10 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
       continue;
     }
 
+    if (uni(ti->mode) != 0) {  // split tiles are served by the 16x16 consumer only
+      raise_abort(abort, 2u);
+      break;
+    }
     f32x16 acc[C::TM][C::TN];
     if (!init_acc<C>(acc, ti, guards, epi, wm, wn, abort)) break;
 
@@ -1107,6 +1119,9 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
   for (int tm = 0; tm < C::TM16; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN16; ++tn) acc[tm][tn] = f32x4{};
+  // the second unit of a split tile adds its partial sum to the first's, which carries the
+  // start value
+  if (uni(ti->mode) == 2) return true;
   const uint64_t biasp = uni64(ti->bias);
   const uint64_t gidxp = uni64(ti->gidx);
   const bool gather = gidxp != 0;
@@ -1301,6 +1316,94 @@ __device__ __forceinline__ void epilogue16(f32x4 (&acc)[C::TM16][C::TN16], int w
   }
 }
 
+// Combine of a tile whose reduction is split between two units on two workgroups (mode 1:
+// the first part of k, mode 2: the rest).  Each consumer wave meets the wave with the same
+// sub-tile in the other unit through its own sync words in the workspace:
+//   - a 64-bit arrival word: the launch's epoch in the high half, the arrivals of this epoch
+//     in the low half (a word from another launch counts as no arrival, so the workspace
+//     needs no clearing between launches);
+//   - a 32-bit ready word: the epoch, published by the first unit to arrive.
+// The first to arrive writes its fp32 accumulators as a register image (block b of lane l at
+// byte 16 (64 b + l) of its 32 KB) and publishes the epoch; the second waits for it, adds the
+// image to its own accumulators and runs the epilogue.  The other unit may run on another
+// XCD, behind another L2, so the image and the sync words go through the agent-coherent path
+// (the sc1 cache policy, which agent-scope atomic loads and stores use): the image stores
+// have completed (s_waitcnt) before the ready word is written, and the image is read only
+// after the ready word has been seen.  No L2 write-back or invalidation is needed, which
+// would also drop the other workgroups' cached operands on that XCD.  A sum of two terms
+// does not depend on their order, so the result does not depend on which unit arrives first.
+// Returns true when this wave holds the combined sub-tile (false: its part is handed over, or
+// the workgroup aborted).
+template <class C>
+__device__ __forceinline__ bool combine_split16(f32x4 (&acc)[C::TM16][C::TN16], const TileInfo* ti, int w,
+                                                const Guards* guards, uint32_t* abort) {
+  constexpr int kImage = C::TM16 * C::TN16 * 64 * 16;  // bytes of one wave's register image
+  static_assert(C::NCG * kImage <= (int)kSplitImageBytes && C::NCG * 12 <= (int)kSplitSyncBytes,
+                "split workspace blocks");
+  const uint32_t epoch = uni(ti->epoch);
+  const uint64_t syncp = uni64(ti->sync), partp = uni64(ti->part);
+  if (!inside(syncp, kSplitSyncBytes, uni64(guards->w_lo), uni64(guards->w_hi)) ||
+      !inside(partp, kSplitImageBytes, uni64(guards->w_lo), uni64(guards->w_hi))) {
+    raise_abort(abort, 8u);
+    return false;
+  }
+  constexpr int kSc1 = 16;  // cache policy: agent-coherent
+  uint64_t* arrive = reinterpret_cast<uint64_t*>(syncp) + w;
+  uint32_t* ready = reinterpret_cast<uint32_t*>(syncp + 8 * C::NCG) + w;
+  const __amdgpu_buffer_rsrc_t rimg = make_rsrc(reinterpret_cast<void*>(partp + (uint64_t)w * kImage), kImage);
+  const int lane = opaque_lane();
+  uint32_t first = 0;
+  if (lane == 0) {
+    uint64_t old = __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+      const uint64_t nw = ((uint32_t)(old >> 32) == epoch) ? old + 1 : (((uint64_t)epoch << 32) | 1u);
+      if (__hip_atomic_compare_exchange_strong(arrive, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    first = ((uint32_t)(old >> 32) != epoch || (uint32_t)old == 0) ? 1u : 0u;
+  }
+  first = uni(first);  // lane 0's value
+  if (first) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+#pragma unroll
+    for (int tm = 0; tm < C::TM16; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::TN16; ++tn) {
+        const f32x4 blk = acc[tm][tn];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, blk), rimg,
+                                               (uint32_t)((tm * C::TN16 + tn) * 64 + lane) * 16u, 0, kSc1);
+      }
+    wait_vmcnt<0>();
+    if (lane == 0) __hip_atomic_store(ready, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  uint32_t ok = 1;
+  if (lane == 0) {
+    uint32_t polls = 0;
+    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      __builtin_amdgcn_s_sleep(2);
+      if ((++polls & 63) == 0) {
+        if (lds_peek(abort) != 0 || polls >= kSpinLimit) {
+          ok = 0;
+          break;
+        }
+      }
+    }
+  }
+  if (uni(ok) == 0) {
+    raise_abort(abort, 1u);
+    return false;
+  }
+#pragma unroll
+  for (int tm = 0; tm < C::TM16; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN16; ++tn)
+      acc[tm][tn] += __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rimg, (uint32_t)((tm * C::TN16 + tn) * 64 + lane) * 16u, 0, kSc1));
+  return true;
+}
+
 // The consumer loop.  Per 32-deep k-slice: 2 halves of TM16/2 row blocks.  The first half
 // runs row-major: a row block's fragment is refilled with the second half's fragment right
 // after its last MFMA.  The second half runs column-major: each B fragment is refilled with
@@ -1462,6 +1565,12 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    }
+
+    // a split tile: the unit that arrives second finishes it
+    if (uni(ti->mode) != 0 && !combine_split16<C>(acc, ti, cw % C::NCG, guards, abort)) {
+      if (uni(lds_peek(abort)) != 0) break;
+      continue;
     }
 
     const int m_rows = (int)uni((uint32_t)ti->m_rows);

@@ -176,6 +176,12 @@ __device__ __forceinline__ int upper_index(const int32_t* pre, int n, int64_t x)
 // load the X rows twice, and measured slower.  Every output element keeps its k-sequence, so
 // results do not change.  The tile count is known only on the device, so each workgroup works
 // this out from the prefix sums.
+//
+// With a workspace, a last round of at most half the workgroups instead runs every tile as
+// two units: full tiles by columns as above, the others (a group's last, partial tile) by
+// reduction, each unit taking half of the k-steps, their fp32 partial sums combined in the
+// workspace by whichever unit finishes second (combine_split16).  Such a tile's sums then
+// run in two parts, so its bits may differ from the unsplit tile's (same tolerance).
 struct GroupedSched {
   struct Args {
     const __bf16* X;
@@ -183,6 +189,9 @@ struct GroupedSched {
     char* Y;
     const float* bias;
     const int32_t* offsets;
+    char* split_sync;      // workspace of the reduction split (null: none)
+    char* split_images;
+    uint32_t epoch;
     int64_t M_total;
     int32_t G, N, K, tiles_n, group_m;
     int32_t epi, out_f32, out_bytes;
@@ -190,9 +199,10 @@ struct GroupedSched {
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
   // offsets[G + 1], full-tile prefix[G + 1], half-tile prefix[G + 1], scan scratch, then the
-  // first tile of the last round and the number of its full tiles that are split by columns
+  // first tile of the last round, the number of its full tiles that are split by columns,
+  // and whether its other tiles are split by reduction
   static constexpr int kScratchInts = 20;
-  static constexpr int LDS_BYTES = 3 * (kMaxGroups + 1) * 4 + kScratchInts * 4 + 2 * 4;
+  static constexpr int LDS_BYTES = 3 * (kMaxGroups + 1) * 4 + kScratchInts * 4 + 3 * 4;
   static constexpr bool kDynamic = false;
 
   // full (more than BM/2 valid rows) and half m-tiles of a group of cnt rows
@@ -231,9 +241,14 @@ struct GroupedSched {
       const int64_t grid = gridDim.x;
       const int64_t last = (T / grid) * grid, rem = T - last;  // the last round's tiles
       const int64_t nf = n_full > last ? min(rem, n_full - last) : 0;  // its full tiles
-      const bool split = nf > 0 && rem + nf <= grid && a.N % C::BN == 0 && C::BN % 128 == 0;
+      const bool by_cols = a.N % C::BN == 0 && C::BN % 128 == 0;
+      // every tile of the last round as two units (columns or reduction): needs the workspace,
+      // at most one unit per workgroup, and at least two k-steps per tile
+      const bool ksplit = a.split_sync != nullptr && rem > 0 && 2 * rem <= grid && a.K > C::BK;
+      const bool split = ksplit || (nf > 0 && rem + nf <= grid && by_cols);
       scratch[kScratchInts] = (int32_t)(split ? last : T);
-      scratch[kScratchInts + 1] = (int32_t)(split ? nf : 0);
+      scratch[kScratchInts + 1] = (int32_t)(split && by_cols ? nf : 0);
+      scratch[kScratchInts + 2] = ksplit ? 1 : 0;
     }
   }
 
@@ -244,10 +259,22 @@ struct GroupedSched {
     const int32_t* pre_half = pre_full + kMaxGroups + 1;
     const int64_t split_from = (pre_half + kMaxGroups + 1)[kScratchInts];
     const int64_t split_nf = (pre_half + kMaxGroups + 1)[kScratchInts + 1];
+    const bool ksplit = (pre_half + kMaxGroups + 1)[kScratchInts + 2] != 0;
     const int r = (int)xcd_rank(blockIdx.x, gridDim.x);
     int64_t L = (int64_t)j * gridDim.x + ((j & 1) ? (int64_t)gridDim.x - 1 - r : r);
-    int part = -1;  // column half of a split tile
-    if (split_nf > 0 && L >= split_from) {
+    int part = -1;   // column half of a split tile
+    int khalf = -1;  // reduction half of a split tile
+    int64_t slot = 0;
+    if (ksplit && L >= split_from) {
+      // units 2 t and 2 t + 1 are the halves of the round's tile t: by columns for its first
+      // split_nf tiles (full ones), by reduction for the others; past the last tile there is
+      // no unit (below)
+      const int64_t u = L - split_from;
+      slot = u / 2;
+      L = split_from + slot;
+      if (slot < split_nf) part = (int)(u & 1);
+      else khalf = (int)(u & 1);
+    } else if (split_nf > 0 && L >= split_from) {
       // units 0 .. 2 nf - 1 are the halves of the round's full tiles, then its half tiles;
       // past the last tile there is no unit (below)
       const int64_t u = L - split_from;
@@ -281,12 +308,22 @@ struct GroupedSched {
     const int64_t m0 = (int64_t)row0 + (int64_t)mt * C::BM;
     const int64_t n0 = (int64_t)nt * C::BN + (part > 0 ? C::BN / 2 : 0);
     const int64_t wsize = (int64_t)a.K * a.N;
-    t.A = a.X + m0 * a.K;
+    // a reduction half: the first unit takes the first half of the k-steps (rounded down)
+    const int64_t k_mid = (int64_t)(tile_steps<C>(a.K) / 2) * C::BK;
+    const int64_t k0 = khalf > 0 ? k_mid : 0;
+    const int64_t kl = khalf < 0 ? a.K : (khalf == 0 ? k_mid : a.K - k_mid);
+    t.A = a.X + m0 * a.K + k0;
     t.lda = a.K;
-    t.B = a.W + g * wsize + (C::B_KN ? n0 : n0 * a.K);
+    t.B = a.W + g * wsize + (C::B_KN ? k0 * a.N + n0 : n0 * a.K + k0);
     t.ldb = C::B_KN ? a.N : a.K;
     t.info.tag = 0;  // set by the producer when it publishes the slot
-    t.info.K = a.K;
+    t.info.K = (int)kl;
+    if (khalf >= 0) {
+      t.info.mode = (uint32_t)(khalf + 1);
+      t.info.epoch = a.epoch;
+      t.info.sync = (uint64_t)(a.split_sync + slot * kSplitSyncBytes);
+      t.info.part = (uint64_t)(a.split_images + slot * kSplitImageBytes);
+    }
     t.info.m_rows = min(C::BM, cnt - mt * C::BM);
     t.info.n_cols = (int)min((int64_t)(part >= 0 ? C::BN / 2 : C::BN), (int64_t)a.N - n0);
     t.info.C = (uint64_t)(a.Y + (m0 * a.N + n0) * a.out_bytes);
@@ -545,6 +582,8 @@ static int device_cus() {
   return cache[dev];
 }
 
+int device_compute_units() { return device_cus(); }
+
 static uint64_t addr(const void* p) { return reinterpret_cast<uint64_t>(p); }
 
 // [p, p + bytes), or the empty range [0, 0) when p is null.
@@ -697,8 +736,17 @@ static hipError_t launch_grouped_cfg(const GroupedLaunch& g, hipStream_t stream)
   a.tiles_n = (int32_t)((g.N + C::BN - 1) / C::BN);
   a.group_m = kGroupedBandM;
   a.epi = g.epi; a.out_f32 = g.out_f32; a.out_bytes = g.out_f32 ? 4 : 2;
+  a.split_sync = nullptr;
+  a.split_images = nullptr;
+  a.epoch = g.epoch;
   Guards& gd = a.guard;
   gd = Guards{};
+  const int cus = device_cus();
+  if (g.workspace && g.ws_bytes >= grouped_split_workspace_bytes(cus)) {
+    a.split_sync = reinterpret_cast<char*>(g.workspace);
+    a.split_images = a.split_sync + grouped_split_sync_bytes(cus);
+    span(g.workspace, grouped_split_workspace_bytes(cus), gd.w_lo, gd.w_hi);
+  }
   span(g.X, (uint64_t)g.M_total * g.K * 2, gd.a_lo, gd.a_hi);
   span(g.W, (uint64_t)g.G * g.K * g.N * 2, gd.b_lo, gd.b_hi);
   span(g.Y, (uint64_t)g.M_total * g.N * a.out_bytes, gd.c_lo, gd.c_hi);

@@ -36,7 +36,25 @@ struct GroupedLaunch {
   int64_t M_total, N, K;
   int32_t G;
   int b_kn, epi, out_f32;
+  // Optional workspace (grouped_split_workspace_bytes) for the reduction split of the last
+  // round's tiles; null: no reduction split.  `epoch` is unique per launch.
+  void* workspace = nullptr;
+  size_t ws_bytes = 0;
+  uint32_t epoch = 0;
 };
+// Workspace of the grouped GEMM's reduction split on a device with `cus` compute units:
+// per split tile (at most cus / 2 of them) a 128-byte block of sync words and a 256 KB image
+// of the partial accumulators (one 32 KB register image per consumer wave).
+constexpr size_t kSplitSyncBytes = 128;
+constexpr size_t kSplitImageBytes = 256 * 256 * 4;
+inline size_t grouped_split_slots(int cus) { return (size_t)(cus > 1 ? cus / 2 : 1); }
+inline size_t grouped_split_sync_bytes(int cus) {
+  return (grouped_split_slots(cus) * kSplitSyncBytes + 4095) / 4096 * 4096;
+}
+inline size_t grouped_split_workspace_bytes(int cus) {
+  return grouped_split_sync_bytes(cus) + grouped_split_slots(cus) * kSplitImageBytes;
+}
+int device_compute_units();
 
 // Weight gradient of the grouped GEMM: dW[g] = X_g^T . dY_g over group g's rows.
 struct WgradLaunch {
@@ -69,6 +87,7 @@ struct Guards {
   uint64_t a_lo, a_hi, b_lo, b_hi;      // DMA sources
   uint64_t c_lo, c_hi;                  // output
   uint64_t bias_lo, bias_hi, gidx_lo, gidx_hi, p_lo, p_hi;  // epilogue operands
+  uint64_t w_lo, w_hi;                  // workspace of a split reduction (images, sync words)
 };
 
 // Workspace layout of a batch: [header 256 B][prefix int32 (count + 1), padded to 256 B][problems].
@@ -81,7 +100,7 @@ struct BatchHeader {
   int32_t out_f32;              // output element type the table was written for (C ranges)
   int32_t reserved0;
   Guards guard;                 // union of the problems' operand ranges
-  int32_t reserved[32];
+  int32_t reserved[28];
 };
 static_assert(sizeof(BatchHeader) == 256, "BatchHeader layout");
 constexpr int32_t kBatchMagic = 0x50544742;  // "PTGB"

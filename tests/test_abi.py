@@ -276,3 +276,14 @@ def test_broadcast_noalloc_validation(L):
     assert L.ptg_broadcast_gemm_workspace(U, N) > 16 << 20
     assert b(U=U, N=N) == UNSUPPORTED
     assert "16777216" in L.ptg_last_error().decode()
+
+
+def test_grouped_split_validation(L):
+    def g(G=4, M=64, N=64, K=64, X=P, W=P, layout=0, off=P, Y=P, dtype=0, bias=None, epi=0, ws=P, wsb=1 << 30):
+        return L.ptg_grouped_gemm_split(G, M, N, K, X, W, layout, off, Y, dtype, bias, epi, ws, wsb, None)
+    assert g(G=0) == INVALID
+    assert g(K=0) == UNSUPPORTED
+    assert g(off=None) == INVALID
+    assert g(ws=None) == WORKSPACE
+    assert g(ws=P + 8) == UNSUPPORTED
+    assert g(M=0, X=None, W=None, Y=None, off=None, ws=None) == OK

@@ -171,3 +171,84 @@ def test_config3_moe_sampled(reading):
     for out_dtype in (torch.bfloat16, torch.float32):
         out = ptg.grouped_gemm(X, W, off, out_dtype=out_dtype)
         check(out[idx], v, w.K, f"config3 {reading} {out_dtype}")
+
+
+# ------------------------------------------------------------------------------------------
+# reduction split of the last round (ptg_grouped_gemm_split)
+# ------------------------------------------------------------------------------------------
+def split_workspace(garbage=True):
+    ws = torch.empty(ptg.grouped_gemm_split_workspace(), dtype=torch.uint8, device="cuda")
+    if garbage:
+        ws.random_(0, 256)     # its content on entry does not matter
+    return ws
+
+
+def offsets_of(counts):
+    off = np.zeros(len(counts) + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    return off
+
+
+@pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_grouped_split_reduction_of_half_tiles(layout, out_dtype):
+    """32 experts of 300 rows between empty ones, K = 512, N = 1536: on an MI355X 192 full and
+    192 half tiles, so the last round's 128 half tiles run as 256 reduction halves, combined in
+    a workspace filled with random bytes.  Integer data (every partial sum exact): bit-exact
+    against the oracle, guard rows untouched; a second call on the same workspace too."""
+    counts = np.array([300, 0] * 16 + [0, 300] * 16)
+    G, K, N = len(counts), 512, 1536
+    M = int(counts.sum())
+    rng = np.random.default_rng(21 + layout)
+    X = int_bf16(rng, (M, K))
+    W = int_bf16(rng, (G, K, N) if layout == wl.B_KN else (G, N, K))
+    off = offsets_of(counts)
+    v = oracle.grouped_gemm(X, W, layout, off)
+    ws = split_workspace()
+    dX, dW, doff = dev_bf16(X), dev_bf16(W), dev(off)
+    for call in range(2):
+        buf = torch.full((M + 2, N), float("nan"), dtype=out_dtype, device="cuda")
+        out = buf[1:M + 1]
+        ptg.grouped_gemm(dX, dW, doff, w_layout=layout, out=out, workspace=ws)
+        exact(out, v, f"split half tiles layout={layout} call {call}")
+        assert bool(torch.isnan(buf[0].float()).all()) and bool(torch.isnan(buf[M + 1].float()).all())
+
+
+def test_grouped_split_reduction_of_full_tiles_and_bias():
+    """N = 1288 (not a multiple of the tile width, so no column split): one expert of 50 full
+    m-tiles gives 300 tiles, and the last round's 44 full tiles run as reduction halves; the
+    bias + SiLU epilogue runs once, on the combined sum.  Against the oracle, fp32 output."""
+    counts = np.array([50 * 256, 0, 0])
+    G, K, N = len(counts), 256, 1288
+    w = wl.grouped(22, G, int(counts.sum()), K, N, with_bias=True, counts=counts)
+    out = ptg.grouped_gemm(dev_bf16(w.X), dev_bf16(w.W), dev(w.offsets), out_dtype=torch.float32,
+                           bias=dev(w.bias), epi=wl.EPI_BIAS_SILU, workspace=split_workspace())
+    v = oracle.grouped_gemm(w.X, w.W, w.w_layout, w.offsets, w.bias, wl.EPI_BIAS_SILU)
+    check(out, v, K, "split full tiles, bias + silu")
+
+
+@pytest.mark.parametrize("reading", ["rank", "sampled"])
+def test_config3_moe_split(reading):
+    """The MoE workload through ptg_grouped_gemm_split, on sampled rows (first and last row of
+    every live expert).  Rank-Zipf routing ends on 106 half tiles that run as reduction halves:
+    within tolerance, and not bit-identical to the unsplit launch (the halves really ran
+    separately).  Zipf-sampled routing ends on full tiles, split by columns only: bit-identical
+    to the unsplit launch."""
+    w = wl.config3(reading)
+    rows = set(sample_rows(w.M_total, 64, 8).tolist())
+    for g in range(w.G):
+        if w.counts[g] > 0:
+            rows |= {int(w.offsets[g]), int(w.offsets[g + 1]) - 1}
+    rows = np.array(sorted(rows), dtype=np.int64)
+    v = oracle.grouped_gemm(w.X, w.W, w.w_layout, w.offsets, rows=rows)
+    X, W, off = dev_bf16(w.X), dev_bf16(w.W), dev(w.offsets)
+    idx = torch.from_numpy(rows).cuda()
+    ws = split_workspace()
+    for out_dtype in (torch.bfloat16, torch.float32):
+        out = ptg.grouped_gemm(X, W, off, out_dtype=out_dtype, workspace=ws)
+        check(out[idx], v, w.K, f"config3 split {reading} {out_dtype}")
+    plain = ptg.grouped_gemm(X, W, off, out_dtype=torch.float32)
+    if reading == "rank":
+        assert not torch.equal(out, plain)
+    else:
+        assert torch.equal(out, plain)

@@ -139,3 +139,21 @@ def test_stress_ptr_array(delay_lib):
         ptg.grouped_gemm_ptr_array(probs, wl.EPI_NONE)
     for i, ((A, B), p) in enumerate(zip(host, probs)):
         exact(p[2], oracle.gemm(A, B, wl.B_KN), f"stress batch problem {i}")
+
+
+def test_stress_grouped_split_reduction(delay_lib):
+    """The last round's half tiles as reduction halves (ptg_grouped_gemm_split): under the pauses
+    either half may finish first; the combined sums stay bit-exact on integer data."""
+    counts = np.array([300, 0] * 16 + [0, 300] * 16)
+    G, K, N = len(counts), 512, 1536
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rng = np.random.default_rng(15)
+    X = int_bf16(rng, (int(off[-1]), K))
+    W = int_bf16(rng, (G, K, N))
+    v = oracle.grouped_gemm(X, W, wl.B_KN, off)
+    with using(delay_lib):
+        ws = torch.empty(ptg.grouped_gemm_split_workspace(), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            Y = torch.full((int(off[-1]), N), float("nan"), dtype=torch.float32, device="cuda")
+            ptg.grouped_gemm(dev_bf16(X), dev_bf16(W), dev(off), out=Y, workspace=ws)
+            exact(Y, v, "stress grouped split")
