@@ -272,6 +272,37 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
                               void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * ptg_broadcast_gemm_fused - ptg_broadcast_gemm as one persistent launch: the final form of the
+ * linear compression in "How We Built TLX", Case Study 2, subsection "TLX Provides a Building
+ * Block for the Final Stage of This Optimization", where the user and candidate products share
+ * one pipeline instead of draining it between launches, with tile-level release and acquire
+ * between workgroups.  Same arguments and results as ptg_broadcast_gemm (P summed over a
+ * different number of slices: fp32 rounding may differ in the last bits); the workspace is
+ * DEVICE scratch of at least ptg_broadcast_gemm_fused_workspace(U, N) bytes (16-byte aligned).
+ * The launch runs, from one ticket counter, user units (slice s of Ku for one 256-column block,
+ * each about half a candidate tile's k-steps; the fp32 partial product goes to the workspace and
+ * each consumer wave then publishes this call's epoch in its arrival flag), reduction units
+ * (the producer waves wait for every flag of their column block, sum the slices in order, add
+ * the bias, write rows of P and count themselves into the block's ready word), then each
+ * workgroup's candidate tiles in a fixed XCD-aware order (published to the consumers once their
+ * column block's ready word is complete; the accumulators start from P).  Sync words carry the call's epoch (from a
+ * process-wide counter), so the workspace needs no clearing between calls; calls that share
+ * one workspace must not overlap.  Every wait is bounded (see ptg_watchdog).
+ * Errors: as ptg_broadcast_gemm; PTG_ERR_UNSUPPORTED also unless U <= 256, Ku > 64 (two
+ * 64-deep slices), N <= 130816 (the sync words' 4 KB block) and the workspace is under 2 GiB.
+ * Measured on MI355X (64 users, 81,403 candidates, [2048 | 512] -> 1024, bf16): slower than
+ * ptg_broadcast_gemm, because the candidates cannot start before P is complete (P is their
+ * accumulators' start value).
+ */
+size_t ptg_broadcast_gemm_fused_workspace(int64_t U, int64_t N);
+ptg_status ptg_broadcast_gemm_fused(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N,
+                                    const void* Xu, const void* Xc, const int32_t* user_idx,
+                                    const void* W, ptg_layout w_layout,
+                                    void* Y, ptg_dtype y_dtype,
+                                    const float* bias, ptg_epilogue epi,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * ptg_broadcast_gemm_noalloc - ptg_broadcast_gemm for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments, results and errors as ptg_broadcast_gemm, without the workspace: P and the

@@ -23,6 +23,7 @@ __all__ = [
     "gemm", "grouped_gemm", "grouped_gemm_split_workspace", "grouped_gemm_check", "grouped_gemm_wgrad", "grouped_gemm_wgrad_workspace", "ikbo_attention",
     "grouped_gemm_ptr_array_workspace", "grouped_gemm_ptr_array", "grouped_gemm_ptr_array_prepare",
     "grouped_gemm_ptr_array_run", "broadcast_gemm_workspace", "broadcast_gemm", "broadcast_gemm_noalloc",
+    "broadcast_gemm_fused_workspace", "broadcast_gemm_fused",
     "broadcast_gemm_check", "watchdog", "version", "describe_config", "status_string",
     "last_error", "library_path",
 ]
@@ -374,6 +375,26 @@ def broadcast_gemm(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W
                                 device=Xc.device)
     _check(_lib().ptg_broadcast_gemm(*args, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+    return out
+
+
+def broadcast_gemm_fused_workspace(U: int, N: int) -> int:
+    return int(_lib().ptg_broadcast_gemm_fused_workspace(U, N))
+
+
+def broadcast_gemm_fused(Xu: torch.Tensor, Xc: torch.Tensor, user_idx: torch.Tensor, W: torch.Tensor, *,
+                         w_layout: int = B_KN, out: Optional[torch.Tensor] = None,
+                         out_dtype: torch.dtype = torch.bfloat16, bias: Optional[torch.Tensor] = None,
+                         epi: int = EPI_NONE, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """broadcast_gemm as one persistent launch (user units, reduction units, candidate tiles)."""
+    args, out = _broadcast_args(Xu, Xc, user_idx, W, w_layout, out, out_dtype, bias, epi)
+    U, N = args[0], args[4]
+    if workspace is None:
+        workspace = torch.empty(max(broadcast_gemm_fused_workspace(U, N), 16), dtype=torch.uint8,
+                                device=Xc.device)
+    _check(_lib().ptg_broadcast_gemm_fused(*args, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)))
     return out
 
 

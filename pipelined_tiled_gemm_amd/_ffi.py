@@ -28,6 +28,7 @@ EXPORTS = (
     "ptg_grouped_gemm_ptr_array_workspace", "ptg_grouped_gemm_ptr_array",
     "ptg_grouped_gemm_ptr_array_prepare", "ptg_grouped_gemm_ptr_array_run",
     "ptg_broadcast_gemm_workspace", "ptg_broadcast_gemm", "ptg_broadcast_gemm_noalloc",
+    "ptg_broadcast_gemm_fused_workspace", "ptg_broadcast_gemm_fused",
     "ptg_broadcast_gemm_check",
     "ptg_status_string", "ptg_last_error", "ptg_watchdog", "ptg_version", "ptg_describe_config",
 )
@@ -85,9 +86,13 @@ def open_library(path: str):
     L.ptg_broadcast_gemm.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, e, p, e, p, e, p, sz, p]
     L.ptg_broadcast_gemm_check.argtypes = [i64, i64, p, p]
     L.ptg_broadcast_gemm_noalloc.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, e, p, e, p, e, p]
+    L.ptg_broadcast_gemm_fused_workspace.argtypes = [i64, i64]
+    L.ptg_broadcast_gemm_fused_workspace.restype = sz
+    L.ptg_broadcast_gemm_fused.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, e, p, e, p, e, p, sz, p]
     for f in (L.ptg_gemm, L.ptg_grouped_gemm, L.ptg_grouped_gemm_split, L.ptg_grouped_gemm_check, L.ptg_grouped_gemm_wgrad, L.ptg_ikbo_attention,
               L.ptg_grouped_gemm_ptr_array, L.ptg_grouped_gemm_ptr_array_prepare,
               L.ptg_grouped_gemm_ptr_array_run, L.ptg_broadcast_gemm, L.ptg_broadcast_gemm_noalloc,
+              L.ptg_broadcast_gemm_fused,
               L.ptg_broadcast_gemm_check):
         f.restype = e
     L.ptg_status_string.argtypes = [e]

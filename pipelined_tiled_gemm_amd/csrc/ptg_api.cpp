@@ -555,17 +555,24 @@ size_t ptg_broadcast_gemm_workspace(int64_t U, int64_t N) {
   return (size_t)U * (size_t)N * sizeof(float) * (splits > 1 ? 1 + (size_t)splits : 1);
 }
 
+size_t ptg_broadcast_gemm_fused_workspace(int64_t U, int64_t N) {
+  if (U <= 0 || N <= 0) return 0;
+  // the sync words, P, then up to 32 partial products
+  return ptg::broadcast_sync_bytes(N, ptg::kBroadcastMaxSlices) +
+         (size_t)U * (size_t)N * sizeof(float) * (1 + (size_t)ptg::kBroadcastMaxSlices);
+}
+
 }  // extern "C"
 
 namespace {
-// The broadcast GEMM behind both entry points.  `scratch(need, &ws, &bytes)` supplies the
+// The broadcast GEMM behind the entry points.  `scratch(need, &ws, &bytes)` supplies the
 // workspace once every host-checkable argument has passed (the caller's, or the library's
-// static array), or returns an error status.
+// static array), or returns an error status.  `fused`: one persistent launch.
 template <class Scratch>
 ptg_status broadcast_call(const char* fn, int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
                           const void* Xc, const int32_t* user_idx, const void* W, ptg_layout w_layout,
                           void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
-                          Scratch scratch, void* stream) {
+                          Scratch scratch, void* stream, bool fused = false) {
   PTG_TRY({
     ptg_status st = PTG_OK;
     if (U <= 0 || Mc < 0 || Ku < 0 || Kc < 0 || N < 0)
@@ -590,15 +597,46 @@ ptg_status broadcast_call(const char* fn, int64_t U, int64_t Mc, int64_t Ku, int
       return fail(PTG_ERR_UNSUPPORTED, "%s: operand or output tile exceeds 2 GiB of addressing", fn);
     if (U * N * 4 >= ((int64_t)1 << 31))
       return fail(PTG_ERR_UNSUPPORTED, "%s: P (U x N fp32) exceeds 2 GiB of addressing", fn);
+    // the one-launch form: at most 256 users (one m-tile), at least two 64-deep slices of Ku,
+    // the sync words of every column block in their 4 KB block, and a workspace under 2 GiB
+    // (its reduction units address it with 31-bit offsets)
+    const int64_t max_splits1 = ptg::kBroadcastMaxSlices;
+    const int64_t unit_steps = std::max<int64_t>(1, (Kc + 63) / 64 / 2);
+    int64_t chunk1 = std::min<int64_t>(unit_steps * 64, (Ku + 127) / 128 * 64);
+    if ((Ku + chunk1 - 1) / chunk1 > max_splits1) chunk1 = ((Ku + max_splits1 - 1) / max_splits1 + 63) / 64 * 64;
+    const int32_t splits1 = (int32_t)((Ku + chunk1 - 1) / chunk1);
+    if (fused && (!ptg::broadcast_single_launch_fits(U, N, splits1) ||
+                  ptg_broadcast_gemm_fused_workspace(U, N) >= ((size_t)1 << 31)))
+      return fail(PTG_ERR_UNSUPPORTED,
+                  "%s: one launch needs U <= 256, Ku > 64, N <= %lld and a workspace under 2 GiB", fn,
+                  (long long)((ptg::broadcast_flags_offset() / 8 - 1) * 256));
     void* workspace = nullptr;
     size_t ws_bytes = 0;
-    const size_t need = ptg_broadcast_gemm_workspace(U, N);
+    const size_t need = fused ? ptg_broadcast_gemm_fused_workspace(U, N) : ptg_broadcast_gemm_workspace(U, N);
     st = scratch(need, &workspace, &ws_bytes);
     if (st) return st;
     if (!workspace || ws_bytes < need)
       return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (fused) {
+      // User units (slice s of Ku for one 256-column block, its fp32 partial product to the
+      // workspace), reduction units (rows of P summed from the partials once all have
+      // arrived) and candidate tiles (started from P once their column block is ready) in
+      // one persistent launch.  Each user unit takes about half a candidate tile's k-steps.
+      ptg::BroadcastLaunch b{};
+      b.Xu = Xu; b.Xc = Xc; b.idx = user_idx; b.W = W; b.Y = Y;
+      b.bias = needs_bias(epi) ? bias : nullptr;
+      b.workspace = workspace;
+      b.U = U; b.Mc = Mc; b.Ku = Ku; b.Kc = Kc; b.N = N;
+      b.S = splits1; b.k_chunk = chunk1;
+      b.sync_bytes = ptg::broadcast_sync_bytes(N, ptg::kBroadcastMaxSlices);
+      b.b_kn = kn; b.epi = epi; b.out_f32 = y_dtype == PTG_F32;
+      b.epoch = next_epoch();
+      const hipError_t e = ptg::launch_broadcast_single(b, s);
+      if (e != hipSuccess) return hip_fail(e, fn);
+      return PTG_OK;
+    }
     float* P = reinterpret_cast<float*>(workspace);
     // Matmul decomposition: the user half of W meets each user's features once ...
     ptg::DenseLaunch u{};
@@ -684,6 +722,18 @@ ptg_status ptg_broadcast_gemm(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int
                           *bytes = ws_bytes;
                           return PTG_OK;
                         }, stream);
+}
+
+ptg_status ptg_broadcast_gemm_fused(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,
+                                    const void* Xc, const int32_t* user_idx, const void* W, ptg_layout w_layout,
+                                    void* Y, ptg_dtype y_dtype, const float* bias, ptg_epilogue epi,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  return broadcast_call("ptg_broadcast_gemm_fused", U, Mc, Ku, Kc, N, Xu, Xc, user_idx, W, w_layout, Y, y_dtype,
+                        bias, epi, [&](size_t, void** ws, size_t* bytes) {
+                          *ws = workspace;
+                          *bytes = ws_bytes;
+                          return PTG_OK;
+                        }, stream, true);
 }
 
 ptg_status ptg_broadcast_gemm_noalloc(int64_t U, int64_t Mc, int64_t Ku, int64_t Kc, int64_t N, const void* Xu,

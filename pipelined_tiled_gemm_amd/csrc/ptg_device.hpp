@@ -195,11 +195,30 @@ struct TileInfo {            // 16 dwords
   // partial sums meet in the workspace (combine_split16).
   uint32_t mode;
   uint32_t epoch;            // the launch's epoch: sync words left by other launches never match
-  uint64_t part;             // workspace: the tile's partial image (32 KB per consumer wave)
-  uint64_t sync;             // workspace: per consumer wave, a 64-bit arrival word, then a 32-bit ready word
-  uint64_t pad;
+  uint64_t part;             // workspace: the tile's partial image (32 KB per consumer wave), or
+                             // (reduction unit) its rows of the first partial product
+  uint64_t sync;             // workspace: split tiles: per consumer wave, a 64-bit arrival word, then
+                             // a 32-bit ready word; broadcast modes: the column block's arrival
+                             // word, its ready word 8 bytes further
+  uint32_t count;            // reduction unit: partial products to sum; candidate: ready count to await
+  uint32_t stride;           // reduction unit: elements between consecutive partial products
 };
 static_assert(sizeof(TileInfo) == 96, "TileInfo is 24 dwords");
+
+// Tile modes (TileInfo::mode).  0: a whole tile.  1, 2: the two units of a tile whose
+// reduction is split (grouped GEMM, combine_split16).  The single-launch broadcast GEMM adds:
+//   3: a user-phase partial product: fp32 output, no epilogue operation, agent-coherent stores,
+//      then every consumer wave counts itself into the tile's arrival word (`sync`);
+//   4: a reduction unit: no matrix work (one empty k-step); the producer waves wait until every
+//      partial product of its column block has arrived, sum them in split order, add the bias,
+//      write its rows of P, then count themselves into the column block's ready word;
+//   5: a candidate tile: published to the consumers only once its column block's P is ready;
+//      the accumulators start from P (agent-coherent loads).
+constexpr uint32_t kModeUserPartial = 3, kModeReduce = 4, kModeCandidate = 5;
+// The kinds of tiles a scheduler hands out (its kModes), so that a consumer compiles in only
+// the code for those: whole tiles only, or also split tiles (1, 2), or also the broadcast
+// modes (3-5).  The others cost its kernel no registers.
+constexpr int kModesNone = 0, kModesSplit = 1, kModesBroadcast = 2;
 
 // Tags of a metadata slot.  The consumer checks the tag of the slot it expects before it
 // uses any address from it: a slot that is not exactly what the producer published stops
@@ -357,6 +376,56 @@ __device__ __forceinline__ void wait_lgkm0() {
 __device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint64_t uni64(uint64_t x) {
   return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | (uint64_t)uni((uint32_t)x);
+}
+
+// Counters shared by the workgroups of one launch live in global memory as 64-bit words:
+// the launch's epoch in the high half and a count in the low half.  A word left by another
+// launch counts as zero, so no launch has to clear them.  They are touched by one lane with
+// agent-scope atomics (vector memory instructions, coherent across the XCDs).
+// Adds one within `epoch` and returns the count before: a fetch-and-add, and when the word
+// still holds another launch's epoch, a compare-and-swap that starts this epoch at one (a
+// fetch-and-add that landed on the old epoch is discarded with it and retried).
+__device__ __forceinline__ uint32_t epoch_add(uint64_t* w, uint32_t epoch) {
+  uint64_t old = __hip_atomic_fetch_add(w, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while ((uint32_t)(old >> 32) != epoch) {
+    uint64_t cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(cur >> 32) == epoch) {
+      old = __hip_atomic_fetch_add(w, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
+    if (__hip_atomic_compare_exchange_strong(w, &cur, ((uint64_t)epoch << 32) | 1u, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      return 0u;
+  }
+  return (uint32_t)old;
+}
+
+__device__ __forceinline__ uint32_t epoch_count(const uint64_t* w, uint32_t epoch) {
+  const uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (uint32_t)(v >> 32) == epoch ? (uint32_t)v : 0u;
+}
+
+// Lane 0 waits (bounded, see kSpinLimit) until the word's count in `epoch` reaches `target`;
+// returns false, with the workgroup aborted, when the wait gives up or the workgroup aborts.
+// Polls are about a thousand clocks apart: many workgroups may poll one word, and a line
+// read that often slows every other access that goes to its memory channel.
+__device__ __forceinline__ bool epoch_wait(const uint64_t* w, uint32_t epoch, uint32_t target, uint32_t* abort) {
+  uint32_t ok = 1;
+  if (lane_id() == 0) {
+    uint32_t polls = 0;
+    while (epoch_count(w, epoch) < target) {
+      __builtin_amdgcn_s_sleep(16);
+      if ((++polls & 63) == 0 && (lds_peek(abort) != 0 || polls >= kSpinLimit)) {
+        ok = 0;
+        break;
+      }
+    }
+  }
+  if (uni(ok) == 0) {
+    raise_abort(abort, 1u);
+    return false;
+  }
+  return true;
 }
 
 // Buffer descriptor over [base, base + nbytes).  Base and size are wave-uniform by
@@ -618,7 +687,7 @@ __device__ __forceinline__ bool schedule_tile(const typename S::Args& args, int 
     uint32_t pos;
     if (pid == 0) {
       uint32_t got = 0;
-      if (lane_id() == 0) got = S::claim(args);
+      if (lane_id() == 0) got = S::claim(args, sched_lds);
       pos = uni(got);
       lds_put64(slot, ((uint64_t)tag << 32) | pos);
     } else {
@@ -641,6 +710,100 @@ __device__ __forceinline__ bool schedule_tile(const typename S::Args& args, int 
   }
 }
 
+// A reduction unit of the single-launch broadcast GEMM, run by the producer waves when they
+// reach it (no ring data: its one k-step is empty).  Once every active consumer wave of every
+// user-phase slice of its column block has published this launch's epoch in its arrival flag,
+// producer p sums rows p, p + NPROD, ... of the slices' partial products in slice order (the
+// order of the separate reduction kernel: the first partial, plus each following one, plus the
+// bias), writes those rows of P, and counts itself into the block's ready word.  Lane l takes
+// columns 4 l .. 4 l + 3.  Partials and P go through the agent-coherent path: they are written
+// and read by workgroups on different XCDs within the launch.
+template <class C>
+__device__ __forceinline__ bool producer_reduce(const TileInfo& ti, int pid, const Guards* guards, uint32_t* abort) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  static_assert(C::BN == 256 && C::NCG <= 32, "one 256-column block: four columns per lane");
+  // Flags, partials and P are addressed as offsets into one descriptor over the workspace
+  // (the host keeps it under 2 GiB): its bound keeps every access inside the workspace, and
+  // the unit needs few scalar registers next to the producer's own state.
+  const uint64_t wlo = uni64(guards->w_lo);
+  const uint32_t wsize = (uint32_t)(uni64(guards->w_hi) - wlo);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<void*>(wlo), wsize);
+  const uint32_t epoch = uni(ti.epoch);
+  const int parts = (int)uni(ti.count);
+  const uint32_t stride = uni(ti.stride), active = uni(ti.p_bytes);
+  const int rows = (int)uni((uint32_t)ti.m_rows), n_cols = (int)uni((uint32_t)ti.n_cols);
+  const uint32_t ld = uni((uint32_t)ti.ldp);
+  const uint32_t flags_off = (uint32_t)(uni64(ti.sync) - wlo);
+  const uint32_t src_off = (uint32_t)(uni64(ti.part) - wlo), dst_off = (uint32_t)(uni64(ti.P) - wlo);
+  const uint64_t span = (uint64_t)(rows - 1) * ld * 4 + (uint64_t)n_cols * 4;
+  if (parts < 1 || parts * C::NCG > 256 || rows < 1 || rows > C::BM || n_cols < 1 || n_cols > C::BN ||
+      uni64(ti.sync) < wlo || uni64(ti.part) < wlo || uni64(ti.P) < wlo ||
+      (uint64_t)flags_off + (uint64_t)parts * C::NCG * 4 > wsize ||
+      (uint64_t)src_off + (uint64_t)(parts - 1) * stride * 4 + span > wsize || (uint64_t)dst_off + span > wsize) {
+    raise_abort(abort, 8u);
+    return false;
+  }
+  const int lane = lane_id();
+  // every active wave's flag of every slice: lane l checks flags l, l + 64, l + 128, l + 192
+  // (polls about a thousand clocks apart, see epoch_wait)
+  uint32_t polls = 0;
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = lane + 64 * q;
+      if (i < parts * C::NCG && ((active >> (i % C::NCG)) & 1u) &&
+          __builtin_amdgcn_raw_buffer_load_b32(rw, flags_off + (uint32_t)i * 4u, 0, 16) != epoch)
+        ok = false;
+    }
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+    __builtin_amdgcn_s_sleep(16);
+    if ((++polls & 63) == 0 && (uni(lds_peek(abort)) != 0 || polls >= kSpinLimit)) {
+      raise_abort(abort, 1u);
+      return false;
+    }
+  }
+  const int col = lane * 4;
+  const bool col_ok = col < n_cols;
+  const uint64_t biasp = uni64(ti.bias);
+  if (biasp != 0 && !inside(biasp, (uint64_t)n_cols * 4, uni64(guards->bias_lo), uni64(guards->bias_hi))) {
+    raise_abort(abort, 8u);
+    return false;
+  }
+  constexpr int kInFlight = 8;  // partial loads in flight per round
+  for (int r = pid; r < rows; r += C::NPROD) {
+    const uint32_t off = (uint32_t)r * ld * 4u + (uint32_t)col * 4u;
+    f32x4 acc = {};
+    for (int p0 = 0; p0 < parts; p0 += kInFlight) {
+      // every load is issued (a slice past the last one reads zeros, touching no memory);
+      // only the slices that exist are added, in order
+      f32x4 v[kInFlight];
+      uint32_t o = src_off + off + (uint32_t)p0 * stride * 4u;  // a running offset: few scalar registers
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i) {
+        v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rw, (col_ok && p0 + i < parts) ? o : kOutOfRange, 0, 16));
+        o += stride * 4u;
+      }
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i) {
+        const f32x4 sum = acc + v[i];
+        acc = p0 + i == 0 ? v[i] : (p0 + i < parts ? sum : acc);
+      }
+    }
+    if (biasp != 0) {
+      // read per row (a short live range: the unit runs beside the producer's own state)
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(reinterpret_cast<void*>(biasp), (uint32_t)(n_cols * 4));
+      acc += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, col_ok ? col * 4 : kOutOfRange, 0, 0));
+    }
+    if (col_ok) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rw, dst_off + off, 0, 16);
+  }
+  // the rows of P have completed before the wave counts itself into the ready word
+  wait_vmcnt<0>();
+  if (lane == 0) epoch_add(reinterpret_cast<uint64_t*>(ti.C), epoch);
+  return true;
+}
+
 template <class C, class S>
 __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, int j, int pid, bool opA,
                                                 int i0, char* sched_lds, TileInfo* info,
@@ -651,6 +814,15 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
   // Every value is the same across the wave; saying so keeps the fetch state in scalar
   // registers (a scheduler may read LDS, whose loads the compiler treats as per-lane).
   f.has = uni(schedule_tile<C, S>(args, j, pid, t, sched_lds, abort) ? 1u : 0u) != 0;
+  if constexpr (S::kModes == kModesBroadcast) {
+    // the single-launch broadcast: the producers run the reduction units, and a candidate tile
+    // is published only once its column block of P is ready
+    const uint32_t mode = f.has ? uni(t.info.mode) : 0u;
+    if (mode == kModeReduce)
+      producer_reduce<C>(t.info, pid, guards, abort);
+    else if (mode == kModeCandidate && pid == 0)
+      epoch_wait(reinterpret_cast<const uint64_t*>(uni64(t.info.sync)), uni(t.info.epoch), uni(t.info.count), abort);
+  }
   if (pid == 0 && lane == 0) {
     TileInfo ti = t.info;
     ti.tag = f.has ? tile_tag(j) : end_tag(j);
@@ -680,7 +852,8 @@ __device__ __forceinline__ FetchTile fetch_tile(const typename S::Args& args, in
     // all zeros and touches no memory
     f.src = 0;
     f.bytes = 0;
-  } else if (!inside(f.src, f.bytes, uni64(opA ? guards->a_lo : guards->b_lo), uni64(opA ? guards->a_hi : guards->b_hi))) {
+  } else if (!inside(f.src, f.bytes, uni64(opA ? guards->a_lo : guards->b_lo), uni64(opA ? guards->a_hi : guards->b_hi)) &&
+             !(opA && inside(f.src, f.bytes, uni64(guards->a2_lo), uni64(guards->a2_hi)))) {
     raise_abort(abort, 4u);
     f.bytes = 0;  // every load of this tile is out of range: nothing is read
   }
@@ -1111,7 +1284,7 @@ __device__ __forceinline__ void consumer_role(char* ring, const TileInfo* info, 
 // columns 0-3, 4-7, 8-11, 12-15 of the same row.
 
 // Start value of the accumulators: bias[col], or P[idx[row]][col] for a gathered launch.
-template <class C>
+template <class C, int MODES>
 __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const TileInfo* ti,
                                            const Guards* guards, int epi, int wm, int wn,
                                            uint32_t* abort) {
@@ -1121,7 +1294,7 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
     for (int tn = 0; tn < C::TN16; ++tn) acc[tm][tn] = f32x4{};
   // the second unit of a split tile adds its partial sum to the first's, which carries the
   // start value
-  if (uni(ti->mode) == 2) return true;
+  if (MODES == kModesSplit && uni(ti->mode) == 2) return true;
   const uint64_t biasp = uni64(ti->bias);
   const uint64_t gidxp = uni64(ti->gidx);
   const bool gather = gidxp != 0;
@@ -1168,6 +1341,11 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
     // same P row.  Then its columns are loaded once and copied into every row block (rows
     // past m_rows take them too; the epilogue never stores those rows).  Lane 0 holds the
     // wave's first row, which is valid: an idle wave does not get here.
+    // (the single-launch broadcast reads P on the agent-coherent path: reduction units wrote
+    // it during this launch, possibly on another XCD)
+    auto load_p = [&](uint32_t off) -> f32x4 {
+      return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, MODES == kModesBroadcast ? 16 : 0));
+    };
     const int p0 = (int)uni((uint32_t)prow[0]);
     bool same = true;
 #pragma unroll
@@ -1180,7 +1358,7 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
       for (int tn = 0; tn < C::TN16; ++tn) {
         const int col = wn * C::WTN + tn * 16 + cq;
         const uint32_t po = col < n_cols ? (uint32_t)(p0 * ldp + col) * 4u : kOutOfRange;
-        const f32x4 p4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, po, 0, 0));
+        const f32x4 p4 = load_p(po);
 #pragma unroll
         for (int tm = 0; tm < C::TM16; ++tm) acc[tm][tn] = p4;
       }
@@ -1193,7 +1371,7 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
         for (int tn = 0; tn < C::TN16; ++tn) {
           const int col = wn * C::WTN + tn * 16 + cq;
           const uint32_t po = (row_ok && col < n_cols) ? (uint32_t)(prow[tm] * ldp + col) * 4u : kOutOfRange;
-          acc[tm][tn] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, po, 0, 0));
+          acc[tm][tn] = load_p(po);
         }
       }
     }
@@ -1210,7 +1388,7 @@ __device__ __forceinline__ bool init_acc16(f32x4 (&acc)[C::TM16][C::TN16], const
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 __device__ __forceinline__ void store_rows128(u32x4_t X, u32x4_t Y, int colX, int colY, int row0, int lane,
                                               int m_rows, int n_cols, int ldc, uint32_t osz,
-                                              __amdgpu_buffer_rsrc_t rc) {
+                                              __amdgpu_buffer_rsrc_t rc, bool coherent = false) {
   const bool lo = (lane & 8) == 0;
   u32x4_t A, B;
 #pragma unroll
@@ -1225,9 +1403,15 @@ __device__ __forceinline__ void store_rows128(u32x4_t X, u32x4_t Y, int colX, in
   const bool col_ok = col < n_cols;
   const uint32_t vA = (rowA < m_rows && col_ok) ? (uint32_t)(rowA * ldc + col) * osz : kOutOfRange;
   const uint32_t vB = (rowB < m_rows && col_ok) ? (uint32_t)(rowB * ldc + col) * osz : kOutOfRange;
-  // cache policy 2: non-temporal
-  __builtin_amdgcn_raw_buffer_store_b128(A, rc, vA, 0, 2);
-  __builtin_amdgcn_raw_buffer_store_b128(B, rc, vB, 0, 2);
+  if (coherent) {
+    // cache policy sc1: agent-coherent (read next by workgroups on other XCDs)
+    __builtin_amdgcn_raw_buffer_store_b128(A, rc, vA, 0, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(B, rc, vB, 0, 16);
+  } else {
+    // cache policy 2: non-temporal
+    __builtin_amdgcn_raw_buffer_store_b128(A, rc, vA, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(B, rc, vB, 0, 2);
+  }
 }
 
 // Epilogue: SiLU if asked, conversion, 16-byte stores.  fp32: one run of 4 columns per lane
@@ -1237,7 +1421,8 @@ __device__ __forceinline__ void store_rows128(u32x4_t X, u32x4_t Y, int colX, in
 // columns 8 (g / 2) .. + 7 of block tn + g % 2.
 template <class C>
 __device__ __forceinline__ void epilogue16(f32x4 (&acc)[C::TM16][C::TN16], int wm, int wn, int m_rows,
-                                           int n_cols, uint64_t Cp, int ldc, bool do_silu, bool f32out) {
+                                           int n_cols, uint64_t Cp, int ldc, bool do_silu, bool f32out,
+                                           bool coherent = false) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   const int lane = opaque_lane();
   const int grp = lane >> 4;
@@ -1267,7 +1452,7 @@ __device__ __forceinline__ void epilogue16(f32x4 (&acc)[C::TM16][C::TN16], int w
         if (f32out) {
           const int colX = wn * C::WTN + tn * 16 + grp * 4;
           store_rows128(__builtin_bit_cast(u32x4, v0), __builtin_bit_cast(u32x4, v1), colX, colX + 16, row0,
-                        lane, m_rows, n_cols, ldc, 4u, rc);
+                        lane, m_rows, n_cols, ldc, 4u, rc, coherent);
         } else {
           const uint32_t x0 = pack_bf16(v0[0], v0[1]), x1 = pack_bf16(v0[2], v0[3]);
           const uint32_t y0 = pack_bf16(v1[0], v1[1]), y1 = pack_bf16(v1[2], v1[3]);
@@ -1278,7 +1463,7 @@ __device__ __forceinline__ void epilogue16(f32x4 (&acc)[C::TM16][C::TN16], int w
             pair0 = d;
           } else {
             const int colX = wn * C::WTN + (grp & 1) * 16 + (grp >> 1) * 8;
-            store_rows128(pair0, d, colX, colX + 32, row0, lane, m_rows, n_cols, ldc, 2u, rc);
+            store_rows128(pair0, d, colX, colX + 32, row0, lane, m_rows, n_cols, ldc, 2u, rc, coherent);
           }
         }
       }
@@ -1411,7 +1596,7 @@ __device__ __forceinline__ bool combine_split16(f32x4 (&acc)[C::TM16][C::TN16], 
 // first-half fragment after the last column.  Fragments in registers: TM16/2 of A and TN16 of
 // B.  The ring slot is released as soon as the last fragment read from it has been consumed
 // (after the first column of the last slice's second half).
-template <class C>
+template <class C, int MODES = kModesNone>
 __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info, uint32_t* full, uint32_t* empty,
                                                 uint32_t* abort, int cw, int epi, bool f32out,
                                                 const Guards* guards) {
@@ -1500,7 +1685,10 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
     // idle wave: only takes part in the handoff (see consumer_role).  The extents are read
     // with hand-issued LDS reads, so that no copy of them stays live across the k-loop (the
     // epilogue reads the metadata again).
-    if (wm * C::WTM >= (int)uni(lds_peek(reinterpret_cast<const uint32_t*>(&ti->m_rows))) ||
+    // A reduction unit of the single-launch broadcast is the producers' work: every consumer
+    // wave treats it as idle.
+    if ((MODES == kModesBroadcast && uni(lds_peek(&ti->mode)) == kModeReduce) ||
+        wm * C::WTM >= (int)uni(lds_peek(reinterpret_cast<const uint32_t*>(&ti->m_rows))) ||
         wn * C::WTN >= (int)uni(lds_peek(reinterpret_cast<const uint32_t*>(&ti->n_cols)))) {
       lds_bump(&empty[s0]);
       ++g;
@@ -1513,7 +1701,7 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
     }
 
     f32x4 acc[C::TM16][C::TN16];
-    if (!init_acc16<C>(acc, ti, guards, epi, wm, wn, abort)) break;
+    if (!init_acc16<C, MODES>(acc, ti, guards, epi, wm, wn, abort)) break;
 
     bf16x8 a[HM], b[C::TN16];
     {
@@ -1567,12 +1755,18 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
       }
     }
 
+    const uint32_t tmode = MODES != kModesNone ? uni(ti->mode) : 0u;
     // a split tile: the unit that arrives second finishes it
-    if (uni(ti->mode) != 0 && !combine_split16<C>(acc, ti, cw % C::NCG, guards, abort)) {
+    if (MODES == kModesSplit && (tmode == 1 || tmode == 2) &&
+        !combine_split16<C>(acc, ti, cw % C::NCG, guards, abort)) {
       if (uni(lds_peek(abort)) != 0) break;
       continue;
     }
 
+    // a user-phase partial product goes to the workspace in fp32, without an epilogue
+    // operation, on the agent-coherent path
+    const bool partial = MODES == kModesBroadcast && tmode == kModeUserPartial;
+    const bool out4 = f32out || partial;
     const int m_rows = (int)uni((uint32_t)ti->m_rows);
     const int n_cols = (int)uni((uint32_t)ti->n_cols);
     const uint64_t Cp = uni64(ti->C);
@@ -1581,12 +1775,21 @@ __device__ __forceinline__ void consumer_role16(char* ring, const TileInfo* info
       raise_abort(abort, 2u);
       break;
     }
-    const uint64_t c_bytes = (uint64_t)((int64_t)(m_rows - 1) * ldc + n_cols) * (f32out ? 4u : 2u);
-    if (!inside(Cp, c_bytes, uni64(guards->c_lo), uni64(guards->c_hi))) {
+    const uint64_t c_bytes = (uint64_t)((int64_t)(m_rows - 1) * ldc + n_cols) * (out4 ? 4u : 2u);
+    if (!inside(Cp, c_bytes, uni64(partial ? guards->w_lo : guards->c_lo), uni64(partial ? guards->w_hi : guards->c_hi))) {
       raise_abort(abort, 8u);
       break;
     }
-    epilogue16<C>(acc, wm, wn, m_rows, n_cols, Cp, ldc, epi == EPI_SILU || epi == EPI_BIAS_SILU, f32out);
+    epilogue16<C>(acc, wm, wn, m_rows, n_cols, Cp, ldc, !partial && (epi == EPI_SILU || epi == EPI_BIAS_SILU), out4,
+                  partial);
+    if (partial) {
+      // the partial product, written on the agent-coherent path, has completed (the reduction
+      // may run on another XCD) before the wave's arrival flag carries this launch's epoch
+      wait_vmcnt<0>();
+      if (lane_id() == 0)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(uni64(ti->sync)) + (cw % C::NCG), uni(ti->epoch),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1616,7 +1819,7 @@ __global__ __launch_bounds__(C::NT, 1) void ptg_kernel(typename S::Args args) {
   if (wave < C::NCONS) {
     __builtin_amdgcn_s_setprio(1);
     if constexpr (C::M16)
-      consumer_role16<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
+      consumer_role16<C, S::kModes>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
     else
       consumer_role<C>(ring, info, full, empty, abort, wave, args.epi, args.out_f32 != 0, guards);
   } else {

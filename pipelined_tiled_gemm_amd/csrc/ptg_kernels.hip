@@ -49,6 +49,7 @@ struct DenseSched {
   __device__ static Guards guards(const Args& a) { return a.guard; }
   static constexpr int LDS_BYTES = 16;
   static constexpr bool kDynamic = false;
+  static constexpr int kModes = kModesNone;
 
   template <class C>
   __device__ static void init(const Args&, char*) {}
@@ -204,6 +205,7 @@ struct GroupedSched {
   static constexpr int kScratchInts = 20;
   static constexpr int LDS_BYTES = 3 * (kMaxGroups + 1) * 4 + kScratchInts * 4 + 3 * 4;
   static constexpr bool kDynamic = false;
+  static constexpr int kModes = kModesSplit;
 
   // full (more than BM/2 valid rows) and half m-tiles of a group of cnt rows
   template <class C>
@@ -373,6 +375,7 @@ struct WgradSched {
   };
   __device__ static Guards guards(const Args& a) { return a.guard; }
   static constexpr bool kDynamic = true;
+  static constexpr int kModes = kModesNone;
   static constexpr int kClaimSlots = 16;
   static constexpr int kQueues = 8;          // one per XCD
   static constexpr int kQueueStride = 8;     // 32 bytes between counters
@@ -419,7 +422,7 @@ struct WgradSched {
   // A ticket for the calling workgroup's next tile: queue (4 bits) and position (28 bits), or
   // kNoTile when every queue is drained.  Called by one lane.  The XCD of a workgroup is
   // blockIdx.x mod 8 (workgroups are dealt to the XCDs round-robin).
-  __device__ static uint32_t claim(const Args& a) {
+  __device__ static uint32_t claim(const Args& a, char*) {
     const int x0 = (int)(blockIdx.x % kQueues);
     for (int d = 0; d < kQueues; ++d) {
       const int x = (x0 + d) % kQueues;
@@ -479,6 +482,171 @@ __global__ void arm_queue_kernel(uint32_t* queue) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Single-launch broadcast (IKBO) scheduler
+// ---------------------------------------------------------------------------------------
+// The in-kernel broadcast GEMM of "Case Study 2: In-Kernel Broadcast Optimization for RecSys"
+// as one persistent launch (the final form its subsection "TLX Provides a Building Block for
+// the Final Stage of This Optimization" describes: user and candidate GEMMs share the
+// pipeline, and tiles hand results to each other with release and acquire flags).  Its work
+// comes in three kinds, in this order of tickets:
+//   - user units (S per column block of P): the partial product of Xu and one K-slice of
+//     the user half of W, written to the workspace;
+//   - reduction units (red_per_nb per column block): once every user unit of the block has
+//     arrived, the sum of the partials in slice order plus the bias, rows of P;
+//   - candidate tiles: Xc . W_c starting from P[idx[r]], once their block of P is ready.
+// Each workgroup takes user and reduction units from a shared ticket word (its claims are in
+// increasing ticket order) until none is left, then its share of the candidate tiles in the
+// dense order (XCD-aware bands of m-tiles).  A unit waits only on units of smaller tickets,
+// already held by running workgroups that wait on nothing later, so the launch finishes
+// whether or not all its workgroups are resident at once.  The ticket, arrival and ready
+// words carry the launch's epoch (epoch_add), so nothing is cleared between launches.
+struct IkboSched {
+  struct Args {
+    const __bf16* Xu;
+    const __bf16* Xc;
+    const __bf16* W;
+    const int32_t* idx;
+    char* Y;
+    const float* bias;
+    float* P;              // [U x N]
+    float* parts;          // [S x U x N]
+    uint64_t* words;       // the ticket word, then one ready word per column block
+    uint32_t* flags;       // arrival flags [n_blocks][S][NCG] (one per consumer wave)
+    uint32_t epoch;
+    int32_t U, Mc, Ku, Kc, N, Kt, S, k_chunk, n_blocks, red_rows, red_per_nb;
+    int32_t T_user, T_dyn;
+    int32_t tiles_m, tiles_n, group_m;
+    int32_t epi, out_f32, out_bytes;
+    Guards guard;
+  };
+  __device__ static Guards guards(const Args& a) { return a.guard; }
+  static constexpr bool kDynamic = true;
+  static constexpr int kModes = kModesBroadcast;
+  static constexpr int kClaimSlots = 16;
+  static constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+  // claim slots [16], then the workgroup's "no unit left" flag and its next candidate index
+  static constexpr int LDS_BYTES = kClaimSlots * 8 + 16;
+  __device__ static uint64_t* claim_slots(char* lds) { return reinterpret_cast<uint64_t*>(lds); }
+  __device__ static int32_t* state(char* lds) { return reinterpret_cast<int32_t*>(lds + kClaimSlots * 8); }
+
+  template <class C>
+  __device__ static void init(const Args&, char* lds) {
+    if (threadIdx.x < kClaimSlots) claim_slots(lds)[threadIdx.x] = 0;
+    if (threadIdx.x < 2) state(lds)[threadIdx.x] = 0;
+  }
+
+  // The launch's arguments, read where they are used (scalar loads from the kernel-argument
+  // segment, where the single argument lies at offset 0).  The empty asm hides that the
+  // pointer is the same on every tile, so the compiler does not keep the thirty-odd fields in
+  // scalar registers across the producer loop, where they would spill.
+  typedef const __attribute__((address_space(4))) Args KArgs;
+  __device__ static KArgs& fresh() {
+    KArgs* p = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return *p;
+  }
+
+  // The next ticket of the calling workgroup (one lane of its first producer): user and
+  // reduction units from the launch's ticket word while they last, then the workgroup's
+  // candidate tiles in the dense path's XCD-aware order (tiles j grid + xcd_rank, so that tiles
+  // sharing Xc rows and W columns meet in one L2).  Measured faster than per-XCD queues of
+  // candidates, whose claims cost a round trip to memory per tile.
+  __device__ static uint32_t claim(const Args&, char* lds) {
+    KArgs& a = fresh();
+    int32_t* st = state(lds);
+    if (st[0] == 0) {
+      const uint32_t t = epoch_add(a.words, a.epoch);
+      if (t < (uint32_t)a.T_dyn) return t;
+      st[0] = 1;
+    }
+    const int64_t L = (int64_t)(st[1]++) * gridDim.x + xcd_rank(blockIdx.x, gridDim.x);
+    if (L >= (int64_t)a.tiles_m * a.tiles_n) return kNoTile;
+    return (uint32_t)(a.T_dyn + L);
+  }
+
+  template <class C>
+  __device__ static bool tile_at(const Args&, uint32_t ticket, TileSrc& t, char*) {
+    if (ticket == kNoTile) return false;
+    KArgs& a = fresh();
+    const int64_t N = a.N;
+    t.info.tag = 0;  // set by the producer when it publishes the slot
+    t.info.epoch = a.epoch;
+    if (ticket < (uint32_t)a.T_user) {
+      // user unit: slice s of Ku for column block nb
+      const int nb = (int)ticket / a.S, s = (int)ticket % a.S;
+      const int64_t k0 = (int64_t)s * a.k_chunk, n0 = (int64_t)nb * C::BN;
+      t.A = a.Xu + k0;
+      t.lda = a.Ku;
+      t.B = C::B_KN ? a.W + k0 * N + n0 : a.W + n0 * a.Kt + k0;
+      t.ldb = C::B_KN ? N : a.Kt;
+      t.info.K = (int)min((int64_t)a.k_chunk, (int64_t)a.Ku - k0);
+      t.info.m_rows = a.U;
+      t.info.n_cols = (int)min((int64_t)C::BN, N - n0);
+      t.info.C = (uint64_t)(a.parts + (int64_t)s * a.U * N + n0);
+      t.info.ldc = N;
+      t.info.mode = kModeUserPartial;
+      t.info.sync = (uint64_t)(a.flags + ((int64_t)nb * a.S + s) * C::NCG);
+      return true;
+    }
+    if (ticket < (uint32_t)a.T_dyn) {
+      // reduction unit q of column block nb: rows [q red_rows, +red_rows) of P
+      const int r = (int)ticket - a.T_user;
+      const int nb = r / a.red_per_nb, q = r % a.red_per_nb;
+      const int64_t row0 = (int64_t)q * a.red_rows, n0 = (int64_t)nb * C::BN;
+      t.A = nullptr;
+      t.B = nullptr;
+      t.info.K = 0;  // one empty k-step
+      t.info.m_rows = (int)min((int64_t)a.red_rows, (int64_t)a.U - row0);
+      t.info.n_cols = (int)min((int64_t)C::BN, N - n0);
+      t.info.part = (uint64_t)(a.parts + row0 * N + n0);
+      t.info.P = (uint64_t)(a.P + row0 * N + n0);
+      t.info.ldp = (int32_t)N;
+      t.info.bias = a.bias ? (uint64_t)(a.bias + n0) : 0;
+      t.info.count = (uint32_t)a.S;
+      t.info.stride = (uint32_t)((int64_t)a.U * N);
+      t.info.mode = kModeReduce;
+      t.info.sync = (uint64_t)(a.flags + (int64_t)nb * a.S * C::NCG);
+      t.info.C = (uint64_t)(a.words + 1 + nb);  // the block's ready word
+      {
+        // the consumer waves of a user unit that own rows and columns of it (the others idle)
+        const int am = min(C::WM, (a.U + C::WTM - 1) / C::WTM);
+        const int an = min(C::WN, (int)((t.info.n_cols + C::WTN - 1) / C::WTN));
+        uint32_t mask = 0;
+        for (int m = 0; m < am; ++m)
+          for (int n = 0; n < an; ++n) mask |= 1u << (m * C::WN + n);
+        t.info.p_bytes = mask;
+      }
+      return true;
+    }
+    // candidate tile L (the dense order: bands of group_m m-tiles walked column by column)
+    const int64_t L = (int64_t)ticket - a.T_dyn;
+    const int64_t per_group = (int64_t)a.group_m * a.tiles_n;
+    const int64_t grp = L / per_group, in = L % per_group;
+    const int first_m = (int)(grp * a.group_m);
+    const int gm = min(a.tiles_m - first_m, a.group_m);
+    const int tm = first_m + (int)(in % gm), tn = (int)(in / gm);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    t.A = a.Xc + m0 * a.Kc;
+    t.lda = a.Kc;
+    t.B = C::B_KN ? a.W + (int64_t)a.Ku * N + n0 : a.W + n0 * a.Kt + a.Ku;
+    t.ldb = C::B_KN ? N : a.Kt;
+    t.info.K = a.Kc;
+    t.info.m_rows = (int)min((int64_t)C::BM, (int64_t)a.Mc - m0);
+    t.info.n_cols = (int)min((int64_t)C::BN, N - n0);
+    t.info.C = (uint64_t)(a.Y + (m0 * N + n0) * a.out_bytes);
+    t.info.ldc = N;
+    t.info.gidx = (uint64_t)(a.idx + m0);
+    t.info.P = (uint64_t)(a.P + n0);
+    t.info.ldp = (int32_t)N;
+    t.info.p_bytes = (uint32_t)(((int64_t)a.U * N - n0) * 4);
+    t.info.mode = kModeCandidate;
+    t.info.sync = (uint64_t)(a.words + 1 + tn);
+    t.info.count = (uint32_t)(a.red_per_nb * C::NPROD);
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // Batch (pointer-array) scheduler
 // ---------------------------------------------------------------------------------------
 struct BatchSched {
@@ -493,6 +661,7 @@ struct BatchSched {
   __device__ static Guards guards(const Args& a) { return *a.guard_ptr; }
   static constexpr int LDS_BYTES = (kMaxBatch + 1) * 4 + 16;
   static constexpr bool kDynamic = false;
+  static constexpr int kModes = kModesNone;
 
   // The launch runs only the table it was asked for: a header whose magic, count, epilogue
   // or output type differs from the launch's arguments (a table written for another call)
@@ -718,6 +887,62 @@ int32_t broadcast_user_splits(int64_t U, int64_t N) {
   const int64_t tiles = use_large(U, N) ? ((U + 255) / 256) * ((N + 255) / 256) : ((U + 127) / 128) * ((N + 127) / 128);
   const int64_t s = 256 / (tiles > 0 ? tiles : 1);
   return (int32_t)(s < 1 ? 1 : (s > 32 ? 32 : s));
+}
+
+// The single launch needs the user rows in one large m-tile, a split user phase (at most 32
+// slices, the reduction units' limit) and its sync words in their 4 KB block; the caller also
+// keeps the whole workspace under 2 GiB (the reduction units address it with 31-bit offsets).
+bool broadcast_single_launch_fits(int64_t U, int64_t N, int32_t S) {
+  const int64_t n_blocks = (N + 255) / 256;
+  return U >= 1 && U <= 256 && S >= 2 && S <= 32 && (1 + n_blocks) * 8 <= (int64_t)broadcast_flags_offset();
+}
+
+template <class C>
+static hipError_t launch_broadcast_single_cfg(const BroadcastLaunch& b, hipStream_t stream) {
+  IkboSched::Args a;
+  a.Xu = reinterpret_cast<const __bf16*>(b.Xu);
+  a.Xc = reinterpret_cast<const __bf16*>(b.Xc);
+  a.W = reinterpret_cast<const __bf16*>(b.W);
+  a.idx = b.idx;
+  a.Y = reinterpret_cast<char*>(b.Y);
+  a.bias = b.bias;
+  char* ws = reinterpret_cast<char*>(b.workspace);
+  a.words = reinterpret_cast<uint64_t*>(ws);
+  a.flags = reinterpret_cast<uint32_t*>(ws + broadcast_flags_offset());
+  a.P = reinterpret_cast<float*>(ws + b.sync_bytes);
+  a.parts = a.P + b.U * b.N;
+  a.epoch = b.epoch;
+  a.U = (int32_t)b.U; a.Mc = (int32_t)b.Mc; a.Ku = (int32_t)b.Ku; a.Kc = (int32_t)b.Kc; a.N = (int32_t)b.N;
+  a.Kt = (int32_t)(b.Ku + b.Kc);
+  a.S = b.S;
+  a.k_chunk = (int32_t)b.k_chunk;
+  a.n_blocks = (int32_t)((b.N + C::BN - 1) / C::BN);
+  a.red_rows = 2 * C::NPROD;  // two rows of P per producer wave
+  a.red_per_nb = (int32_t)((b.U + a.red_rows - 1) / a.red_rows);
+  a.T_user = a.n_blocks * a.S;
+  a.T_dyn = a.T_user + a.n_blocks * a.red_per_nb;
+  a.tiles_m = (int32_t)((b.Mc + C::BM - 1) / C::BM);
+  a.tiles_n = a.n_blocks;
+  a.group_m = 4;
+  a.epi = b.epi; a.out_f32 = b.out_f32; a.out_bytes = b.out_f32 ? 4 : 2;
+  Guards& g = a.guard;
+  g = Guards{};
+  const int64_t Kt = b.Ku + b.Kc;
+  span(b.Xc, mat_bytes(b.Mc, b.Kc, b.Kc, 2), g.a_lo, g.a_hi);
+  span(b.Xu, mat_bytes(b.U, b.Ku, b.Ku, 2), g.a2_lo, g.a2_hi);
+  span(b.W, b.b_kn ? mat_bytes(Kt, b.N, b.N, 2) : mat_bytes(b.N, Kt, Kt, 2), g.b_lo, g.b_hi);
+  span(b.Y, mat_bytes(b.Mc, b.N, b.N, a.out_bytes), g.c_lo, g.c_hi);
+  span(b.bias, (uint64_t)b.N * 4, g.bias_lo, g.bias_hi);
+  span(b.idx, (uint64_t)b.Mc * 4, g.gidx_lo, g.gidx_hi);
+  span(a.P, (uint64_t)b.U * b.N * 4, g.p_lo, g.p_hi);
+  span(b.workspace, b.sync_bytes + (uint64_t)(1 + b.S) * b.U * b.N * 4, g.w_lo, g.w_hi);
+  return launch_persistent<C, IkboSched>(a, (int64_t)a.T_dyn + (int64_t)a.tiles_m * a.tiles_n, stream);
+}
+
+hipError_t launch_broadcast_single(const BroadcastLaunch& b, hipStream_t stream) {
+  if (b.Mc == 0 || b.N == 0) return hipSuccess;
+  return b.b_kn ? launch_broadcast_single_cfg<CfgLarge<true>>(b, stream)
+                : launch_broadcast_single_cfg<CfgLarge<false>>(b, stream);
 }
 
 // m-tiles per band of the grouped tile order

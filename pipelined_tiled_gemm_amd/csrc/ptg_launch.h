@@ -87,7 +87,8 @@ struct Guards {
   uint64_t a_lo, a_hi, b_lo, b_hi;      // DMA sources
   uint64_t c_lo, c_hi;                  // output
   uint64_t bias_lo, bias_hi, gidx_lo, gidx_hi, p_lo, p_hi;  // epilogue operands
-  uint64_t w_lo, w_hi;                  // workspace of a split reduction (images, sync words)
+  uint64_t w_lo, w_hi;                  // workspace (split images, sync words, P and partials)
+  uint64_t a2_lo, a2_hi;                // a second first-operand range (broadcast: Xu beside Xc)
 };
 
 // Workspace layout of a batch: [header 256 B][prefix int32 (count + 1), padded to 256 B][problems].
@@ -100,7 +101,7 @@ struct BatchHeader {
   int32_t out_f32;              // output element type the table was written for (C ranges)
   int32_t reserved0;
   Guards guard;                 // union of the problems' operand ranges
-  int32_t reserved[28];
+  int32_t reserved[24];
 };
 static_assert(sizeof(BatchHeader) == 256, "BatchHeader layout");
 constexpr int32_t kBatchMagic = 0x50544742;  // "PTGB"
@@ -133,6 +134,35 @@ hipError_t launch_reduce_splits(float* out, const float* parts, int64_t count, i
 // Split count of the broadcast path's user phase for a U x N product (a function of the
 // shape only, so that the workspace query and the call agree), and the maximum over K.
 int32_t broadcast_user_splits(int64_t U, int64_t N);
+// The one-launch broadcast workspace: a block of sync words (4 KB of 64-bit words: the ticket
+// word, one ready word per 256-column block; then the arrival flags, 8 per user-phase slice and
+// column block), rounded to 4 KB, then P [U x N] fp32, then the user phase's partial products
+// [S x U x N] fp32.
+inline size_t broadcast_flags_offset() { return 4096; }
+constexpr int32_t kBroadcastMaxSlices = 32;  // user-phase slices of the one-launch form
+inline size_t broadcast_sync_bytes(int64_t N, int32_t S) {
+  const int64_t n_blocks = (N + 255) / 256;
+  return (broadcast_flags_offset() + (size_t)n_blocks * (size_t)(S > 1 ? S : 1) * 8 * 4 + 4095) / 4096 * 4096;
+}
+// The broadcast GEMM as one persistent launch (user units, reduction units and candidate
+// tiles; IkboSched in ptg_kernels.hip).  Used when broadcast_single_launch_fits holds.
+struct BroadcastLaunch {
+  const void* Xu;
+  const void* Xc;
+  const int32_t* idx;
+  const void* W;
+  void* Y;
+  const float* bias;          // [N] or null
+  void* workspace;            // sync_bytes + (1 + S) U N 4 bytes
+  size_t sync_bytes;          // the sync block (broadcast_sync_bytes of the workspace query)
+  int64_t U, Mc, Ku, Kc, N;
+  int32_t S;                  // user-phase slices
+  int64_t k_chunk;            // k per slice (whole k-steps)
+  int b_kn, epi, out_f32;
+  uint32_t epoch;             // unique per launch
+};
+bool broadcast_single_launch_fits(int64_t U, int64_t N, int32_t S);
+hipError_t launch_broadcast_single(const BroadcastLaunch& b, hipStream_t stream);
 hipError_t launch_grouped(const GroupedLaunch& g, hipStream_t stream);
 hipError_t launch_batch(const BatchLaunch& b, hipStream_t stream);
 hipError_t launch_grouped_wgrad(const WgradLaunch& w, hipStream_t stream);

@@ -195,6 +195,30 @@ def test_broadcast_validation(L):
     assert "P (U x N fp32)" in L.ptg_last_error().decode()
 
 
+def test_broadcast_fused_validation(L):
+    U, N = 4, 64
+    need = L.ptg_broadcast_gemm_fused_workspace(U, N)
+    # 4 KB of 64-bit sync words, the arrival flags (8 per slice and 256-column block, up to 32
+    # slices) in 4 KB pages, then P and 32 partial products
+    sync = (4096 + 1 * 32 * 8 * 4 + 4095) // 4096 * 4096
+    assert need == sync + U * N * 4 * (1 + 32)
+
+    def f(U=U, Mc=100, Ku=192, Kc=64, N=N, Xu=P, Xc=P, idx=P, W=P, layout=0, Y=P, dtype=0,
+          bias=None, epi=0, ws=P, wsb=need):
+        return L.ptg_broadcast_gemm_fused(U, Mc, Ku, Kc, N, Xu, Xc, idx, W, layout, Y, dtype, bias, epi,
+                                          ws, wsb, None)
+    assert f(U=0) == INVALID
+    assert f(idx=None) == INVALID
+    # one m-tile of users, at least two 64-deep slices of Ku, the sync words in their block
+    assert f(U=257, wsb=1 << 40) == UNSUPPORTED
+    assert "one launch" in L.ptg_last_error().decode()
+    assert f(Ku=64) == UNSUPPORTED
+    assert f(N=511 * 256 + 8, wsb=1 << 40) == UNSUPPORTED
+    assert f(wsb=need - 16) == WORKSPACE
+    assert f(ws=P + 8) == UNSUPPORTED
+    assert f(Mc=0, Xu=None, Xc=None, idx=None, W=None, Y=None, ws=None, wsb=0) == OK
+
+
 def test_wgrad_validation(L):
     need = L.ptg_grouped_gemm_wgrad_workspace()
     assert need == 256

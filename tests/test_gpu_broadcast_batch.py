@@ -107,6 +107,70 @@ def test_broadcast_large_tiles_runs_of_users_guard_rows(out_dtype):
     assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[Mc + 1]).all()), "guard rows written"
 
 
+@pytest.mark.parametrize("U,Ku,Kc,N,layout", [
+    (61, 1000, 200, 712, wl.B_KN),   # 8 user slices (the last short), 8 reduction rows per unit
+    (61, 1000, 200, 712, wl.B_NK),
+    (256, 136, 72, 264, wl.B_KN),    # the most users in one m-tile, 3 slices
+    (7, 72, 40, 136, wl.B_NK),       # 2 slices (the second 8 deep), one ragged column block
+])
+def test_broadcast_fused_exact(U, Ku, Kc, N, layout):
+    """The one-launch form: user units write partial products, reduction units sum them into P
+    once every partial of their column block has arrived, candidate tiles start from P once
+    their column block is ready.  Integer data with a bias, candidates in runs of one user, a
+    ragged last column block and tile: bit-exact against the oracle in both output types; the
+    rows around the output (NaN sentinels) untouched; a second call on the same workspace (whose
+    flags, partials and P the first call left behind) bit-identical."""
+    rng = np.random.default_rng(U * 7 + N + layout)
+    counts = rng.integers(1, 2 * 4000 // U, U)  # about 4000 candidates
+    idx = np.repeat(np.arange(U), counts).astype(np.int32)
+    Mc = int(idx.size)
+    Xu, Xc = int_bf16(rng, (U, Ku)), int_bf16(rng, (Mc, Kc))
+    W = int_bf16(rng, (Ku + Kc, N))
+    Wl = W if layout == wl.B_KN else np.ascontiguousarray(W.T)
+    bias = rng.integers(-8, 9, N).astype(np.float32)
+    v = oracle.broadcast_gemm(Xu, Xc, idx, Wl, layout, bias, wl.EPI_BIAS)
+    ws = torch.empty(ptg.broadcast_gemm_fused_workspace(U, N), dtype=torch.uint8, device="cuda")
+    args = (dev_bf16(Xu), dev_bf16(Xc), dev(idx), dev_bf16(Wl))
+    for out_dtype in (torch.float32, torch.bfloat16):
+        first = None
+        for call in range(2):
+            buf = torch.full((Mc + 2, N), float("nan"), dtype=out_dtype, device="cuda")
+            out = buf[1:Mc + 1]
+            ptg.broadcast_gemm_fused(*args, w_layout=layout, out=out, bias=dev(bias), epi=wl.EPI_BIAS,
+                                     workspace=ws)
+            exact(out, v, f"broadcast U={U} Ku={Ku} N={N} layout={layout} {out_dtype} call {call}")
+            assert bool(torch.isnan(buf[0]).all()) and bool(torch.isnan(buf[Mc + 1]).all()), "guard rows written"
+            if first is None:
+                first = out.clone()
+            else:
+                assert torch.equal(first, out), "second call differs"
+
+
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_broadcast_fused_silu_matches_oracle(shuffle):
+    """The one-launch form with the fused bias and SiLU on N(0,1) data, candidates in runs of
+    one user or shuffled, against the fp64 oracle."""
+    w = wl.broadcast(77, 40, 768, 320, 1024, cmin=20, cmax=400, w_layout=wl.B_NK, with_bias=True,
+                     shuffle=shuffle)
+    out = ptg.broadcast_gemm_fused(dev_bf16(w.Xu), dev_bf16(w.Xc), dev(w.idx), dev_bf16(w.W),
+                                   w_layout=w.w_layout, out_dtype=torch.float32, bias=dev(w.bias),
+                                   epi=wl.EPI_BIAS_SILU)
+    v = oracle.broadcast_gemm(w.Xu, w.Xc, w.idx, w.W, w.w_layout, w.bias, wl.EPI_BIAS_SILU)
+    check(out, v, w.Ku + w.Kc, f"broadcast fused, bias + SiLU, shuffle={shuffle}")
+
+
+def test_broadcast_fused_refuses_what_one_launch_cannot_do():
+    """More users than one m-tile, or a user reduction of one k-step, is refused (the
+    stream-ordered ptg_broadcast_gemm covers them)."""
+    rng = np.random.default_rng(5)
+    for U, Ku in ((300, 256), (4, 64)):
+        Xu, Xc = int_bf16(rng, (U, Ku)), int_bf16(rng, (10, 64))
+        W = int_bf16(rng, (Ku + 64, 128))
+        idx = (np.arange(10) % U).astype(np.int32)
+        with pytest.raises(ptg.PtgError):
+            ptg.broadcast_gemm_fused(dev_bf16(Xu), dev_bf16(Xc), dev(idx), dev_bf16(W))
+
+
 def test_broadcast_check_helper():
     idx = torch.tensor([0, 1, 4, 2], dtype=torch.int32, device="cuda")
     with pytest.raises(ptg.PtgError) as e:
@@ -125,9 +189,10 @@ def test_config4_ikbo_sampled():
     v = oracle.broadcast_gemm(w.Xu, w.Xc, w.idx, w.W, w.w_layout, rows=rows)
     args = (dev_bf16(w.Xu), dev_bf16(w.Xc), dev(w.idx), dev_bf16(w.W))
     idx = torch.from_numpy(rows).cuda()
-    for out_dtype in (torch.bfloat16, torch.float32):
-        out = ptg.broadcast_gemm(*args, out_dtype=out_dtype)
-        check(out[idx], v, w.Ku + w.Kc, f"config4 {out_dtype}")
+    for fn in (ptg.broadcast_gemm, ptg.broadcast_gemm_fused):
+        for out_dtype in (torch.bfloat16, torch.float32):
+            out = fn(*args, out_dtype=out_dtype)
+            check(out[idx], v, w.Ku + w.Kc, f"config4 {fn.__name__} {out_dtype}")
 
 
 # ------------------------------------------------------------------------------------------

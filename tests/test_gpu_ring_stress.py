@@ -10,7 +10,8 @@ a sum.
 Cases: the large tile (two 64 KB slots, register-staged producers) on long reductions (64
 k-steps per tile) in both B layouts; the medium tile (four slots, buffer-to-LDS producers, two
 ping-pong consumer groups); the grouped GEMM with empty experts and a column-split last round;
-the weight gradient's dynamic tile queue; the pointer-array batch.
+the weight gradient's dynamic tile queue; the pointer-array batch; the broadcast GEMM's one-launch
+form, whose reduction units and candidate tiles wait on other workgroups' results.
 """
 import contextlib
 
@@ -157,3 +158,22 @@ def test_stress_grouped_split_reduction(delay_lib):
             Y = torch.full((int(off[-1]), N), float("nan"), dtype=torch.float32, device="cuda")
             ptg.grouped_gemm(dev_bf16(X), dev_bf16(W), dev(off), out=Y, workspace=ws)
             exact(Y, v, "stress grouped split")
+
+
+def test_stress_broadcast_fused(delay_lib):
+    """User units, reduction units and candidate tiles of one launch, with the pauses shifting
+    which workgroup reaches which unit when: bit-exact, twice on one workspace."""
+    rng = np.random.default_rng(64)
+    U, Ku, Kc, N = 64, 2048, 512, 1024
+    idx = np.repeat(np.arange(U), rng.integers(10, 40, U)).astype(np.int32)
+    Mc = int(idx.size)
+    Xu, Xc, W = int_bf16(rng, (U, Ku)), int_bf16(rng, (Mc, Kc)), int_bf16(rng, (Ku + Kc, N))
+    bias = rng.integers(-8, 9, N).astype(np.float32)
+    v = oracle.broadcast_gemm(Xu, Xc, idx, W, wl.B_KN, bias, wl.EPI_BIAS)
+    with using(delay_lib):
+        ws = torch.empty(ptg.broadcast_gemm_fused_workspace(U, N), dtype=torch.uint8, device="cuda")
+        for call in range(2):
+            out = ptg.broadcast_gemm_fused(dev_bf16(Xu), dev_bf16(Xc), dev(idx), dev_bf16(W),
+                                           out_dtype=torch.float32, bias=dev(bias), epi=wl.EPI_BIAS,
+                                           workspace=ws)
+            exact(out, v, f"stress broadcast fused, call {call}")
