@@ -290,7 +290,14 @@ def secondary(torch, np, ptg, wl, steps, warmup, cold_reps=20, warm_s=0.2, cpu=T
                                       f"{n} random candidate rows of {w.Mc}, materialised [Xu[idx] | Xc] . W "
                                       f"(flops as computed)")
     out["broadcast_ikbo_64users_81403cand"] = e
-    del Xu, Xc, idx, W, Y, ws
+    # the same workload through the one-launch form (ptg_broadcast_gemm_fused)
+    wsf = torch.empty(ptg.broadcast_gemm_fused_workspace(w.U, w.N), dtype=torch.uint8, device="cuda")
+    call = lambda: ptg.broadcast_gemm_fused(Xu, Xc, idx, W, out=Y, workspace=wsf)  # noqa: E731
+    _, ms = time_calls(call, steps, warmup, torch, min_warm_s=warm_s)
+    out["broadcast_ikbo_64users_81403cand_fused"] = entry(
+        f, b, ms, time_cold(call, cold_reps, torch), entry_point="ptg_broadcast_gemm_fused",
+        note="one persistent launch; the stream-ordered ptg_broadcast_gemm above is the faster path")
+    del Xu, Xc, idx, W, Y, ws, wsf
     # IKBO attention: 64 users (C_u ~ U{256..2048}), context of 1024 keys, 4 heads of 128
     w = wl.ikbo_attention_workload()
     Q, K, V = (to_dev(w.Q.reshape(w.Mc, -1), torch, np).view(w.Mc, w.H, w.D),
