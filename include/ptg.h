@@ -46,6 +46,14 @@
  *     watchdog bit and leaves its output incomplete.  The enqueueing call has already
  *     returned PTG_OK by then: ptg_watchdog() reports it, and the *_check helpers return
  *     PTG_ERR_DEVICE_CHECK while the current device's watchdog word is nonzero.
+ *   - Debug switches, read from the environment at every call (set and not "0" turns one
+ *     on).  PTG_LOG: each launch prints its entry point, shape and tile configuration to
+ *     stderr.  PTG_CHECK: the calls whose inputs include device-resident bookkeeping
+ *     (ptg_grouped_gemm, ptg_grouped_gemm_split and ptg_grouped_gemm_wgrad: group offsets;
+ *     ptg_ikbo_attention: user offsets; the ptg_broadcast_gemm family: user indices) first
+ *     run the matching *_check helper, which synchronises the stream, and return its error
+ *     (PTG_ERR_DEVICE_CHECK) instead of launching.  Both are for debugging: PTG_CHECK makes
+ *     those calls wait for the stream.
  */
 #ifndef PTG_H_
 #define PTG_H_

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <algorithm>
@@ -46,6 +47,26 @@ bool bad_dim(int64_t x) { return x < 0; }
   } catch (...) {                                                      \
     return fail(PTG_ERR_HIP, "internal error");                        \
   }
+
+// Debug switches, read from the environment at every call (set and not "0": on).
+//   PTG_LOG    each launch prints its entry point, shape and tile configuration to stderr.
+//   PTG_CHECK  entry points whose inputs include device-resident bookkeeping (group or user
+//              offsets, user indices) first run that bookkeeping's device check, which
+//              synchronises the stream, and return its error instead of launching.
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+void log_launch(const char* fmt, ...) {
+  if (!env_on("PTG_LOG")) return;
+  char line[384];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[ptg] %s\n", line);
+}
 
 bool valid_epi(int e) { return e >= PTG_EPI_NONE && e <= PTG_EPI_BIAS_SILU; }
 bool needs_bias(int e) { return e == PTG_EPI_BIAS || e == PTG_EPI_BIAS_SILU; }
@@ -143,6 +164,11 @@ ptg_status ptg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
     d.lda = lda; d.ldb = ldb; d.ldc = ldc;
     d.M = M; d.N = N; d.K = K;
     d.b_kn = kn; d.epi = epi; d.out_f32 = c_dtype == PTG_F32;
+    int32_t cfg[6];
+    ptg::dense_config(M, N, K, kn, cfg);
+    log_launch("%s M=%lld N=%lld K=%lld %s %s: tile %dx%dx%d, %d slots, %d consumer and %d producer waves", fn,
+               (long long)M, (long long)N, (long long)K, kn ? "KN" : "NK", d.out_f32 ? "fp32" : "bf16", cfg[0], cfg[1],
+               cfg[2], cfg[3], cfg[4], cfg[5]);
     hipError_t e = ptg::launch_dense(d, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
@@ -199,6 +225,13 @@ ptg_status grouped_call(const char* fn, int32_t G, int64_t M_total, int64_t N, i
     g.X = X; g.W = W; g.Y = Y; g.bias = needs_bias(epi) ? bias : nullptr; g.offsets = group_offsets;
     g.M_total = M_total; g.N = N; g.K = K; g.G = G;
     g.b_kn = kn; g.epi = epi; g.out_f32 = y_dtype == PTG_F32;
+    if (env_on("PTG_CHECK")) {
+      st = ptg_grouped_gemm_check(G, M_total, group_offsets, stream);
+      if (st) return st;
+    }
+    log_launch("%s G=%d M_total=%lld N=%lld K=%lld %s %s: tile 256x256x64, 2 slots, 8 consumer and 4 producer waves%s",
+               fn, G, (long long)M_total, (long long)N, (long long)K, kn ? "KN" : "NK", g.out_f32 ? "fp32" : "bf16",
+               with_ws ? ", last round split through the workspace" : "");
     hipError_t e = ptg::launch_grouped(g, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
@@ -263,6 +296,13 @@ ptg_status ptg_grouped_gemm_wgrad(int32_t G, int64_t M_total, int64_t K, int64_t
     w.X = X; w.dY = dY; w.dW = dW; w.offsets = group_offsets; w.workspace = workspace;
     w.M_total = M_total; w.K = K; w.N = N; w.G = G;
     w.out_f32 = dw_dtype == PTG_F32;
+    if (env_on("PTG_CHECK")) {
+      const ptg_status st = ptg_grouped_gemm_check(G, M_total, group_offsets, stream);
+      if (st) return st;
+    }
+    log_launch("%s G=%d M_total=%lld K=%lld N=%lld %s: tile 256x256x64 (A staged K x M), 2 slots, 8 consumer and 4 "
+               "producer waves, tiles from per-XCD queues", fn, G, (long long)M_total, (long long)K, (long long)N,
+               w.out_f32 ? "fp32" : "bf16");
     hipError_t e = ptg::launch_grouped_wgrad(w, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
@@ -294,6 +334,12 @@ ptg_status ptg_ikbo_attention(int64_t U, int64_t Mc, int64_t H, int64_t D, int64
     ptg::AttentionLaunch a{};
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.offsets = user_offsets;
     a.U = U; a.Mc = Mc; a.H = H; a.L = L; a.scale = scale; a.out_f32 = o_dtype == PTG_F32;
+    if (env_on("PTG_CHECK")) {
+      const ptg_status st = ptg_grouped_gemm_check((int32_t)U, Mc, user_offsets, stream);
+      if (st) return st;
+    }
+    log_launch("%s U=%lld Mc=%lld H=%lld D=%lld L=%lld %s: 128 candidates per tile, 64-key blocks in 4 slots", fn,
+               (long long)U, (long long)Mc, (long long)H, (long long)D, (long long)L, a.out_f32 ? "fp32" : "bf16");
     hipError_t e = ptg::launch_attention(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
@@ -535,6 +581,8 @@ ptg_status ptg_grouped_gemm_ptr_array_run(int32_t count, const void* workspace, 
     if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
     ptg::BatchLaunch b{};
     b.workspace = workspace; b.count = count; b.epi = epi; b.out_f32 = c_dtype == PTG_F32;
+    log_launch("%s count=%d %s: tile 128x128x64, 4 slots, 2 groups of 4 consumer waves, 2 producer waves", fn, count,
+               b.out_f32 ? "fp32" : "bf16");
     hipError_t e = ptg::launch_batch(b, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
@@ -619,6 +667,10 @@ ptg_status broadcast_call(const char* fn, int64_t U, int64_t Mc, int64_t Ku, int
       return fail(PTG_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
     if (!aligned16(workspace)) return fail(PTG_ERR_UNSUPPORTED, "%s: workspace must be 16-byte aligned", fn);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (env_on("PTG_CHECK")) {
+      st = ptg_broadcast_gemm_check(U, Mc, user_idx, stream);
+      if (st) return st;
+    }
     if (fused) {
       // User units (slice s of Ku for one 256-column block, its fp32 partial product to the
       // workspace), reduction units (rows of P summed from the partials once all have
@@ -633,6 +685,8 @@ ptg_status broadcast_call(const char* fn, int64_t U, int64_t Mc, int64_t Ku, int
       b.sync_bytes = ptg::broadcast_sync_bytes(N, ptg::kBroadcastMaxSlices);
       b.b_kn = kn; b.epi = epi; b.out_f32 = y_dtype == PTG_F32;
       b.epoch = next_epoch();
+      log_launch("%s U=%lld Mc=%lld Ku=%lld Kc=%lld N=%lld: one launch, %d user slices of %lld, tile 256x256x64", fn,
+                 (long long)U, (long long)Mc, (long long)Ku, (long long)Kc, (long long)N, splits1, (long long)chunk1);
       const hipError_t e = ptg::launch_broadcast_single(b, s);
       if (e != hipSuccess) return hip_fail(e, fn);
       return PTG_OK;
@@ -651,6 +705,16 @@ ptg_status broadcast_call(const char* fn, int64_t U, int64_t Mc, int64_t Ku, int
     const int32_t max_splits = ptg::broadcast_user_splits(U, N);
     const int64_t chunk = ((Ku + max_splits - 1) / max_splits + 63) / 64 * 64;  // whole k-steps
     const int32_t splits = (int32_t)((Ku + chunk - 1) / chunk);
+    {
+      int32_t cu[6];
+      int32_t cc[6];
+      ptg::dense_config(U, N, Ku, kn, cu);
+      ptg::dense_config(Mc, N, Kc, kn, cc);
+      log_launch("%s U=%lld Mc=%lld Ku=%lld Kc=%lld N=%lld: user phase tile %dx%dx%d in %d slices of %lld%s, "
+                 "candidate phase tile %dx%dx%d", fn, (long long)U, (long long)Mc, (long long)Ku, (long long)Kc,
+                 (long long)N, cu[0], cu[1], cu[2], splits, (long long)chunk, splits > 1 ? " + ordered reduction" : "",
+                 cc[0], cc[1], cc[2]);
+    }
     hipError_t e;
     if (splits > 1) {
       u.C = P + U * N;
