@@ -159,6 +159,28 @@ def test_broadcast_fused_silu_matches_oracle(shuffle):
     check(out, v, w.Ku + w.Kc, f"broadcast fused, bias + SiLU, shuffle={shuffle}")
 
 
+def test_broadcast_fused_full_workload_integer_exact():
+    """The 64-user workload's shapes and user run lengths (81,403 candidates, [2048 | 512] ->
+    1024) on integer data, where every sum is exact: the one-launch form equals the
+    stream-ordered path on every element, and both equal the oracle on sampled rows (the first
+    and last candidate of every user among them)."""
+    w = wl.config4()
+    rng = np.random.default_rng(44)
+    Xu, Xc = int_bf16(rng, (w.U, w.Ku), -2, 2), int_bf16(rng, (w.Mc, w.Kc), -2, 2)
+    W = int_bf16(rng, (w.Ku + w.Kc, w.N), -2, 2)
+    bias = rng.integers(-8, 9, w.N).astype(np.float32)
+    args = (dev_bf16(Xu), dev_bf16(Xc), dev(w.idx), dev_bf16(W))
+    kw = dict(w_layout=wl.B_KN, out_dtype=torch.float32, bias=dev(bias), epi=wl.EPI_BIAS)
+    plain = ptg.broadcast_gemm(*args, **kw)
+    fused = ptg.broadcast_gemm_fused(*args, **kw)
+    assert torch.equal(plain, fused), "the one-launch form differs from the stream-ordered path"
+    starts = np.concatenate([[0], np.cumsum(w.counts)])
+    rows = set(sample_rows(w.Mc, 48, 5).tolist()) | set(starts[:-1].tolist()) | set((starts[1:] - 1).tolist())
+    rows = np.array(sorted(rows), dtype=np.int64)
+    v = oracle.broadcast_gemm(Xu, Xc, w.idx, W, wl.B_KN, bias, wl.EPI_BIAS, rows=rows)
+    exact(fused[torch.from_numpy(rows).cuda()], v, "broadcast fused, full workload, sampled rows")
+
+
 def test_broadcast_fused_refuses_what_one_launch_cannot_do():
     """More users than one m-tile, or a user reduction of one k-step, is refused (the
     stream-ordered ptg_broadcast_gemm covers them)."""
