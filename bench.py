@@ -426,6 +426,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(), "kernel_ms": round(ev_ms, 4)},
     }
+    # Context, not the target: the vendor GEMM (torch.mm, which calls hipBLASLt) on the same
+    # inputs and output, timed the same way right after, on the same part at the same clock.
+    vendor = lambda: torch.mm(A, B.t(), out=C)  # noqa: E731
+    v_wall, v_ev = time_calls(vendor, args.steps, args.warmup, torch, min_warm_s=args.warm_s)
+    line["vendor_reference"] = {"library": "torch.mm (hipBLASLt)", "ms_per_step": round(v_wall * 1e3, 4),
+                                "tflops": round(flops / v_wall / 1e12, 2),
+                                "pct_peak": round(100 * flops / v_wall / 1e12 / PEAK_TFLOPS, 2)}
     del A, B, C
     torch.cuda.empty_cache()
     if args.copy_probe:
