@@ -101,8 +101,11 @@ bool out_fits(int64_t ldc, int64_t osz) {
 // bounded wait or a range check, and its output is incomplete) is reported as a failed check.
 ptg_status watchdog_status(const char* fn) {
   uint32_t gemm = 0, attention = 0;
+  uint32_t onerole = 0;
   hipError_t e = ptg::read_watchdog(&gemm, 0);
   if (e == hipSuccess) e = ptg::read_attention_watchdog(&attention, 0);
+  if (e == hipSuccess) e = ptg::read_onerole_watchdog(&onerole, 0);
+  gemm |= onerole;
   if (e != hipSuccess) return hip_fail(e, fn);
   if (gemm | attention)
     return fail(PTG_ERR_DEVICE_CHECK, "%s: the device's watchdog word is 0x%x (an earlier launch stopped early)",
@@ -166,9 +169,14 @@ ptg_status ptg_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
     d.b_kn = kn; d.epi = epi; d.out_f32 = c_dtype == PTG_F32;
     int32_t cfg[6];
     ptg::dense_config(M, N, K, kn, cfg);
-    log_launch("%s M=%lld N=%lld K=%lld %s %s: tile %dx%dx%d, %d slots, %d consumer and %d producer waves", fn,
-               (long long)M, (long long)N, (long long)K, kn ? "KN" : "NK", d.out_f32 ? "fp32" : "bf16", cfg[0], cfg[1],
-               cfg[2], cfg[3], cfg[4], cfg[5]);
+    if (cfg[5] == 0)
+      log_launch("%s M=%lld N=%lld K=%lld %s %s: tile %dx%dx%d, %d slots, %d waves each copying and computing", fn,
+                 (long long)M, (long long)N, (long long)K, kn ? "KN" : "NK", d.out_f32 ? "fp32" : "bf16", cfg[0],
+                 cfg[1], cfg[2], cfg[3], cfg[4]);
+    else
+      log_launch("%s M=%lld N=%lld K=%lld %s %s: tile %dx%dx%d, %d slots, %d consumer and %d producer waves", fn,
+                 (long long)M, (long long)N, (long long)K, kn ? "KN" : "NK", d.out_f32 ? "fp32" : "bf16", cfg[0],
+                 cfg[1], cfg[2], cfg[3], cfg[4], cfg[5]);
     hipError_t e = ptg::launch_dense(d, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, fn);
     return PTG_OK;
@@ -820,10 +828,12 @@ ptg_status ptg_watchdog(uint32_t* value, int32_t clear) {
     if (!value) return fail(PTG_ERR_INVALID_ARG, "ptg_watchdog: value is NULL");
     uint32_t gemm = 0;
     uint32_t attention = 0;
+    uint32_t onerole = 0;
     hipError_t e = ptg::read_watchdog(&gemm, clear);
     if (e == hipSuccess) e = ptg::read_attention_watchdog(&attention, clear);
+    if (e == hipSuccess) e = ptg::read_onerole_watchdog(&onerole, clear);
     if (e != hipSuccess) return hip_fail(e, "ptg_watchdog");
-    *value = gemm | attention;
+    *value = gemm | attention | onerole;
     return PTG_OK;
   })
 }

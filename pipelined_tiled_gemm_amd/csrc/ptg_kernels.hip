@@ -788,7 +788,12 @@ static bool use_large(int64_t M, int64_t N) {
 }
 
 void dense_config(int64_t M, int64_t N, int64_t K, int b_kn, int32_t cfg[6]) {
-  (void)K;
+  DenseLaunch probe{};
+  probe.M = M; probe.N = N; probe.K = K; probe.b_kn = b_kn;
+  if (onerole_fits(probe)) {
+    onerole_describe(cfg);
+    return;
+  }
   if (use_large(M, N)) {
     if (b_kn) describe<CfgLarge<true>>(cfg); else describe<CfgLarge<false>>(cfg);
   } else {
@@ -837,6 +842,7 @@ static hipError_t launch_dense_cfg(const DenseLaunch& d, hipStream_t stream) {
 
 hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream) {
   if (d.M == 0 || d.N == 0) return hipSuccess;
+  if (onerole_fits(d)) return launch_onerole(d, stream);
   if (use_large(d.M, d.N)) {
     return d.b_kn ? launch_dense_cfg<CfgLarge<true>>(d, stream) : launch_dense_cfg<CfgLarge<false>>(d, stream);
   }

@@ -128,6 +128,13 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int kBatchBM = 128, kBatchBN = 128;
 
 hipError_t launch_dense(const DenseLaunch& d, hipStream_t stream);
+
+// The one-role dense kernel (every wave both copies and computes; 256 x 256 x 32 tiles, three
+// LDS slots): second operand N x K, K a multiple of 32, no split, at least 128 tiles.
+// launch_dense takes it whenever onerole_fits holds.
+bool onerole_fits(const DenseLaunch& d);
+hipError_t launch_onerole(const DenseLaunch& d, hipStream_t stream);
+void onerole_describe(int32_t cfg[6]);
 // out[i] = sum over s of parts[s * count + i] (s ascending), plus bias[i % n] if bias.
 hipError_t launch_reduce_splits(float* out, const float* parts, int64_t count, int32_t splits,
                                 const float* bias, int64_t n, hipStream_t stream);
@@ -194,6 +201,7 @@ void dense_config(int64_t M, int64_t N, int64_t K, int b_kn, int32_t cfg[6]);
 // Watchdog words of the bounded waits (nonzero if a wait ever gave up): the GEMM kernels'
 // word and the attention kernel's word.
 hipError_t read_watchdog(uint32_t* value, int clear);
+hipError_t read_onerole_watchdog(uint32_t* value, int clear);
 hipError_t read_attention_watchdog(uint32_t* value, int clear);
 
 }  // namespace ptg

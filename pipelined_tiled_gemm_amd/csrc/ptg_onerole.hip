@@ -1,0 +1,391 @@
+// ptg_onerole.hip - the one-role dense GEMM kernel and its watchdog word.
+//
+// The pipelined tiled GEMM of "Introducing TLX" (listing 1: acc = 0; for each K block load the
+// A and B tiles, acc += A.B; store), with the loads run ahead of the matrix work through a ring
+// of LDS slots as the warp-specialised kernels of that page and of "How We Built TLX" do.  Here
+// the roles are not split over separate waves: each of the four waves issues a quarter of every
+// k-step's memory-to-LDS copies and computes a 128 x 128 quarter of the 256 x 256 output tile.
+// With one wave per SIMD a wave stall is a matrix-core stall, so the loop is written for an
+// uninterrupted instruction stream:
+//   - copies go straight from memory into LDS (buffer loads with the LDS flag), each wave's
+//     copies of step st + 3 issued between the MFMAs of step st: three 32-deep slots of 32 KB;
+//   - the k-loop is unrolled over the ring, so every fragment read is a fixed per-lane base
+//     register plus an immediate offset: no address arithmetic sits between the MFMAs;
+//   - the MFMAs are inline asm, which fixes the issue order of every LDS and memory access
+//     between them to the source order.
+// One barrier per step.  Before it, each wave waits for its own copies of step st + 1 and for
+// its reads of step st's slot (its fragments were read during step st - 1).  After it, step
+// st + 1 is complete in LDS and step st's slot is free for step st + 3, which takes the same
+// slot (mod 3).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "ptg_device.hpp"
+#include "ptg_launch.h"
+
+namespace ptg {
+
+namespace {
+
+// 256 x 256 x 32 tile, three slots; 2 x 2 waves of 128 x 128 (16 x 16 MFMA blocks); the
+// producer count (4) fixes each wave's share of a step's 1 KB copies (8)
+using CfgOneRole = Cfg<256, 256, 32, 3, 2, 2, 4, false, 1, true, false, false, 1>;
+
+struct OneRoleArgs {
+  const __bf16* A;
+  const __bf16* B;
+  char* C;
+  const float* bias;
+  int64_t lda, ldb, ldc;
+  int32_t M, N, K;
+  int32_t tiles_m, tiles_n;
+  int32_t epi, out_f32;
+  Guards guard;
+};
+
+// Tile L of the launch order.  Tiles are taken in blocks of 16 x 16 (row-major over block
+// rows, the block columns of odd block rows in reverse, so that consecutive blocks share a
+// panel of A or of B); inside a block, in strips of four tile rows taken column by column.
+// A persistent launch of 256 workgroups runs tiles j * 256 + xcd_rank(w): round j is one
+// block, and the 32 workgroups of one XCD (one L2) take a 4 x 8 patch of it, which reads 4
+// panels of A and 8 of B.  Edge blocks and strips are smaller; the order stays a bijection.
+__device__ __forceinline__ void onerole_tile(uint64_t L, uint32_t tiles_m, uint32_t tiles_n, int& tm, int& tn) {
+  // unsigned throughout: every quantity is nonnegative, and 32-bit values widen by zero
+  // extension
+  const uint64_t row_tiles = 16ull * tiles_n;
+  const uint32_t bi = (uint32_t)(L / row_tiles);
+  uint64_t in = L - (uint64_t)bi * row_tiles;
+  const uint32_t bm = min(16u, tiles_m - 16u * bi);
+  const uint32_t nbj = (tiles_n + 15u) / 16u;
+  const uint32_t last_bn = tiles_n - 16u * (nbj - 1u);
+  uint32_t bj, bn;
+  if ((bi & 1u) == 0) {
+    bj = (uint32_t)(in / (16ull * bm));
+    in -= (uint64_t)bj * 16u * bm;
+    bn = min(16u, tiles_n - 16u * bj);
+  } else if (in < (uint64_t)last_bn * bm) {
+    // odd block row: the (possibly narrower) last block column comes first
+    bj = nbj - 1u;
+    bn = last_bn;
+  } else {
+    in -= (uint64_t)last_bn * bm;
+    const uint32_t e = 1u + (uint32_t)(in / (16ull * bm));
+    in -= (uint64_t)(e - 1u) * 16u * bm;
+    bj = nbj - 1u - e;
+    bn = 16u;
+  }
+  const uint32_t s = (uint32_t)(in / (4ull * bn));
+  const uint32_t in3 = (uint32_t)(in - (uint64_t)s * 4u * bn);
+  const uint32_t sm = min(4u, bm - 4u * s);
+  tm = (int)(16u * bi + 4u * s + in3 % sm);
+  tn = (int)(16u * bj + in3 / sm);
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
+  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
+  constexpr int S = C::STAGES, L = C::LOADS;
+  constexpr int D = S;                       // copies run S steps ahead of the matrix work
+  static_assert(C::BK == 32 && !C::B_KN && L == 8 && S == 3, "three 32-deep N x K slots, 8 copies per wave");
+  constexpr int TM = C::TM16, TN = C::TN16;  // 8 x 8 blocks of 16 x 16 per wave
+  static_assert(TM == 8 && TN == 8, "128 x 128 per wave");
+  const int w = (int)uni(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int wm = w >> 1, wn = w & 1;
+  const int i0 = w * L;                      // this wave's copies: 1 KB chunks i0 .. i0 + 7
+  const bool opA = i0 < C::A_INSTR;
+  const int wave_lds = opA ? i0 * 1024 : C::A_BYTES + (i0 - C::A_INSTR) * 1024;
+
+  // Fragment bases: lane l reads row (l mod 16) of a 16-row block, 16-byte k-chunk l / 16
+  // (swizzled as the copies laid it out).  Slots 0 and 1 through base 0, slot 2 through base 1
+  // (a read's immediate offset holds 16 bits).  Opaque, so that they stay in registers instead
+  // of being re-derived inside the loop.
+  const int ra = wm * C::WTM + (lane & 15);
+  const int rb = wn * C::WTN + (lane & 15);
+  int a0 = ra * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_A>(ra)) << 4);
+  int b0 = C::A_BYTES + rb * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_B>(rb)) << 4);
+  int a1 = a0 + 2 * C::STAGE_BYTES, b1 = b0 + 2 * C::STAGE_BYTES;
+  asm volatile("" : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1));
+  // Every lambda of the kernel is forced inline: one left out of line takes the accumulators
+  // by reference through memory, and stores them right after an asm MFMA whose results the
+  // compiler does not know to wait for.
+  auto rd = [&](int base, int imm) __attribute__((always_inline)) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(ring + base + imm); };
+  auto frag_a = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? a0 : a1, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
+  auto frag_b = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? b0 : b1, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
+
+  const uint64_t ntiles = (uint64_t)(uint32_t)args.tiles_m * (uint32_t)args.tiles_n;
+  const int K = args.K;
+  const int nsteps = K / C::BK;
+  const Guards& gd = args.guard;
+  // sizes and leading dimensions are nonnegative: unsigned 64-bit address arithmetic
+  const uint64_t lda = (uint64_t)args.lda, ldb = (uint64_t)args.ldb, ldc = (uint64_t)args.ldc;
+  for (uint64_t Lt = (uint64_t)xcd_rank(blockIdx.x, gridDim.x); Lt < ntiles; Lt += gridDim.x) {
+    int tm = 0, tn = 0;
+    onerole_tile(Lt, (uint32_t)args.tiles_m, (uint32_t)args.tiles_n, tm, tn);
+    const uint32_t m0 = (uint32_t)tm * C::BM, n0 = (uint32_t)tn * C::BN;
+    const int m_rows = min(C::BM, args.M - (int)m0);
+    const int n_cols = min(C::BN, args.N - (int)n0);
+    const uint64_t ld = opA ? lda : ldb;
+    const int extent = opA ? m_rows : n_cols;
+    const uint64_t src = uni64(reinterpret_cast<uint64_t>(opA ? args.A + m0 * lda : args.B + n0 * ldb));
+    uint32_t bytes = (uint32_t)((uint64_t)(uint32_t)(extent - 1) * ld * 2u + (uint64_t)(uint32_t)K * 2u);
+    if (!inside(src, bytes, uni64(opA ? gd.a_lo : gd.b_lo), uni64(opA ? gd.a_hi : gd.b_hi))) {
+      if (lane == 0) atomicOr(&g_watchdog, 4u);
+      bytes = 0;  // nothing is read: the tile's operand is all zeros
+    }
+    bytes = uni(bytes);
+    // per-lane offset of each copy; rows past the tile take an out-of-range offset (zeros)
+    uint32_t voff[L];
+#pragma unroll
+    for (int q = 0; q < L; ++q) {
+      int row, c;
+      chunk_of<C>(i0 + q, lane, row, c);
+      voff[q] = row < extent ? (uint32_t)(row * ld * 2 + c * 16) : kOutOfRange;
+    }
+    // step st's copy q into slot sl: the k-step moves the descriptor base; a step past K
+    // gets an empty descriptor (no access, zeros)
+    auto copy = [&](int st, int sl, int q) __attribute__((always_inline)) {
+      const uint32_t kbytes = (uint32_t)st * C::BK * 2u;
+      const uint32_t rem = kbytes < bytes ? bytes - kbytes : 0u;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const void*>(src + (rem ? kbytes : 0)), rem);
+      dma16(rs, ring + sl * C::STAGE_BYTES + wave_lds + q * 1024, voff[q], 0u);
+    };
+
+    // accumulators start at the bias (bias epilogues) or zero; lane l holds columns
+    // 4 (l / 16) .. + 3 of each 16-column block
+    f32x4 acc[TM][TN];
+    {
+      const bool do_bias = (args.epi == EPI_BIAS || args.epi == EPI_BIAS_SILU) && args.bias != nullptr;
+      const uint64_t bp = uni64(reinterpret_cast<uint64_t>(args.bias + n0));
+      const bool bias_ok = do_bias && inside(bp, (uint64_t)n_cols * 4, uni64(gd.bias_lo), uni64(gd.bias_hi));
+      if (do_bias && !bias_ok && lane == 0) atomicOr(&g_watchdog, 8u);
+      const __amdgpu_buffer_rsrc_t rbias = make_rsrc(reinterpret_cast<const void*>(bp), bias_ok ? (uint32_t)n_cols * 4u : 0u);
+#pragma unroll
+      for (int y = 0; y < TN; ++y) {
+        const int col = wn * C::WTN + y * 16 + (lane >> 4) * 4;
+        const f32x4 b4 = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbias, col < n_cols ? col * 4 : kOutOfRange, 0, 0));
+#pragma unroll
+        for (int x = 0; x < TM; ++x) acc[x][y] = b4;
+      }
+    }
+    auto mf = [&](int x, int y, const bf16x8& fa, const bf16x8& fb) __attribute__((always_inline)) {
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[x][y]) : "v"(fb), "v"(fa));
+    };
+
+    // prologue: steps 0 .. D - 1 into slots 0 .. D - 1; step 0's fragments into registers
+    for (int st = 0; st < D; ++st)
+#pragma unroll
+      for (int q = 0; q < L; ++q) copy(st, st, q);
+    wait_vmcnt<(D - 1) * L>();
+    __builtin_amdgcn_s_barrier();
+    bf16x8 xa[TM], xb[TN], ya[TM], yb[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) xb[t] = frag_b(0, t);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) xa[t] = frag_a(0, t);
+    // the asm MFMAs do not show the compiler that they read the accumulators just written by
+    // ordinary vector instructions: wait states by hand
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+
+    // The stress build's pause is a small loop: a block boundary, after which the compiler may
+    // move accumulators, so the MFMAs' results are waited for first
+    auto pause = [&]() __attribute__((always_inline)) {
+#if PTG_DELAY_INJECT
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      stress_pause();
+#endif
+    };
+    // step st in slot SL = st mod 3 (compile time): its 64 MFMAs on fa/fb; between them, the
+    // copies of step st + 3 into slot SL (one per 8 MFMAs) and step st + 1's 16 fragments from
+    // slot SL + 1 (one per 3 MFMAs, all done well before the step's end)
+    auto body = [&](int st, auto SLc, const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN], bf16x8 (&na)[TM],
+                    bf16x8 (&nb)[TN]) __attribute__((always_inline)) {
+      constexpr int SL = decltype(SLc)::value;
+      pause();                     // the stress build skews the waves here (a no-op otherwise)
+      wait_vmcnt<(D - 2) * L>();   // this wave's copies of step st + 1 have landed
+      wait_lgkm0();                // and its reads of slot SL (step st's fragments) are done
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y) {
+          const int k = x * TN + y;
+          mf(x, y, fa[x], fb[y]);
+          if (k % 8 == 2) copy(st + D, SL, k / 8);
+          if (k == 35) pause();          // and between the copies and reads of a step
+          if (k % 3 == 0 && k / 3 < TN + TM) {
+            const int r = k / 3;
+            if (r < TN) nb[r] = frag_b((SL + 1) % S, r);
+            else na[r - TN] = frag_a((SL + 1) % S, r - TN);
+          }
+        }
+    };
+    auto last = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y) mf(x, y, fa[x], fb[y]);
+    };
+    // six steps per pass: two turns of the ring and an even number of x/y swaps
+    constexpr int U = 2 * S;
+    auto step_j = [&](int st0, auto Jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(Jc)::value;
+      if constexpr (J % 2 == 0) body(st0 + J, std::integral_constant<int, J % S>{}, xa, xb, ya, yb);
+      else body(st0 + J, std::integral_constant<int, J % S>{}, ya, yb, xa, xb);
+    };
+    // Where a block boundary follows an MFMA the compiler may move accumulators between
+    // registers (it does at the loop exit); it does not see that the asm MFMAs write them late,
+    // so 24 wait states (more than an MFMA's passes) come first
+    auto settle = [&]() __attribute__((always_inline)) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
+    int st = 0;
+    for (; st + U < nsteps; st += U) {
+      step_j(st, std::integral_constant<int, 0>{});
+      step_j(st, std::integral_constant<int, 1>{});
+      step_j(st, std::integral_constant<int, 2>{});
+      step_j(st, std::integral_constant<int, 3>{});
+      step_j(st, std::integral_constant<int, 4>{});
+      step_j(st, std::integral_constant<int, 5>{});
+      settle();
+    }
+    // 1 to 6 steps left, the first in slot 0 with its fragments in x
+    const int left = nsteps - st;
+    if (left >= 2) { step_j(st, std::integral_constant<int, 0>{}); settle(); }
+    if (left >= 3) { step_j(st, std::integral_constant<int, 1>{}); settle(); }
+    if (left >= 4) { step_j(st, std::integral_constant<int, 2>{}); settle(); }
+    if (left >= 5) { step_j(st, std::integral_constant<int, 3>{}); settle(); }
+    if (left >= 6) { step_j(st, std::integral_constant<int, 4>{}); settle(); }
+    if ((left - 1) & 1) {
+      wait_lgkm0();
+#pragma unroll
+      for (int t = 0; t < TM; ++t) xa[t] = ya[t];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) xb[t] = yb[t];
+    }
+    last(xa, xb);
+    // ... nor that the epilogue reads what they wrote: wait for the last MFMAs' results
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    // the copies issued past the last step (empty descriptors) have landed and every wave is
+    // done with the ring before the next tile's prologue refills it
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+
+    const uint32_t osz = args.out_f32 ? 4u : 2u;
+    const uint64_t Cp = uni64(reinterpret_cast<uint64_t>(args.C + ((uint64_t)m0 * ldc + n0) * osz));
+    const uint64_t c_bytes = ((uint64_t)(uint32_t)(m_rows - 1) * ldc + (uint32_t)n_cols) * osz;
+    if (!inside(Cp, c_bytes, uni64(gd.c_lo), uni64(gd.c_hi))) {
+      if (lane == 0) atomicOr(&g_watchdog, 8u);
+      continue;
+    }
+    // epilogue: SiLU if asked, conversion, whole 128-byte row segments per store (lane l
+    // holds columns 4 (l / 16) .. + 3 of each 16-column block, rows l mod 16)
+    const bool do_silu = args.epi == EPI_SILU || args.epi == EPI_BIAS_SILU;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)c_bytes);
+    // the lane index re-read here: offsets derived from it are not hoisted out of the tile loop
+    // (they would be held across the k-loop, where no register is free)
+    const int elane = opaque_lane();
+    const int grp = elane >> 4;
+    const int ldc_i = (int)args.ldc;
+#pragma unroll
+    for (int x = 0; x < TM; ++x) {
+      const int row0 = wm * C::WTM + x * 16;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4_t pair0 = {};
+#pragma unroll
+        for (int y0 = 0; y0 < 4; y0 += 2) {
+          const int y = 4 * h + y0;
+          f32x4 v0 = acc[x][y], v1 = acc[x][y + 1];
+          if (do_silu) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              v0[t] = silu(v0[t]);
+              v1[t] = silu(v1[t]);
+            }
+          }
+          if (args.out_f32) {
+            // blocks y and y + 1 of a row: 128 contiguous bytes
+            const int colX = wn * C::WTN + y * 16 + grp * 4;
+            store_rows128(__builtin_bit_cast(u32x4_t, v0), __builtin_bit_cast(u32x4_t, v1), colX, colX + 16, row0,
+                          elane, m_rows, n_cols, ldc_i, 4u, rc);
+          } else {
+            // bf16: runs of 4 packed to 8 bytes; v_permlane16_swap trades runs between the
+            // 16-lane groups so that group g holds columns 8 (g / 2) .. + 7 of block y + g % 2
+            const uint32_t x0 = pack_bf16(v0[0], v0[1]), x1 = pack_bf16(v0[2], v0[3]);
+            const uint32_t y0v = pack_bf16(v1[0], v1[1]), y1v = pack_bf16(v1[2], v1[3]);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0v, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1v, false, false);
+            const u32x4_t d = {s0[0], s1[0], s0[1], s1[1]};
+            if (y0 == 0) {
+              pair0 = d;
+            } else {
+              // the two block pairs y - 2 .. y + 1: 64 columns, 128 bytes per row
+              const int colX = wn * C::WTN + h * 64 + (grp & 1) * 16 + (grp >> 1) * 8;
+              store_rows128(pair0, d, colX, colX + 32, row0, elane, m_rows, n_cols, ldc_i, 2u, rc);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// [p, p + bytes), or the empty range when p is null
+void span(const void* p, uint64_t bytes, uint64_t& lo, uint64_t& hi) {
+  lo = p ? reinterpret_cast<uint64_t>(p) : 0;
+  hi = p ? reinterpret_cast<uint64_t>(p) + bytes : 0;
+}
+
+// bytes of a row-major [rows x cols] matrix with row stride ld (elements of esize bytes)
+uint64_t mat_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+  return rows > 0 ? (uint64_t)(((rows - 1) * ld + cols) * esize) : 0;
+}
+
+}  // namespace
+
+bool onerole_fits(const DenseLaunch& d) {
+  // N x K second operand, 32-deep k-steps, enough 256 x 256 tiles to fill the chip, no split
+  return !d.b_kn && d.K % 32 == 0 && d.splits <= 1 && d.gidx == nullptr && d.P == nullptr &&
+         ((d.M + 255) / 256) * ((d.N + 255) / 256) >= 128;
+}
+
+hipError_t launch_onerole(const DenseLaunch& d, hipStream_t stream) {
+  using C = CfgOneRole;
+  OneRoleArgs a{};
+  a.A = reinterpret_cast<const __bf16*>(d.A);
+  a.B = reinterpret_cast<const __bf16*>(d.B);
+  a.C = reinterpret_cast<char*>(d.C);
+  a.bias = d.bias;
+  a.lda = d.lda; a.ldb = d.ldb; a.ldc = d.ldc;
+  a.M = (int32_t)d.M; a.N = (int32_t)d.N; a.K = (int32_t)d.K;
+  a.tiles_m = (int32_t)((d.M + C::BM - 1) / C::BM);
+  a.tiles_n = (int32_t)((d.N + C::BN - 1) / C::BN);
+  a.epi = d.epi; a.out_f32 = d.out_f32;
+  Guards& g = a.guard;
+  span(d.A, mat_bytes(d.M, d.K, d.lda, 2), g.a_lo, g.a_hi);
+  span(d.B, mat_bytes(d.N, d.K, d.ldb, 2), g.b_lo, g.b_hi);
+  span(d.C, mat_bytes(d.M, d.N, d.ldc, d.out_f32 ? 4 : 2), g.c_lo, g.c_hi);
+  span(d.bias, (uint64_t)d.N * 4, g.bias_lo, g.bias_hi);
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  const int cus = device_compute_units();
+  if (cus <= 0) return hipErrorNoDevice;
+  const int grid = (int)(tiles < cus ? tiles : cus);
+  hipLaunchKernelGGL(onerole_kernel<C>, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+void onerole_describe(int32_t cfg[6]) {
+  cfg[0] = CfgOneRole::BM; cfg[1] = CfgOneRole::BN; cfg[2] = CfgOneRole::BK;
+  cfg[3] = CfgOneRole::STAGES; cfg[4] = 4; cfg[5] = 0;  // four waves, each copying and computing
+}
+
+hipError_t read_onerole_watchdog(uint32_t* value, int clear) {
+  hipError_t e = hipMemcpyFromSymbol(value, HIP_SYMBOL(g_watchdog), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !clear) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_watchdog), &zero, sizeof(uint32_t), 0, hipMemcpyHostToDevice);
+}
+
+}  // namespace ptg

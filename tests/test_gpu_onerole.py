@@ -1,0 +1,127 @@
+"""GPU parity of the one-role dense kernel (every wave both copies and computes; 256 x 256 x 32
+tiles in three LDS slots) against the fp64 CPU oracle.
+
+ptg_gemm takes this kernel when B is stored N x K, K is a multiple of 32 and the output has at
+least 128 tiles of 256 x 256.  The cases cover every remainder of the unrolled k-loop (one to
+twelve 32-deep steps), output grids whose 16 x 16 tile blocks and 4-row strips are partial
+(including the reversed odd block rows), ragged M and N, every epilogue and both output types,
+and strided operands and outputs inside guard bands.  Integer data make the fp32 result exact
+in any summation order, so those cases are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pipelined_tiled_gemm_amd as ptg
+import workloads as wl
+from parity import check, dev, dev_bf16, exact, int_bf16, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _no_watchdog():
+    ptg.watchdog(clear=True)
+    yield
+    torch.cuda.synchronize()
+    assert ptg.watchdog(clear=True) == 0, "a range check of the kernel fired"
+
+
+def onerole(M, N, K, layout=wl.B_NK) -> bool:
+    return ptg.describe_config(M, N, K, layout)["producers"] == 0
+
+
+def test_routing():
+    assert onerole(8192, 8192, 8192)
+    assert onerole(4096, 2048, 32)
+    assert not onerole(8192, 8192, 8192, wl.B_KN)      # B stored K x N: the two-role kernel
+    assert not onerole(4096, 4096, 264)                # K not a multiple of 32
+    assert not onerole(2048, 2048, 1024)               # 64 tiles: too few to fill the chip
+    cfg = ptg.describe_config(8192, 8192, 8192, wl.B_NK)
+    assert (cfg["BM"], cfg["BN"], cfg["BK"], cfg["stages"]) == (256, 256, 32, 3)
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 7, 9, 12])
+def test_every_loop_remainder_integer_exact(steps):
+    """K = 32 steps: the unrolled loop runs six steps per pass and finishes with one to six;
+    4096 x 2048 (128 tiles, one round), every element bit-exact in fp32 and bf16."""
+    M, N, K = 4096, 2048, 32 * steps
+    assert onerole(M, N, K)
+    rng = np.random.default_rng(100 + steps)
+    A, B = int_bf16(rng, (M, K)), int_bf16(rng, (N, K))
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    v = oracle.gemm(A, B, wl.B_NK)
+    exact(ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.float32), v, f"K={K} fp32")
+    exact(ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.bfloat16), v, f"K={K} bf16")
+
+
+@pytest.mark.parametrize("shape", [(4196, 2088, 96),       # 17 x 9 tiles: a one-row last block row
+                                   (8392, 4392, 64),       # 33 x 18: reversed odd block rows whose
+                                                           # narrow last block column comes first
+                                   (4100, 8200, 160),      # 17 x 33: three block columns, the last
+                                                           # one tile wide
+                                   (4600, 3000, 128)])     # 18 x 12: a last strip of two tile rows
+def test_tile_order_edges_integer_exact(shape):
+    """Output grids whose tile blocks and strips are partial: every tile is computed exactly
+    once (the output is NaN-filled first) and every element is bit-exact."""
+    M, N, K = shape
+    assert onerole(M, N, K)
+    rng = np.random.default_rng(M + N + K)
+    A, B = int_bf16(rng, (M, K)), int_bf16(rng, (N, K))
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ptg.gemm(dev_bf16(A), dev_bf16(B), b_layout=wl.B_NK, out=out)
+    exact(out, oracle.gemm(A, B, wl.B_NK), f"one-role {shape}")
+
+
+@pytest.mark.parametrize("epi", [wl.EPI_NONE, wl.EPI_BIAS, wl.EPI_SILU, wl.EPI_BIAS_SILU])
+def test_epilogues_ragged(epi):
+    """Ragged M and N, N(0,1)/sqrt(K) data, every epilogue, both output types; sampled rows
+    plus the whole last (partial) row of tiles against the oracle."""
+    M, N, K = 4096 + 40, 2048 + 24, 288
+    assert onerole(M, N, K)
+    w = wl.dense(31, M, N, K, dist="normal", b_layout=wl.B_NK, scale=K ** -0.5, with_bias=True)
+    A, B, bias = dev_bf16(w.A), dev_bf16(w.B), dev(w.bias)
+    rows = np.unique(np.concatenate([sample_rows(M, 64, 2), np.arange(M - 40, M)]))
+    v = oracle.gemm(w.A, w.B, wl.B_NK, w.bias, epi, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = ptg.gemm(A, B, b_layout=wl.B_NK, out_dtype=out_dtype, bias=bias, epi=epi)
+        check(out[idx], v, K, f"one-role epi={epi} {out_dtype}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_strided_operands_and_guard_bands(out_dtype):
+    """lda, ldb > K and ldc > N (views into wider buffers); the output view sits inside a
+    NaN-filled buffer: every element of the view is written, nothing around it."""
+    M, N, K = 4096 + 8, 2048 + 16, 128
+    assert onerole(M, N, K)
+    rng = np.random.default_rng(77)
+    Aw = int_bf16(rng, (M, K + 24))
+    Bw = int_bf16(rng, (N, K + 40))
+    A, B = dev_bf16(Aw)[:, 8:8 + K], dev_bf16(Bw)[:, 16:16 + K]
+    big = torch.full((M + 2, N + 24), float("nan"), dtype=out_dtype, device="cuda")
+    view = big[1:M + 1, 8:8 + N]
+    ptg.gemm(A, B, b_layout=wl.B_NK, out=view)
+    v = oracle.gemm(np.ascontiguousarray(Aw[:, 8:8 + K]), np.ascontiguousarray(Bw[:, 16:16 + K]), wl.B_NK)
+    exact(view, v, "one-role strided")
+    g = big.float()
+    inside = torch.zeros_like(g, dtype=torch.bool)
+    inside[1:M + 1, 8:8 + N] = True
+    assert bool(torch.isnan(g[~inside]).all()), "guard band overwritten"
+
+
+def test_repeat_and_two_role_agree():
+    """Two calls give the same bits; on integer data the one-role result equals the two-role
+    kernel's (the same product through B stored K x N)."""
+    M, N, K = 4096, 4096, 512
+    rng = np.random.default_rng(5)
+    A, Bnk = int_bf16(rng, (M, K)), int_bf16(rng, (N, K))
+    dA = dev_bf16(A)
+    dB = dev_bf16(Bnk)
+    o1 = ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.float32)
+    o2 = ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.float32)
+    assert torch.equal(o1, o2)
+    assert not onerole(M, N, K, wl.B_KN)
+    o3 = ptg.gemm(dA, dB.t().contiguous(), b_layout=wl.B_KN, out_dtype=torch.float32)
+    assert torch.equal(o1, o3)

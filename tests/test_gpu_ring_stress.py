@@ -8,7 +8,9 @@ result stays bit-exact against the oracle: a slot overwritten early or read stal
 a sum.
 
 Cases: the large tile (two 64 KB slots, register-staged producers) on long reductions (64
-k-steps per tile) in both B layouts; the medium tile (four slots, buffer-to-LDS producers, two
+k-steps per tile) in both B layouts; the one-role kernel (three 32 KB slots that change hands
+at a per-step barrier; the stress build pauses each wave before that barrier and between its
+copies and fragment reads); the medium tile (four slots, buffer-to-LDS producers, two
 ping-pong consumer groups); the grouped GEMM with empty experts and a column-split last round;
 the weight gradient's dynamic tile queue; the pointer-array batch; the broadcast GEMM's one-launch
 form, whose reduction units and candidate tiles wait on other workgroups' results.
@@ -54,17 +56,23 @@ def _no_watchdog(delay_lib):
         assert ptg.watchdog(clear=True) == 0, "a pipeline wait of the stress build gave up"
 
 
-@pytest.mark.parametrize("layout", [wl.B_NK, wl.B_KN])
-def test_stress_large_tile_long_k(delay_lib, layout):
-    M = N = K = 4096
-    rng = np.random.default_rng(4096 + layout)
+@pytest.mark.parametrize("layout,K,stages,producers", [(wl.B_NK, 4104, 2, 4),   # two-role (K mod 32 = 8)
+                                                       (wl.B_KN, 4096, 2, 4),   # two-role
+                                                       (wl.B_NK, 4096, 3, 0)])  # one-role
+def test_stress_large_tile_long_k(delay_lib, layout, K, stages, producers):
+    """Large tiles over a long K in the stress build: the two-role ring (producer and consumer
+    waves hand slots over through LDS counters) and the one-role kernel (every wave copies and
+    computes; slots change hands at the per-step barrier), each with pauses that skew the waves."""
+    M = N = 4096
+    rng = np.random.default_rng(K + layout)
     A = int_bf16(rng, (M, K))
     B = int_bf16(rng, (N, K) if layout == wl.B_NK else (K, N))
-    assert ptg.describe_config(M, N, K, layout)["stages"] == 2
+    cfg = ptg.describe_config(M, N, K, layout)
+    assert (cfg["stages"], cfg["producers"]) == (stages, producers)
     dA, dB = dev_bf16(A), dev_bf16(B)
     with using(delay_lib):
         out = ptg.gemm(dA, dB, b_layout=layout, out_dtype=torch.float32)
-    exact(out, oracle.gemm(A, B, layout), f"stress large 4096^3 layout={layout}")
+    exact(out, oracle.gemm(A, B, layout), f"stress large 4096x4096x{K} layout={layout}")
 
 
 def test_stress_is_slower_than_the_product_build(delay_lib):

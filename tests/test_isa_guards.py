@@ -15,6 +15,11 @@
   reads element 0 whatever the subscript (an fp32 epilogue built that way stored column 0
   of every 4-column run four times).  The compiler behaviour itself is pinned too.
 - Every 16-byte output store takes four distinct registers (no broadcast of one value).
+- The one-role kernel writes its MFMAs as inline asm, whose results the compiler's hazard
+  tracking does not see: no accumulator is read, moved or stored within 20 wait states of an
+  MFMA, and none is written by a vector instruction within 3 wait states before one.  Its
+  k-loop holds only the matrix instructions, the fragment reads, the copies and the per-step
+  scalar work: no address arithmetic between the MFMAs.
 """
 import os
 import re
@@ -43,8 +48,9 @@ def asm(tmp_path_factory):
 
 
 def kernels(asm_text):
-    # the pipelined GEMM kernels and the attention kernel
-    for m in re.finditer(r"\n(_ZN3ptg(?:10ptg_kernel|4attn16attention_kernel)\S+):", asm_text):
+    # the pipelined GEMM kernels, the one-role dense kernel and the attention kernel
+    for m in re.finditer(r"\n(_ZN3ptg(?:10ptg_kernel|4attn16attention_kernel|12_GLOBAL__N_114onerole_kernel)\S+):",
+                         asm_text):
         start = m.start()
         end = asm_text.index(".Lfunc_end", start)
         yield m.group(1), asm_text[start:end].split("\n")
@@ -152,3 +158,87 @@ def test_stress_pauses_only_in_the_test_build(asm, tmp_path):
            "--cuda-device-only", os.path.join(build.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     assert memtimes(out.read_text()) > 0
+
+
+def onerole_body(asm_text):
+    found = [body for name, body in kernels(asm_text) if "onerole_kernel" in name]
+    assert len(found) == 1
+    return found[0]
+
+
+def wait_states(line):
+    m = re.match(r"s_nop (\d+)", line)
+    return int(m.group(1)) + 1 if m else 1
+
+
+def instructions(body):
+    for line in body:
+        s = line.strip()
+        if s and not s.startswith((";", ".")) and not s.endswith(":"):
+            yield s
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+@pytest.mark.parametrize("variant", [None, "delay"])
+def test_onerole_waits_for_its_asm_mfmas(asm, tmp_path, variant):
+    """In code order (every block boundary after an MFMA run is preceded by the padding, so
+    order is enough): reads of accumulators wait out the MFMA's passes, and writes to them
+    come at least 3 wait states before the next MFMA.  Checked in the product and the stress
+    build, whose pauses add block boundaries."""
+    if variant is None:
+        text = asm
+    else:
+        out = tmp_path / "onerole_delay.s"
+        src = "ptg_onerole.hip"
+        subprocess.run([build.hipcc(), *build.compile_flags(build.VARIANTS[variant], source=src), "-S",
+                        "--cuda-device-only", os.path.join(build.CSRC, src), "-o", str(out)],
+                       check=True, capture_output=True)
+        text = out.read_text()
+    since_mfma, since_acc_write = None, 99
+    n_mfma = 0
+    for s in instructions(onerole_body(text)):
+        if s.startswith("v_mfma"):
+            n_mfma += 1
+            assert since_acc_write >= 3, f"accumulator written {since_acc_write} wait states before {s}"
+            since_mfma = 0
+            since_acc_write += 1
+            continue
+        reads_acc = re.match(r"(v_accvgpr_(read|mov)|buffer_store|v_cvt|v_permlane)", s)
+        if since_mfma is not None and reads_acc:
+            assert since_mfma >= 20, f"{s}: {since_mfma} wait states after an MFMA"
+        if re.match(r"v_accvgpr_(write|mov)", s):
+            since_acc_write = 0
+        else:
+            since_acc_write += wait_states(s)
+        if since_mfma is not None:
+            since_mfma += wait_states(s)
+    assert n_mfma >= 384
+    # everything inlined: no calls, no accumulators passed through memory
+    body = onerole_body(text)
+    assert not any(re.match(r"\s+(s_swappc|s_setpc|flat_load|flat_store|scratch_)", l) for l in body)
+    assert not re.search(r"\n_ZZN3ptg12_GLOBAL__N_114onerole_kernel\S*:", text), "a lambda left out of line"
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+def test_onerole_k_loop_is_lean(asm):
+    """The k-loop (the block of six unrolled steps): 384 MFMAs, 96 fragment reads of 16 bytes,
+    48 copies to LDS, 6 barriers, and no more than 24 other vector instructions (the copies'
+    descriptor work), none of them writing LDS or touching scratch."""
+    body = onerole_body(asm)
+    blocks, cur = [], None
+    for line in body:
+        if re.match(r"^(\.LBB\S+|; %bb\.\d+):", line):
+            cur = []
+            blocks.append(cur)
+        elif cur is not None:
+            cur.append(line.strip())
+    loops = [b for b in blocks if sum(l.startswith("v_mfma") for l in b) == 384]
+    assert len(loops) == 1
+    loop = loops[0]
+    count = lambda p: sum(1 for l in loop if l.startswith(p))
+    assert count("ds_read_b128") == 96
+    assert count("buffer_load_dwordx4") == 48 and all(" lds" in l for l in loop if l.startswith("buffer_load"))
+    assert count("s_barrier") == 6
+    assert count("ds_write") == 0 and count("scratch_") == 0
+    other_valu = [l for l in loop if l.startswith("v_") and not l.startswith(("v_mfma", "v_accvgpr"))]
+    assert len(other_valu) <= 24, other_valu
