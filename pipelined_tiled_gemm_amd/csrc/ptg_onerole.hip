@@ -7,16 +7,24 @@
 // k-step's memory-to-LDS copies and computes a 128 x 128 quarter of the 256 x 256 output tile.
 // With one wave per SIMD a wave stall is a matrix-core stall, so the loop is written for an
 // uninterrupted instruction stream:
-//   - copies go straight from memory into LDS (buffer loads with the LDS flag), each wave's
-//     copies of step st + 3 issued between the MFMAs of step st: three 32-deep slots of 32 KB;
-//   - the k-loop is unrolled over the ring, so every fragment read is a fixed per-lane base
-//     register plus an immediate offset: no address arithmetic sits between the MFMAs;
+//   - copies go straight from memory into LDS (buffer loads with the LDS flag) into five
+//     32-deep slots of 32 KB;
+//   - copies go in pairs of k-steps (2p, 2p + 1), whose two 64-byte halves make up each
+//     128-byte row segment: each copy of step 2p is followed at once by the copy of the same
+//     rows of step 2p + 1, so the second half is served by the line the first brought into
+//     L1 (one L2 request per line instead of two).  A pair is split by rows over two steps
+//     (rows of copies 0-3 at step 2p - 4, 4-7 at step 2p - 3), so every step issues 8
+//     copies per wave, one after every 8th MFMA;
+//   - the k-loop is unrolled over ten steps (two turns of the ring), so every fragment read
+//     is a fixed per-lane base register plus an immediate offset: no address arithmetic sits
+//     between the MFMAs;
 //   - the MFMAs are inline asm, which fixes the issue order of every LDS and memory access
 //     between them to the source order.
 // One barrier per step.  Before it, each wave waits for its own copies of step st + 1 and for
 // its reads of step st's slot (its fragments were read during step st - 1).  After it, step
-// st + 1 is complete in LDS and step st's slot is free for step st + 3, which takes the same
-// slot (mod 3).
+// st + 1 is complete in LDS, and every wave has finished step st - 1, so the slots of steps
+// st - 1 and st (their fragments are in registers) take the copies issued during step st:
+// steps st + 4 and st + 5 at even steps, st + 3 and st + 4 at odd steps (the same slots mod 5).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -28,9 +36,9 @@ namespace ptg {
 
 namespace {
 
-// 256 x 256 x 32 tile, three slots; 2 x 2 waves of 128 x 128 (16 x 16 MFMA blocks); the
+// 256 x 256 x 32 tile, five slots; 2 x 2 waves of 128 x 128 (16 x 16 MFMA blocks); the
 // producer count (4) fixes each wave's share of a step's 1 KB copies (8)
-using CfgOneRole = Cfg<256, 256, 32, 3, 2, 2, 4, false, 1, true, false, false, 1>;
+using CfgOneRole = Cfg<256, 256, 32, 5, 2, 2, 4, false, 1, true, false, false, 1>;
 
 struct OneRoleArgs {
   const __bf16* A;
@@ -86,8 +94,7 @@ template <class C>
 __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
   constexpr int S = C::STAGES, L = C::LOADS;
-  constexpr int D = S;                       // copies run S steps ahead of the matrix work
-  static_assert(C::BK == 32 && !C::B_KN && L == 8 && S == 3, "three 32-deep N x K slots, 8 copies per wave");
+  static_assert(C::BK == 32 && !C::B_KN && L == 8 && S == 5, "five 32-deep N x K slots, 8 copies per wave");
   constexpr int TM = C::TM16, TN = C::TN16;  // 8 x 8 blocks of 16 x 16 per wave
   static_assert(TM == 8 && TN == 8, "128 x 128 per wave");
   const int w = (int)uni(threadIdx.x >> 6);
@@ -98,21 +105,22 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
   const int wave_lds = opA ? i0 * 1024 : C::A_BYTES + (i0 - C::A_INSTR) * 1024;
 
   // Fragment bases: lane l reads row (l mod 16) of a 16-row block, 16-byte k-chunk l / 16
-  // (swizzled as the copies laid it out).  Slots 0 and 1 through base 0, slot 2 through base 1
-  // (a read's immediate offset holds 16 bits).  Opaque, so that they stay in registers instead
+  // (swizzled as the copies laid it out).  Slots 0-1 through base 0, 2-3 through base 1, 4
+  // through base 2 (a read's immediate offset holds 16 bits).  Opaque, so that they stay in registers instead
   // of being re-derived inside the loop.
   const int ra = wm * C::WTM + (lane & 15);
   const int rb = wn * C::WTN + (lane & 15);
   int a0 = ra * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_A>(ra)) << 4);
   int b0 = C::A_BYTES + rb * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_B>(rb)) << 4);
   int a1 = a0 + 2 * C::STAGE_BYTES, b1 = b0 + 2 * C::STAGE_BYTES;
-  asm volatile("" : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1));
+  int a2 = a0 + 4 * C::STAGE_BYTES, b2 = b0 + 4 * C::STAGE_BYTES;
+  asm volatile("" : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2));
   // Every lambda of the kernel is forced inline: one left out of line takes the accumulators
   // by reference through memory, and stores them right after an asm MFMA whose results the
   // compiler does not know to wait for.
   auto rd = [&](int base, int imm) __attribute__((always_inline)) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(ring + base + imm); };
-  auto frag_a = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? a0 : a1, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
-  auto frag_b = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? b0 : b1, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
+  auto frag_a = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? a0 : sl < 4 ? a1 : a2, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
+  auto frag_b = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? b0 : sl < 4 ? b1 : b2, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
 
   const uint64_t ntiles = (uint64_t)(uint32_t)args.tiles_m * (uint32_t)args.tiles_n;
   const int K = args.K;
@@ -174,11 +182,12 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[x][y]) : "v"(fb), "v"(fa));
     };
 
-    // prologue: steps 0 .. D - 1 into slots 0 .. D - 1; step 0's fragments into registers
-    for (int st = 0; st < D; ++st)
+    // prologue: steps 0 .. 3 (pairs 0-1 and 2-3) into slots 0 .. 3; step 0's fragments into
+    // registers
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int q = 0; q < L; ++q) copy(st, st, q);
-    wait_vmcnt<(D - 1) * L>();
+    wait_vmcnt<3 * L>();
     __builtin_amdgcn_s_barrier();
     bf16x8 xa[TM], xb[TN], ya[TM], yb[TN];
 #pragma unroll
@@ -197,15 +206,18 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
       stress_pause();
 #endif
     };
-    // step st in slot SL = st mod 3 (compile time): its 64 MFMAs on fa/fb; between them, the
-    // copies of step st + 3 into slot SL (one per 8 MFMAs) and step st + 1's 16 fragments from
-    // slot SL + 1 (one per 3 MFMAs, all done well before the step's end)
-    auto body = [&](int st, auto SLc, const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN], bf16x8 (&na)[TM],
+    // Step st = pass start + J (J, 0..9, known at compile time; slot J mod 5): its 64 MFMAs on
+    // fa/fb; between them, 8 copies (one after every 8th MFMA) and step st + 1's 16 fragments
+    // from slot (J + 1) mod 5 (one per 3 MFMAs, all done well before the step's end)
+    auto body = [&](int st, auto Jc, const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN], bf16x8 (&na)[TM],
                     bf16x8 (&nb)[TN]) __attribute__((always_inline)) {
-      constexpr int SL = decltype(SLc)::value;
+      constexpr int J = decltype(Jc)::value;
       pause();                     // the stress build skews the waves here (a no-op otherwise)
-      wait_vmcnt<(D - 2) * L>();   // this wave's copies of step st + 1 have landed
-      wait_lgkm0();                // and its reads of slot SL (step st's fragments) are done
+      // this wave's copies of step st + 1 have landed: after its last one came 9 younger
+      // copies (st odd: the rest of its step, then one step's 8) or 16 (st even: two steps')
+      if constexpr (J % 2 == 1) wait_vmcnt<L + 1>();
+      else wait_vmcnt<2 * L>();
+      wait_lgkm0();                // and its reads of step st's slot are done
       __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int x = 0; x < TM; ++x)
@@ -213,12 +225,19 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
         for (int y = 0; y < TN; ++y) {
           const int k = x * TN + y;
           mf(x, y, fa[x], fb[y]);
-          if (k % 8 == 2) copy(st + D, SL, k / 8);
+          // even step: pair p = st / 2 + 2, rows 0..3; odd step: p = (st + 3) / 2, rows 4..7
+          if (k % 8 == 2) {
+            const int i = k / 8;                    // 0..7: row group i / 2, half i % 2
+            const int q = (J % 2 == 0 ? 0 : 4) + i / 2;
+            const int n = (J % 2 == 0 ? st + 4 : st + 3) + (i & 1);
+            const int ns = (J % 2 == 0 ? J + 4 : J + 3) + (i & 1);
+            copy(n, ns % S, q);
+          }
           if (k == 35) pause();          // and between the copies and reads of a step
           if (k % 3 == 0 && k / 3 < TN + TM) {
             const int r = k / 3;
-            if (r < TN) nb[r] = frag_b((SL + 1) % S, r);
-            else na[r - TN] = frag_a((SL + 1) % S, r - TN);
+            if (r < TN) nb[r] = frag_b((J + 1) % S, r);
+            else na[r - TN] = frag_a((J + 1) % S, r - TN);
           }
         }
     };
@@ -228,12 +247,12 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
 #pragma unroll
         for (int y = 0; y < TN; ++y) mf(x, y, fa[x], fb[y]);
     };
-    // six steps per pass: two turns of the ring and an even number of x/y swaps
+    // ten steps per pass: two turns of the ring, whole copy pairs, an even number of swaps
     constexpr int U = 2 * S;
     auto step_j = [&](int st0, auto Jc) __attribute__((always_inline)) {
       constexpr int J = decltype(Jc)::value;
-      if constexpr (J % 2 == 0) body(st0 + J, std::integral_constant<int, J % S>{}, xa, xb, ya, yb);
-      else body(st0 + J, std::integral_constant<int, J % S>{}, ya, yb, xa, xb);
+      if constexpr (J % 2 == 0) body(st0 + J, std::integral_constant<int, J>{}, xa, xb, ya, yb);
+      else body(st0 + J, std::integral_constant<int, J>{}, ya, yb, xa, xb);
     };
     // Where a block boundary follows an MFMA the compiler may move accumulators between
     // registers (it does at the loop exit); it does not see that the asm MFMAs write them late,
@@ -247,15 +266,23 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
       step_j(st, std::integral_constant<int, 3>{});
       step_j(st, std::integral_constant<int, 4>{});
       step_j(st, std::integral_constant<int, 5>{});
+      step_j(st, std::integral_constant<int, 6>{});
+      step_j(st, std::integral_constant<int, 7>{});
+      step_j(st, std::integral_constant<int, 8>{});
+      step_j(st, std::integral_constant<int, 9>{});
       settle();
     }
-    // 1 to 6 steps left, the first in slot 0 with its fragments in x
+    // 1 to 10 steps left, the first in slot 0 with its fragments in x
     const int left = nsteps - st;
     if (left >= 2) { step_j(st, std::integral_constant<int, 0>{}); settle(); }
     if (left >= 3) { step_j(st, std::integral_constant<int, 1>{}); settle(); }
     if (left >= 4) { step_j(st, std::integral_constant<int, 2>{}); settle(); }
     if (left >= 5) { step_j(st, std::integral_constant<int, 3>{}); settle(); }
     if (left >= 6) { step_j(st, std::integral_constant<int, 4>{}); settle(); }
+    if (left >= 7) { step_j(st, std::integral_constant<int, 5>{}); settle(); }
+    if (left >= 8) { step_j(st, std::integral_constant<int, 6>{}); settle(); }
+    if (left >= 9) { step_j(st, std::integral_constant<int, 7>{}); settle(); }
+    if (left >= 10) { step_j(st, std::integral_constant<int, 8>{}); settle(); }
     if ((left - 1) & 1) {
       wait_lgkm0();
 #pragma unroll

@@ -1,9 +1,9 @@
 """GPU parity of the one-role dense kernel (every wave both copies and computes; 256 x 256 x 32
-tiles in three LDS slots) against the fp64 CPU oracle.
+tiles in five LDS slots) against the fp64 CPU oracle.
 
 ptg_gemm takes this kernel when B is stored N x K, K is a multiple of 32 and the output has at
-least 128 tiles of 256 x 256.  The cases cover every remainder of the unrolled k-loop (one to
-twelve 32-deep steps), output grids whose 16 x 16 tile blocks and 4-row strips are partial
+least 128 tiles of 256 x 256.  The cases cover every remainder of the unrolled k-loop (ten
+32-deep steps per pass: one to ten steps after zero, one or two passes), output grids whose 16 x 16 tile blocks and 4-row strips are partial
 (including the reversed odd block rows), ragged M and N, every epilogue and both output types,
 and strided operands and outputs inside guard bands.  Integer data make the fp32 result exact
 in any summation order, so those cases are compared bit for bit.
@@ -39,13 +39,14 @@ def test_routing():
     assert not onerole(4096, 4096, 264)                # K not a multiple of 32
     assert not onerole(2048, 2048, 1024)               # 64 tiles: too few to fill the chip
     cfg = ptg.describe_config(8192, 8192, 8192, wl.B_NK)
-    assert (cfg["BM"], cfg["BN"], cfg["BK"], cfg["stages"]) == (256, 256, 32, 3)
+    assert (cfg["BM"], cfg["BN"], cfg["BK"], cfg["stages"]) == (256, 256, 32, 5)
 
 
-@pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 7, 9, 12])
+@pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 15, 20, 21])
 def test_every_loop_remainder_integer_exact(steps):
-    """K = 32 steps: the unrolled loop runs six steps per pass and finishes with one to six;
-    4096 x 2048 (128 tiles, one round), every element bit-exact in fp32 and bf16."""
+    """K = 32 steps: the unrolled loop runs ten steps per pass and finishes with one to ten;
+    copies go in pairs of steps (odd step counts leave a pair half past K).  4096 x 2048 (128
+    tiles, one round), every element bit-exact in fp32 and bf16."""
     M, N, K = 4096, 2048, 32 * steps
     assert onerole(M, N, K)
     rng = np.random.default_rng(100 + steps)

@@ -8,7 +8,7 @@ result stays bit-exact against the oracle: a slot overwritten early or read stal
 a sum.
 
 Cases: the large tile (two 64 KB slots, register-staged producers) on long reductions (64
-k-steps per tile) in both B layouts; the one-role kernel (three 32 KB slots that change hands
+k-steps per tile) in both B layouts; the one-role kernel (five 32 KB slots that change hands
 at a per-step barrier; the stress build pauses each wave before that barrier and between its
 copies and fragment reads); the medium tile (four slots, buffer-to-LDS producers, two
 ping-pong consumer groups); the grouped GEMM with empty experts and a column-split last round;
@@ -58,7 +58,7 @@ def _no_watchdog(delay_lib):
 
 @pytest.mark.parametrize("layout,K,stages,producers", [(wl.B_NK, 4104, 2, 4),   # two-role (K mod 32 = 8)
                                                        (wl.B_KN, 4096, 2, 4),   # two-role
-                                                       (wl.B_NK, 4096, 3, 0)])  # one-role
+                                                       (wl.B_NK, 4096, 5, 0)])  # one-role
 def test_stress_large_tile_long_k(delay_lib, layout, K, stages, producers):
     """Large tiles over a long K in the stress build: the two-role ring (producer and consumer
     waves hand slots over through LDS counters) and the one-role kernel (every wave copies and

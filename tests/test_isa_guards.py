@@ -212,7 +212,7 @@ def test_onerole_waits_for_its_asm_mfmas(asm, tmp_path, variant):
             since_acc_write += wait_states(s)
         if since_mfma is not None:
             since_mfma += wait_states(s)
-    assert n_mfma >= 384
+    assert n_mfma >= 640
     # everything inlined: no calls, no accumulators passed through memory
     body = onerole_body(text)
     assert not any(re.match(r"\s+(s_swappc|s_setpc|flat_load|flat_store|scratch_)", l) for l in body)
@@ -221,8 +221,8 @@ def test_onerole_waits_for_its_asm_mfmas(asm, tmp_path, variant):
 
 @pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
 def test_onerole_k_loop_is_lean(asm):
-    """The k-loop (the block of six unrolled steps): 384 MFMAs, 96 fragment reads of 16 bytes,
-    48 copies to LDS, 6 barriers, and no more than 24 other vector instructions (the copies'
+    """The k-loop (the block of ten unrolled steps): 640 MFMAs, 160 fragment reads of 16 bytes,
+    80 copies to LDS, 10 barriers, and no more than 40 other vector instructions (the copies'
     descriptor work), none of them writing LDS or touching scratch."""
     body = onerole_body(asm)
     blocks, cur = [], None
@@ -232,13 +232,13 @@ def test_onerole_k_loop_is_lean(asm):
             blocks.append(cur)
         elif cur is not None:
             cur.append(line.strip())
-    loops = [b for b in blocks if sum(l.startswith("v_mfma") for l in b) == 384]
+    loops = [b for b in blocks if sum(l.startswith("v_mfma") for l in b) == 640]
     assert len(loops) == 1
     loop = loops[0]
     count = lambda p: sum(1 for l in loop if l.startswith(p))
-    assert count("ds_read_b128") == 96
-    assert count("buffer_load_dwordx4") == 48 and all(" lds" in l for l in loop if l.startswith("buffer_load"))
-    assert count("s_barrier") == 6
+    assert count("ds_read_b128") == 160
+    assert count("buffer_load_dwordx4") == 80 and all(" lds" in l for l in loop if l.startswith("buffer_load"))
+    assert count("s_barrier") == 10
     assert count("ds_write") == 0 and count("scratch_") == 0
     other_valu = [l for l in loop if l.startswith("v_") and not l.startswith(("v_mfma", "v_accvgpr"))]
-    assert len(other_valu) <= 24, other_valu
+    assert len(other_valu) <= 40, other_valu
