@@ -10,9 +10,9 @@
 //   - copies go straight from memory into LDS (buffer loads with the LDS flag) into five
 //     32-deep slots of 32 KB;
 //   - copies go in pairs of k-steps (2p, 2p + 1), whose two 64-byte halves make up each
-//     128-byte row segment: each copy of step 2p is followed at once by the copy of the same
-//     rows of step 2p + 1, so the second half is served by the line the first brought into
-//     L1 (one L2 request per line instead of two).  A pair is split by rows over two steps
+//     128-byte row segment: each copy of step 2p is followed, 8 MFMAs later, by the copy of
+//     the same rows of step 2p + 1, so the second half is served by the line the first
+//     brought into L1 (one L2 request per line instead of two).  A pair is split by rows over two steps
 //     (rows of copies 0-3 at step 2p - 4, 4-7 at step 2p - 3), so every step issues 8
 //     copies per wave, one after every 8th MFMA;
 //   - the k-loop is unrolled over ten steps (two turns of the ring), so every fragment read
