@@ -289,6 +289,13 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
       for (int t = 0; t < TM; ++t) xa[t] = ya[t];
 #pragma unroll
       for (int t = 0; t < TN; ++t) xb[t] = yb[t];
+      // the moves are vector writes of the MFMAs' source registers, which the compiler does
+      // not know the asm MFMAs read: 8 wait states after them (the asm takes the moved values,
+      // so the moves come before it)
+      asm volatile("s_nop 7" ::"v"(xa[0]), "v"(xa[1]), "v"(xa[2]), "v"(xa[3]), "v"(xa[4]), "v"(xa[5]), "v"(xa[6]),
+                   "v"(xa[7]));
+      asm volatile("s_nop 7" ::"v"(xb[0]), "v"(xb[1]), "v"(xb[2]), "v"(xb[3]), "v"(xb[4]), "v"(xb[5]), "v"(xb[6]),
+                   "v"(xb[7]));
     }
     last(xa, xb);
     // ... nor that the epilogue reads what they wrote: wait for the last MFMAs' results

@@ -219,6 +219,42 @@ def test_onerole_waits_for_its_asm_mfmas(asm, tmp_path, variant):
     assert not re.search(r"\n_ZZN3ptg12_GLOBAL__N_114onerole_kernel\S*:", text), "a lambda left out of line"
 
 
+def vgprs(op):
+    m = re.match(r"v\[(\d+):(\d+)\]", op)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", op)
+    return {int(m.group(1))} if m else set()
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+@pytest.mark.parametrize("variant", [None, "delay"])
+def test_onerole_mfma_sources_settle(asm, tmp_path, variant):
+    """No vector instruction writes a register that an asm MFMA reads as its A or B operand
+    within 8 wait states before it (the compiler inserts no wait states for the asm): the
+    fragment registers are written by LDS reads (counted waits) and by the one move of the
+    x/y fragments before the last step, which is padded."""
+    if variant is None:
+        text = asm
+    else:
+        out = tmp_path / "onerole_delay.s"
+        src = "ptg_onerole.hip"
+        subprocess.run([build.hipcc(), *build.compile_flags(build.VARIANTS[variant], source=src), "-S",
+                        "--cuda-device-only", os.path.join(build.CSRC, src), "-o", str(out)],
+                       check=True, capture_output=True)
+        text = out.read_text()
+    recent = []  # (wait states since, registers written, instruction)
+    for s in instructions(onerole_body(text)):
+        if s.startswith("v_mfma"):
+            ops = [o.strip() for o in s.split(None, 1)[1].split(",")]
+            src = vgprs(ops[1]) | vgprs(ops[2])
+            for ago, w, txt in recent:
+                assert not (ago < 8 and w & src), f"{txt} then {s} after {ago} wait states"
+        elif s.startswith("v_") and not s.startswith("v_accvgpr_read") and " " in s:
+            recent.append((0, vgprs(s.split(None, 1)[1].split(",")[0].strip()), s))
+        recent = [(a + wait_states(s), w, x) for a, w, x in recent if a + wait_states(s) < 16]
+
+
 @pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
 def test_onerole_k_loop_is_lean(asm):
     """The k-loop (the block of ten unrolled steps): 640 MFMAs, 160 fragment reads of 16 bytes,
