@@ -37,8 +37,10 @@ namespace ptg {
 namespace {
 
 // 256 x 256 x 32 tile, five slots; 2 x 2 waves of 128 x 128 (16 x 16 MFMA blocks); the
-// producer count (4) fixes each wave's share of a step's 1 KB copies (8)
-using CfgOneRole = Cfg<256, 256, 32, 5, 2, 2, 4, false, 1, true, false, false, 1>;
+// producer count (4) fixes each wave's share of a step's 1 KB copies (8).  B stored N x K
+// (KN false) or K x N (KN true).
+template <bool KN>
+using CfgOneRole = Cfg<256, 256, 32, 5, 2, 2, 4, KN, 1, true, false, false, 1>;
 
 struct OneRoleArgs {
   const __bf16* A;
@@ -90,11 +92,23 @@ __device__ __forceinline__ void onerole_tile(uint64_t L, uint32_t tiles_m, uint3
   tn = (int)(16u * bj + in3 / sm);
 }
 
+// One 16-byte-per-lane copy from memory into LDS (M0 + lane * 16), written as asm.  The
+// compiler tracks a copy made with the builtin as an LDS write, and before an LDS read it
+// cannot prove disjoint from it (the transposing reads of B stored K x N) it waits for every
+// copy in flight, which serialises copies and matrix work; it does not track asm.  The kernel
+// orders copies and reads itself (per-step vector-memory waits and the barrier).  The
+// descriptor is built in scalar registers: base, stride 0, size, the flags make_rsrc uses.
+__device__ __forceinline__ void copy_lds16(uint64_t base, uint32_t nbytes, uint32_t lds, uint32_t voff) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4s;
+  const u32x4s d = {uni((uint32_t)base), uni((uint32_t)(base >> 32)) & 0xffffu, uni(nbytes), 0x00020000u};
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d), "{m0}"(uni(lds)) : "memory");
+}
+
 template <class C>
 __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
   constexpr int S = C::STAGES, L = C::LOADS;
-  static_assert(C::BK == 32 && !C::B_KN && L == 8 && S == 5, "five 32-deep N x K slots, 8 copies per wave");
+  static_assert(C::BK == 32 && L == 8 && S == 5, "five 32-deep slots, 8 copies per wave");
   constexpr int TM = C::TM16, TN = C::TN16;  // 8 x 8 blocks of 16 x 16 per wave
   static_assert(TM == 8 && TN == 8, "128 x 128 per wave");
   const int w = (int)uni(threadIdx.x >> 6);
@@ -103,24 +117,55 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
   const int i0 = w * L;                      // this wave's copies: 1 KB chunks i0 .. i0 + 7
   const bool opA = i0 < C::A_INSTR;
   const int wave_lds = opA ? i0 * 1024 : C::A_BYTES + (i0 - C::A_INSTR) * 1024;
+  const uint32_t ring_lds = uni(lds_addr(ring));   // the ring's LDS byte address
 
-  // Fragment bases: lane l reads row (l mod 16) of a 16-row block, 16-byte k-chunk l / 16
-  // (swizzled as the copies laid it out).  Slots 0-1 through base 0, 2-3 through base 1, 4
-  // through base 2 (a read's immediate offset holds 16 bits).  Opaque, so that they stay in registers instead
-  // of being re-derived inside the loop.
+  // Fragment bases.  A (and B stored N x K): lane l reads row (l mod 16) of a 16-row block,
+  // 16-byte k-chunk l / 16 (swizzled as the copies laid it out).  B stored K x N: two
+  // transposing 8-byte reads per fragment, 4 k-rows apart; block t's base is the lane's base
+  // XOR t * 32 bytes (the swizzle XORs chunk bits 1-3, which the wave's column offset leaves
+  // clear), one register per block.  Slots 0-1 through base set 0, 2-3 through set 1, 4
+  // through set 2 (a read's immediate offset holds 16 bits).  Opaque, so that they stay in
+  // registers instead of being re-derived inside the loop.
   const int ra = wm * C::WTM + (lane & 15);
-  const int rb = wn * C::WTN + (lane & 15);
   int a0 = ra * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_A>(ra)) << 4);
-  int b0 = C::A_BYTES + rb * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_B>(rb)) << 4);
-  int a1 = a0 + 2 * C::STAGE_BYTES, b1 = b0 + 2 * C::STAGE_BYTES;
-  int a2 = a0 + 4 * C::STAGE_BYTES, b2 = b0 + 4 * C::STAGE_BYTES;
-  asm volatile("" : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2));
+  int a1 = a0 + 2 * C::STAGE_BYTES;
+  int a2 = a0 + 4 * C::STAGE_BYTES;
+  asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2));
+  constexpr int NBB = C::B_KN ? TN : 1;      // B bases per slot group
+  int bb[3][NBB];
+  if constexpr (!C::B_KN) {
+    const int rb = wn * C::WTN + (lane & 15);
+    bb[0][0] = C::A_BYTES + rb * C::BK * 2 + (((lane >> 4) ^ swz_k<C::CPR_B>(rb)) << 4);
+  } else {
+    const int kr = (lane >> 4) * 8 + ((lane & 15) >> 2);
+    const int n = wn * C::WTN + (lane & 3) * 4;
+    const int bkn = kr * C::BN * 2 + (((n >> 3) ^ swz_n<C::CPR_B>(kr)) << 4) + ((n >> 2) & 1) * 8;
+#pragma unroll
+    for (int t2 = 0; t2 < NBB; ++t2) bb[0][t2] = C::A_BYTES + (bkn ^ (t2 << 5));
+  }
+#pragma unroll
+  for (int t2 = 0; t2 < NBB; ++t2) {
+    bb[1][t2] = bb[0][t2] + 2 * C::STAGE_BYTES;
+    bb[2][t2] = bb[0][t2] + 4 * C::STAGE_BYTES;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) asm volatile("" : "+v"(bb[g][t2]));
+  }
   // Every lambda of the kernel is forced inline: one left out of line takes the accumulators
   // by reference through memory, and stores them right after an asm MFMA whose results the
   // compiler does not know to wait for.
   auto rd = [&](int base, int imm) __attribute__((always_inline)) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(ring + base + imm); };
   auto frag_a = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? a0 : sl < 4 ? a1 : a2, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
-  auto frag_b = [&](int sl, int t) __attribute__((always_inline)) { return rd(sl < 2 ? b0 : sl < 4 ? b1 : b2, (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2); };
+  auto frag_b = [&](int sl, int t) __attribute__((always_inline)) -> bf16x8 {
+    const int g = sl < 2 ? 0 : sl < 4 ? 1 : 2;
+    if constexpr (!C::B_KN) {
+      return rd(bb[g][0], (sl & 1) * C::STAGE_BYTES + t * 16 * C::BK * 2);
+    } else {
+      const char* p = ring + bb[g][t] + (sl & 1) * C::STAGE_BYTES;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * C::BN * 2));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
 
   const uint64_t ntiles = (uint64_t)(uint32_t)args.tiles_m * (uint32_t)args.tiles_n;
   const int K = args.K;
@@ -134,30 +179,45 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
     const uint32_t m0 = (uint32_t)tm * C::BM, n0 = (uint32_t)tn * C::BN;
     const int m_rows = min(C::BM, args.M - (int)m0);
     const int n_cols = min(C::BN, args.N - (int)n0);
+    // the wave's operand: A (m-rows of K), or B as n-rows of K (N x K) or k-rows of N (K x N)
+    const bool kmajor = !opA && C::B_KN;
     const uint64_t ld = opA ? lda : ldb;
     const int extent = opA ? m_rows : n_cols;
-    const uint64_t src = uni64(reinterpret_cast<uint64_t>(opA ? args.A + m0 * lda : args.B + n0 * ldb));
-    uint32_t bytes = (uint32_t)((uint64_t)(uint32_t)(extent - 1) * ld * 2u + (uint64_t)(uint32_t)K * 2u);
+    const uint64_t src = uni64(reinterpret_cast<uint64_t>(opA ? args.A + m0 * lda
+                                                              : (C::B_KN ? args.B + n0 : args.B + n0 * ldb)));
+    uint32_t bytes = kmajor ? (uint32_t)((uint64_t)(uint32_t)(K - 1) * ld * 2u + (uint64_t)(uint32_t)extent * 2u)
+                            : (uint32_t)((uint64_t)(uint32_t)(extent - 1) * ld * 2u + (uint64_t)(uint32_t)K * 2u);
+    const uint32_t kstride = kmajor ? (uint32_t)ld * 2u : 2u;   // bytes per unit of k
     if (!inside(src, bytes, uni64(opA ? gd.a_lo : gd.b_lo), uni64(opA ? gd.a_hi : gd.b_hi))) {
       if (lane == 0) atomicOr(&g_watchdog, 4u);
       bytes = 0;  // nothing is read: the tile's operand is all zeros
     }
     bytes = uni(bytes);
-    // per-lane offset of each copy; rows past the tile take an out-of-range offset (zeros)
+    // per-lane offset of each copy; rows (or, for B stored K x N, columns) past the tile take
+    // an out-of-range offset (zeros)
     uint32_t voff[L];
 #pragma unroll
     for (int q = 0; q < L; ++q) {
       int row, c;
       chunk_of<C>(i0 + q, lane, row, c);
-      voff[q] = row < extent ? (uint32_t)(row * ld * 2 + c * 16) : kOutOfRange;
+      const bool ok = kmajor ? c * 8 < extent : row < extent;
+      voff[q] = ok ? (uint32_t)(row * ld * 2 + c * 16) : kOutOfRange;
     }
     // step st's copy q into slot sl: the k-step moves the descriptor base; a step past K
     // gets an empty descriptor (no access, zeros)
     auto copy = [&](int st, int sl, int q) __attribute__((always_inline)) {
-      const uint32_t kbytes = (uint32_t)st * C::BK * 2u;
+      const uint32_t kbytes = (uint32_t)st * C::BK * kstride;
       const uint32_t rem = kbytes < bytes ? bytes - kbytes : 0u;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const void*>(src + (rem ? kbytes : 0)), rem);
-      dma16(rs, ring + sl * C::STAGE_BYTES + wave_lds + q * 1024, voff[q], 0u);
+      if constexpr (C::B_KN) {
+        copy_lds16(src + (rem ? kbytes : 0), rem, ring_lds + (uint32_t)(sl * C::STAGE_BYTES + wave_lds + q * 1024),
+                   voff[q]);
+      } else {
+        // B stored N x K: every fragment read is a plain 16-byte load, which the compiler does
+        // not make wait for the builtin's copies (checked on the compiled loop); the builtin
+        // form measured 1.6% faster than the asm one here
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const void*>(src + (rem ? kbytes : 0)), rem);
+        dma16(rs, ring + sl * C::STAGE_BYTES + wave_lds + q * 1024, voff[q], 0u);
+      }
     };
 
     // accumulators start at the bias (bias epilogues) or zero; lane l holds columns
@@ -380,13 +440,14 @@ uint64_t mat_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
 }  // namespace
 
 bool onerole_fits(const DenseLaunch& d) {
-  // N x K second operand, 32-deep k-steps, enough 256 x 256 tiles to fill the chip, no split
-  return !d.b_kn && d.K % 32 == 0 && d.splits <= 1 && d.gidx == nullptr && d.P == nullptr &&
+  // 32-deep k-steps, enough 256 x 256 tiles to fill the chip, no split, no gathered start
+  return d.K % 32 == 0 && d.splits <= 1 && d.gidx == nullptr && d.P == nullptr &&
          ((d.M + 255) / 256) * ((d.N + 255) / 256) >= 128;
 }
 
-hipError_t launch_onerole(const DenseLaunch& d, hipStream_t stream) {
-  using C = CfgOneRole;
+template <bool KN>
+static hipError_t launch_onerole_cfg(const DenseLaunch& d, hipStream_t stream) {
+  using C = CfgOneRole<KN>;
   OneRoleArgs a{};
   a.A = reinterpret_cast<const __bf16*>(d.A);
   a.B = reinterpret_cast<const __bf16*>(d.B);
@@ -399,7 +460,7 @@ hipError_t launch_onerole(const DenseLaunch& d, hipStream_t stream) {
   a.epi = d.epi; a.out_f32 = d.out_f32;
   Guards& g = a.guard;
   span(d.A, mat_bytes(d.M, d.K, d.lda, 2), g.a_lo, g.a_hi);
-  span(d.B, mat_bytes(d.N, d.K, d.ldb, 2), g.b_lo, g.b_hi);
+  span(d.B, KN ? mat_bytes(d.K, d.N, d.ldb, 2) : mat_bytes(d.N, d.K, d.ldb, 2), g.b_lo, g.b_hi);
   span(d.C, mat_bytes(d.M, d.N, d.ldc, d.out_f32 ? 4 : 2), g.c_lo, g.c_hi);
   span(d.bias, (uint64_t)d.N * 4, g.bias_lo, g.bias_hi);
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
@@ -410,9 +471,14 @@ hipError_t launch_onerole(const DenseLaunch& d, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_onerole(const DenseLaunch& d, hipStream_t stream) {
+  return d.b_kn ? launch_onerole_cfg<true>(d, stream) : launch_onerole_cfg<false>(d, stream);
+}
+
 void onerole_describe(int32_t cfg[6]) {
-  cfg[0] = CfgOneRole::BM; cfg[1] = CfgOneRole::BN; cfg[2] = CfgOneRole::BK;
-  cfg[3] = CfgOneRole::STAGES; cfg[4] = 4; cfg[5] = 0;  // four waves, each copying and computing
+  using C = CfgOneRole<false>;  // the same tile for both layouts
+  cfg[0] = C::BM; cfg[1] = C::BN; cfg[2] = C::BK;
+  cfg[3] = C::STAGES; cfg[4] = 4; cfg[5] = 0;  // four waves, each copying and computing
 }
 
 hipError_t read_onerole_watchdog(uint32_t* value, int clear) {

@@ -57,8 +57,9 @@ def _no_watchdog(delay_lib):
 
 
 @pytest.mark.parametrize("layout,K,stages,producers", [(wl.B_NK, 4104, 2, 4),   # two-role (K mod 32 = 8)
-                                                       (wl.B_KN, 4096, 2, 4),   # two-role
-                                                       (wl.B_NK, 4096, 5, 0)])  # one-role
+                                                       (wl.B_KN, 4104, 2, 4),   # two-role
+                                                       (wl.B_NK, 4096, 5, 0),   # one-role
+                                                       (wl.B_KN, 4096, 5, 0)])  # one-role
 def test_stress_large_tile_long_k(delay_lib, layout, K, stages, producers):
     """Large tiles over a long K in the stress build: the two-role ring (producer and consumer
     waves hand slots over through LDS counters) and the one-role kernel (every wave copies and

@@ -160,10 +160,16 @@ def test_stress_pauses_only_in_the_test_build(asm, tmp_path):
     assert memtimes(out.read_text()) > 0
 
 
-def onerole_body(asm_text):
-    found = [body for name, body in kernels(asm_text) if "onerole_kernel" in name]
-    assert len(found) == 1
-    return found[0]
+def onerole_bodies(asm_text):
+    """{layout: kernel body} of the one-role kernel's two instantiations (B N x K, B K x N)."""
+    found = {}
+    for name, body in kernels(asm_text):
+        if "onerole_kernel" in name:
+            # the Cfg's B_KN flag is its eighth template argument
+            args = re.search(r"CfgILi256ELi256ELi32ELi5ELi2ELi2ELi4ELb(\d)", name)
+            found["kn" if args.group(1) == "1" else "nk"] = body
+    assert sorted(found) == ["kn", "nk"], sorted(found)
+    return found
 
 
 def wait_states(line):
@@ -194,29 +200,34 @@ def test_onerole_waits_for_its_asm_mfmas(asm, tmp_path, variant):
                         "--cuda-device-only", os.path.join(build.CSRC, src), "-o", str(out)],
                        check=True, capture_output=True)
         text = out.read_text()
+    for layout, body in onerole_bodies(text).items():
+        check_acc_waits(layout, body)
+    # everything inlined: no calls, no accumulators passed through memory
+    for body in onerole_bodies(text).values():
+        assert not any(re.match(r"\s+(s_swappc|s_setpc|flat_load|flat_store|scratch_)", l) for l in body)
+    assert not re.search(r"\n_ZZN3ptg12_GLOBAL__N_114onerole_kernel\S*:", text), "a lambda left out of line"
+
+
+def check_acc_waits(layout, body):
     since_mfma, since_acc_write = None, 99
     n_mfma = 0
-    for s in instructions(onerole_body(text)):
+    for s in instructions(body):
         if s.startswith("v_mfma"):
             n_mfma += 1
-            assert since_acc_write >= 3, f"accumulator written {since_acc_write} wait states before {s}"
+            assert since_acc_write >= 3, f"{layout}: accumulator written {since_acc_write} wait states before {s}"
             since_mfma = 0
             since_acc_write += 1
             continue
         reads_acc = re.match(r"(v_accvgpr_(read|mov)|buffer_store|v_cvt|v_permlane)", s)
         if since_mfma is not None and reads_acc:
-            assert since_mfma >= 20, f"{s}: {since_mfma} wait states after an MFMA"
+            assert since_mfma >= 20, f"{layout}: {s}: {since_mfma} wait states after an MFMA"
         if re.match(r"v_accvgpr_(write|mov)", s):
             since_acc_write = 0
         else:
             since_acc_write += wait_states(s)
         if since_mfma is not None:
             since_mfma += wait_states(s)
-    assert n_mfma >= 640
-    # everything inlined: no calls, no accumulators passed through memory
-    body = onerole_body(text)
-    assert not any(re.match(r"\s+(s_swappc|s_setpc|flat_load|flat_store|scratch_)", l) for l in body)
-    assert not re.search(r"\n_ZZN3ptg12_GLOBAL__N_114onerole_kernel\S*:", text), "a lambda left out of line"
+    assert n_mfma >= 640, layout
 
 
 def vgprs(op):
@@ -243,24 +254,28 @@ def test_onerole_mfma_sources_settle(asm, tmp_path, variant):
                         "--cuda-device-only", os.path.join(build.CSRC, src), "-o", str(out)],
                        check=True, capture_output=True)
         text = out.read_text()
-    recent = []  # (wait states since, registers written, instruction)
-    for s in instructions(onerole_body(text)):
-        if s.startswith("v_mfma"):
-            ops = [o.strip() for o in s.split(None, 1)[1].split(",")]
-            src = vgprs(ops[1]) | vgprs(ops[2])
-            for ago, w, txt in recent:
-                assert not (ago < 8 and w & src), f"{txt} then {s} after {ago} wait states"
-        elif s.startswith("v_") and not s.startswith("v_accvgpr_read") and " " in s:
-            recent.append((0, vgprs(s.split(None, 1)[1].split(",")[0].strip()), s))
-        recent = [(a + wait_states(s), w, x) for a, w, x in recent if a + wait_states(s) < 16]
+    for layout, body in onerole_bodies(text).items():
+        recent = []  # (wait states since, registers written, instruction)
+        for s in instructions(body):
+            if s.startswith("v_mfma"):
+                ops = [o.strip() for o in s.split(None, 1)[1].split(",")]
+                src = vgprs(ops[1]) | vgprs(ops[2])
+                for ago, w, txt in recent:
+                    assert not (ago < 8 and w & src), f"{layout}: {txt} then {s} after {ago} wait states"
+            elif s.startswith("v_") and not s.startswith("v_accvgpr_read") and " " in s:
+                recent.append((0, vgprs(s.split(None, 1)[1].split(",")[0].strip()), s))
+            recent = [(a + wait_states(s), w, x) for a, w, x in recent if a + wait_states(s) < 16]
 
 
 @pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
-def test_onerole_k_loop_is_lean(asm):
-    """The k-loop (the block of ten unrolled steps): 640 MFMAs, 160 fragment reads of 16 bytes,
-    80 copies to LDS, 10 barriers, and no more than 40 other vector instructions (the copies'
-    descriptor work), none of them writing LDS or touching scratch."""
-    body = onerole_body(asm)
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+def test_onerole_k_loop_is_lean(asm, layout):
+    """The k-loop (the block of ten unrolled steps): 640 MFMAs; the fragment reads (160 of 16
+    bytes for B stored N x K; for K x N, 80 of 16 bytes for A and 160 transposing 8-byte reads
+    for B); 80 copies to LDS; 10 barriers; no vector-memory wait for all copies; and no more
+    than 40 other vector instructions (the copies' descriptor work), none of them writing LDS
+    or touching scratch."""
+    body = onerole_bodies(asm)[layout]
     blocks, cur = [], None
     for line in body:
         if re.match(r"^(\.LBB\S+|; %bb\.\d+):", line):
@@ -272,9 +287,16 @@ def test_onerole_k_loop_is_lean(asm):
     assert len(loops) == 1
     loop = loops[0]
     count = lambda p: sum(1 for l in loop if l.startswith(p))
-    assert count("ds_read_b128") == 160
+    if layout == "nk":
+        assert count("ds_read_b128") == 160
+    else:
+        assert count("ds_read_b128") == 80 and count("ds_read_b64_tr_b16") == 160
     assert count("buffer_load_dwordx4") == 80 and all(" lds" in l for l in loop if l.startswith("buffer_load"))
     assert count("s_barrier") == 10
     assert count("ds_write") == 0 and count("scratch_") == 0
+    # the only vector-memory waits are the kernel's own per-step ones: a compiler wait for
+    # every copy in flight (before an LDS read it cannot tell from the copies) serialises
+    # copies and matrix work
+    assert count("s_waitcnt vmcnt(0)") == 0
     other_valu = [l for l in loop if l.startswith("v_") and not l.startswith(("v_mfma", "v_accvgpr"))]
     assert len(other_valu) <= 40, other_valu
