@@ -98,10 +98,16 @@ __device__ __forceinline__ void onerole_tile(uint64_t L, uint32_t tiles_m, uint3
 // copy in flight, which serialises copies and matrix work; it does not track asm.  The kernel
 // orders copies and reads itself (per-step vector-memory waits and the barrier).  The
 // descriptor is built in scalar registers: base, stride 0, size, the flags make_rsrc uses.
+// Nor does the compiler insert wait states before an asm instruction.  A copy to LDS right
+// after a scalar write of M0 may use the old M0 (the wrong place): the s_nop inside the asm
+// gives the one wait state needed.  A memory instruction reading a scalar register that a
+// vector instruction wrote (v_readfirstlane) needs 5: the descriptor words are computed with
+// scalar instructions only (checked on the compiled kernel), so none comes that way.
 __device__ __forceinline__ void copy_lds16(uint64_t base, uint32_t nbytes, uint32_t lds, uint32_t voff) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4s;
   const u32x4s d = {uni((uint32_t)base), uni((uint32_t)(base >> 32)) & 0xffffu, uni(nbytes), 0x00020000u};
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d), "{m0}"(uni(lds)) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(d), "{m0}"(uni(lds))
+               : "memory");
 }
 
 template <class C>
@@ -207,7 +213,9 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
     // gets an empty descriptor (no access, zeros)
     auto copy = [&](int st, int sl, int q) __attribute__((always_inline)) {
       const uint32_t kbytes = (uint32_t)st * C::BK * kstride;
-      const uint32_t rem = kbytes < bytes ? bytes - kbytes : 0u;
+      // bytes left from the step on (operand spans stay below 2 GiB); a signed maximum keeps it
+      // in scalar instructions (an unsigned clamp is done in vector ones)
+      const uint32_t rem = (uint32_t)max((int32_t)(bytes - kbytes), 0);
       if constexpr (C::B_KN) {
         copy_lds16(src + (rem ? kbytes : 0), rem, ring_lds + (uint32_t)(sl * C::STAGE_BYTES + wave_lds + q * 1024),
                    voff[q]);

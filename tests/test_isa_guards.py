@@ -267,6 +267,56 @@ def test_onerole_mfma_sources_settle(asm, tmp_path, variant):
             recent = [(a + wait_states(s), w, x) for a, w, x in recent if a + wait_states(s) < 16]
 
 
+def sgprs(op):
+    m = re.match(r"s\[(\d+):(\d+)\]", op)
+    if m:
+        return {f"s{i}" for i in range(int(m.group(1)), int(m.group(2)) + 1)}
+    return {op} if re.match(r"s\d+$", op) else set()
+
+
+@pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
+@pytest.mark.parametrize("variant", [None, "delay"])
+def test_onerole_copies_wait_for_their_scalar_operands(asm, tmp_path, variant):
+    """Every copy to LDS (a buffer load with the LDS flag) comes at least 5 wait states after a
+    vector instruction (v_readfirstlane, v_readlane) wrote a scalar register of its descriptor,
+    and at least 1 after a write of M0 (its LDS address); sooner, the load may read the old
+    value.  The compiler pads its own loads (B stored N x K), not the asm copies (K x N), which
+    carry the padding inside the asm.  Checked in code order, in the product and the stress
+    build."""
+    if variant is None:
+        text = asm
+    else:
+        out = tmp_path / "onerole_delay.s"
+        src = "ptg_onerole.hip"
+        subprocess.run([build.hipcc(), *build.compile_flags(build.VARIANTS[variant], source=src), "-S",
+                        "--cuda-device-only", os.path.join(build.CSRC, src), "-o", str(out)],
+                       check=True, capture_output=True)
+        text = out.read_text()
+    for layout, body in onerole_bodies(text).items():
+        since = {}  # scalar register (or m0) -> wait states since its last write of concern
+        copies = 0
+        for s in instructions(body):
+            if re.match(r"buffer_load\S* .* lds$", s):
+                copies += 1
+                ops = [o.strip() for o in s.split(None, 1)[1].split(",")]
+                for r in sgprs(ops[1]):
+                    assert since.get(r, 99) >= 5, f"{layout}: {s} reads {r} {since[r]} wait states after a vector write"
+                assert since.get("m0", 99) >= 1, f"{layout}: {s} right after a write of m0"
+            m = re.match(r"v_read(firstlane|lane)_b32 (s\d+),", s)
+            w = re.match(r"s_\w+ m0,", s)
+            for r in since:
+                since[r] += wait_states(s)
+            if m:
+                since[m.group(2)] = 0
+            elif re.match(r"s_\w+ (s\d+|s\[\d+:\d+\]),", s):
+                # a scalar write replaces the vector one
+                for r in sgprs(s.split(None, 1)[1].split(",")[0].strip()):
+                    since.pop(r, None)
+            if w:
+                since["m0"] = 0
+        assert copies >= 80, layout
+
+
 @pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
 @pytest.mark.parametrize("layout", ["nk", "kn"])
 def test_onerole_k_loop_is_lean(asm, layout):
