@@ -229,13 +229,16 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
     };
 
     // accumulators start at the bias (bias epilogues) or zero; lane l holds columns
-    // 4 (l / 16) .. + 3 of each 16-column block
+    // 4 (l / 16) .. + 3 of each 16-column block.  Without a bias nothing is loaded: the
+    // compiler waits for every memory access in flight before it uses a loaded value (it does
+    // not see that the asm copies issued after the loads are younger), which would hold the
+    // first step until the whole prologue has landed.
     f32x4 acc[TM][TN];
-    {
-      const bool do_bias = (args.epi == EPI_BIAS || args.epi == EPI_BIAS_SILU) && args.bias != nullptr;
+    const bool do_bias = (args.epi == EPI_BIAS || args.epi == EPI_BIAS_SILU) && args.bias != nullptr;
+    if (do_bias) {
       const uint64_t bp = uni64(reinterpret_cast<uint64_t>(args.bias + n0));
-      const bool bias_ok = do_bias && inside(bp, (uint64_t)n_cols * 4, uni64(gd.bias_lo), uni64(gd.bias_hi));
-      if (do_bias && !bias_ok && lane == 0) atomicOr(&g_watchdog, 8u);
+      const bool bias_ok = inside(bp, (uint64_t)n_cols * 4, uni64(gd.bias_lo), uni64(gd.bias_hi));
+      if (!bias_ok && lane == 0) atomicOr(&g_watchdog, 8u);
       const __amdgpu_buffer_rsrc_t rbias = make_rsrc(reinterpret_cast<const void*>(bp), bias_ok ? (uint32_t)n_cols * 4u : 0u);
 #pragma unroll
       for (int y = 0; y < TN; ++y) {
@@ -245,7 +248,18 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
 #pragma unroll
         for (int x = 0; x < TM; ++x) acc[x][y] = b4;
       }
+    } else {
+#pragma unroll
+      for (int y = 0; y < TN; ++y)
+#pragma unroll
+        for (int x = 0; x < TM; ++x) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // in accumulator registers before the first copy (else the compiler moves them into place
+    // after the prologue, behind its wait for every load in flight)
+#pragma unroll
+    for (int x = 0; x < TM; ++x)
+#pragma unroll
+      for (int y = 0; y < TN; ++y) asm volatile("" : "+a"(acc[x][y]));
     auto mf = [&](int x, int y, const bf16x8& fa, const bf16x8& fb) __attribute__((always_inline)) {
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[x][y]) : "v"(fb), "v"(fa));
     };
