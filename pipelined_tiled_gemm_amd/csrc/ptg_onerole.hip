@@ -50,7 +50,7 @@ struct OneRoleArgs {
   int64_t lda, ldb, ldc;
   int32_t M, N, K;
   int32_t tiles_m, tiles_n;
-  int32_t epi, out_f32;
+  int32_t epi;
   Guards guard;
 };
 
@@ -110,7 +110,9 @@ __device__ __forceinline__ void copy_lds16(uint64_t base, uint32_t nbytes, uint3
                : "memory");
 }
 
-template <class C>
+// F32: fp32 output (else bf16), a template argument: the two epilogues behind one runtime
+// branch make the compiler spill registers across the whole kernel
+template <class C, bool F32>
 __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
   constexpr int S = C::STAGES, L = C::LOADS;
@@ -383,65 +385,83 @@ __global__ __launch_bounds__(256, 1) void onerole_kernel(OneRoleArgs args) {
     // ... nor that the epilogue reads what they wrote: wait for the last MFMAs' results
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // the copies issued past the last step (empty descriptors) have landed and every wave is
-    // done with the ring before the next tile's prologue refills it
+    // done with the ring before the epilogue writes slot 4 and the next tile's prologue
+    // refills slots 0-3 (the empty asm keeps the epilogue's LDS writes after the barrier)
     wait_vmcnt<0>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    const uint32_t osz = args.out_f32 ? 4u : 2u;
+    constexpr uint32_t osz = F32 ? 4u : 2u;
     const uint64_t Cp = uni64(reinterpret_cast<uint64_t>(args.C + ((uint64_t)m0 * ldc + n0) * osz));
     const uint64_t c_bytes = ((uint64_t)(uint32_t)(m_rows - 1) * ldc + (uint32_t)n_cols) * osz;
     if (!inside(Cp, c_bytes, uni64(gd.c_lo), uni64(gd.c_hi))) {
       if (lane == 0) atomicOr(&g_watchdog, 8u);
       continue;
     }
-    // epilogue: SiLU if asked, conversion, whole 128-byte row segments per store (lane l
-    // holds columns 4 (l / 16) .. + 3 of each 16-column block, rows l mod 16)
+    // epilogue: SiLU if asked, conversion, and the store through LDS.  Lane l holds columns
+    // 4 (l / 16) .. + 3 of each 16-column block, row l mod 16.  Each wave writes its results
+    // into its own 8 KB of slot 4, a piece at a time (32 rows of bf16, 16 rows of fp32), reads
+    // them back as 16-byte chunks of whole rows and stores 256-byte (bf16) or 512-byte (fp32)
+    // row segments.  A chunk sits at position chunk ^ (row mod 16) in its row, so that neither
+    // the writes (16 rows at one column) nor the reads (whole rows) meet on one LDS bank.  The
+    // wave's LDS accesses run in order, so a piece's reads see its writes and precede the next
+    // piece's writes.  Slot 4 is next written by the copies of the next tile's step 4, issued
+    // after a barrier that each wave reaches once its epilogue is done.
     const bool do_silu = args.epi == EPI_SILU || args.epi == EPI_BIAS_SILU;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(reinterpret_cast<void*>(Cp), (uint32_t)c_bytes);
     // the lane index re-read here: offsets derived from it are not hoisted out of the tile loop
     // (they would be held across the k-loop, where no register is free)
     const int elane = opaque_lane();
-    const int grp = elane >> 4;
-    const int ldc_i = (int)args.ldc;
+    char* const stg = ring + 4 * C::STAGE_BYTES + w * 8192;
+    const uint32_t ldc_b = (uint32_t)args.ldc * osz;
+    auto put = [&](const u32x4_t& v, int row, int col) __attribute__((always_inline)) {
+      const uint32_t off = (row < m_rows && col < n_cols) ? (uint32_t)row * ldc_b + (uint32_t)col * osz : kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 2);  // non-temporal
+    };
+    auto act = [&](f32x4 v) __attribute__((always_inline)) -> f32x4 {
+      if (do_silu) {
 #pragma unroll
-    for (int x = 0; x < TM; ++x) {
-      const int row0 = wm * C::WTM + x * 16;
+        for (int t = 0; t < 4; ++t) v[t] = silu(v[t]);
+      }
+      return v;
+    };
+    const int r = elane & 15, g = elane >> 4;
+    if constexpr (!F32) {
+      // write: 8 bytes, columns y * 16 + 4 g .. + 3 of row 16 h + r (chunk 2 y + g / 2); read:
+      // row 4 i + g, chunk r (columns 8 r .. + 7)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4_t pair0 = {};
+      for (int pc = 0; pc < TM / 2; ++pc) {
 #pragma unroll
-        for (int y0 = 0; y0 < 4; y0 += 2) {
-          const int y = 4 * h + y0;
-          f32x4 v0 = acc[x][y], v1 = acc[x][y + 1];
-          if (do_silu) {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              v0[t] = silu(v0[t]);
-              v1[t] = silu(v1[t]);
-            }
+          for (int y = 0; y < TN; ++y) {
+            const f32x4 v = act(acc[2 * pc + h][y]);
+            const uint32_t lo = pack_bf16(v[0], v[1]), hi = pack_bf16(v[2], v[3]);
+            *reinterpret_cast<uint2*>(stg + h * 4096 + r * 256 + (((2 * y + (g >> 1)) ^ r) << 4) + (g & 1) * 8) =
+                uint2{lo, hi};
           }
-          if (args.out_f32) {
-            // blocks y and y + 1 of a row: 128 contiguous bytes
-            const int colX = wn * C::WTN + y * 16 + grp * 4;
-            store_rows128(__builtin_bit_cast(u32x4_t, v0), __builtin_bit_cast(u32x4_t, v1), colX, colX + 16, row0,
-                          elane, m_rows, n_cols, ldc_i, 4u, rc);
-          } else {
-            // bf16: runs of 4 packed to 8 bytes; v_permlane16_swap trades runs between the
-            // 16-lane groups so that group g holds columns 8 (g / 2) .. + 7 of block y + g % 2
-            const uint32_t x0 = pack_bf16(v0[0], v0[1]), x1 = pack_bf16(v0[2], v0[3]);
-            const uint32_t y0v = pack_bf16(v1[0], v1[1]), y1v = pack_bf16(v1[2], v1[3]);
-            const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0v, false, false);
-            const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1v, false, false);
-            const u32x4_t d = {s0[0], s1[0], s0[1], s1[1]};
-            if (y0 == 0) {
-              pair0 = d;
-            } else {
-              // the two block pairs y - 2 .. y + 1: 64 columns, 128 bytes per row
-              const int colX = wn * C::WTN + h * 64 + (grp & 1) * 16 + (grp >> 1) * 8;
-              store_rows128(pair0, d, colX, colX + 32, row0, elane, m_rows, n_cols, ldc_i, 2u, rc);
-            }
-          }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + g;
+          const u32x4_t d = *reinterpret_cast<const u32x4_t*>(stg + row * 256 + ((r ^ (row & 15)) << 4));
+          put(d, wm * C::WTM + 32 * pc + row, wn * C::WTN + 8 * r);
+        }
+      }
+    } else {
+      // write: 16 bytes, columns y * 16 + 4 g .. + 3 of row r (chunk 4 y + g); read: row
+      // 2 i + l / 32, chunk l mod 32 (columns 4 (l mod 32) .. + 3)
+      const int q = elane >> 5, c = elane & 31;
+#pragma unroll
+      for (int x = 0; x < TM; ++x) {
+#pragma unroll
+        for (int y = 0; y < TN; ++y)
+          *reinterpret_cast<f32x4*>(stg + r * 512 + (((4 * y + g) ^ r) << 4)) = act(acc[x][y]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 2 * i + q;
+          const u32x4_t d = *reinterpret_cast<const u32x4_t*>(stg + row * 512 + ((c ^ row) << 4));
+          put(d, wm * C::WTM + 16 * x + row, wn * C::WTN + 4 * c);
         }
       }
     }
@@ -479,7 +499,7 @@ static hipError_t launch_onerole_cfg(const DenseLaunch& d, hipStream_t stream) {
   a.M = (int32_t)d.M; a.N = (int32_t)d.N; a.K = (int32_t)d.K;
   a.tiles_m = (int32_t)((d.M + C::BM - 1) / C::BM);
   a.tiles_n = (int32_t)((d.N + C::BN - 1) / C::BN);
-  a.epi = d.epi; a.out_f32 = d.out_f32;
+  a.epi = d.epi;
   Guards& g = a.guard;
   span(d.A, mat_bytes(d.M, d.K, d.lda, 2), g.a_lo, g.a_hi);
   span(d.B, KN ? mat_bytes(d.K, d.N, d.ldb, 2) : mat_bytes(d.N, d.K, d.ldb, 2), g.b_lo, g.b_hi);
@@ -489,7 +509,10 @@ static hipError_t launch_onerole_cfg(const DenseLaunch& d, hipStream_t stream) {
   const int cus = device_compute_units();
   if (cus <= 0) return hipErrorNoDevice;
   const int grid = (int)(tiles < cus ? tiles : cus);
-  hipLaunchKernelGGL(onerole_kernel<C>, dim3(grid), dim3(256), 0, stream, a);
+  if (d.out_f32)
+    hipLaunchKernelGGL((onerole_kernel<C, true>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((onerole_kernel<C, false>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

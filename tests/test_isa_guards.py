@@ -161,14 +161,15 @@ def test_stress_pauses_only_in_the_test_build(asm, tmp_path):
 
 
 def onerole_bodies(asm_text):
-    """{layout: kernel body} of the one-role kernel's two instantiations (B N x K, B K x N)."""
+    """{form: kernel body} of the one-role kernel's four instantiations: B N x K or K x N
+    ("nk", "kn"), bf16 or fp32 output (suffix "_f32")."""
     found = {}
     for name, body in kernels(asm_text):
         if "onerole_kernel" in name:
-            # the Cfg's B_KN flag is its eighth template argument
-            args = re.search(r"CfgILi256ELi256ELi32ELi5ELi2ELi2ELi4ELb(\d)", name)
-            found["kn" if args.group(1) == "1" else "nk"] = body
-    assert sorted(found) == ["kn", "nk"], sorted(found)
+            # the Cfg's B_KN flag is its eighth template argument; the output flag follows the Cfg
+            args = re.search(r"CfgILi256ELi256ELi32ELi5ELi2ELi2ELi4ELb(\d)\S*?EEELb(\d)E", name)
+            found[("kn" if args.group(1) == "1" else "nk") + ("_f32" if args.group(2) == "1" else "")] = body
+    assert sorted(found) == ["kn", "kn_f32", "nk", "nk_f32"], sorted(found)
     return found
 
 
@@ -318,7 +319,7 @@ def test_onerole_copies_wait_for_their_scalar_operands(asm, tmp_path, variant):
 
 
 @pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
-@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("layout", ["nk", "kn", "nk_f32", "kn_f32"])
 def test_onerole_k_loop_is_lean(asm, layout):
     """The k-loop (the block of ten unrolled steps): 640 MFMAs; the fragment reads (160 of 16
     bytes for B stored N x K; for K x N, 80 of 16 bytes for A and 160 transposing 8-byte reads
@@ -337,7 +338,7 @@ def test_onerole_k_loop_is_lean(asm, layout):
     assert len(loops) == 1
     loop = loops[0]
     count = lambda p: sum(1 for l in loop if l.startswith(p))
-    if layout == "nk":
+    if layout.startswith("nk"):
         assert count("ds_read_b128") == 160
     else:
         assert count("ds_read_b128") == 80 and count("ds_read_b64_tr_b16") == 160
