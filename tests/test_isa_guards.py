@@ -294,28 +294,59 @@ def test_onerole_copies_wait_for_their_scalar_operands(asm, tmp_path, variant):
                        check=True, capture_output=True)
         text = out.read_text()
     for layout, body in onerole_bodies(text).items():
-        since = {}  # scalar register (or m0) -> wait states since its last write of concern
-        copies = 0
-        for s in instructions(body):
-            if re.match(r"buffer_load\S* .* lds$", s):
-                copies += 1
-                ops = [o.strip() for o in s.split(None, 1)[1].split(",")]
-                for r in sgprs(ops[1]):
-                    assert since.get(r, 99) >= 5, f"{layout}: {s} reads {r} {since[r]} wait states after a vector write"
-                assert since.get("m0", 99) >= 1, f"{layout}: {s} right after a write of m0"
-            m = re.match(r"v_read(firstlane|lane)_b32 (s\d+),", s)
-            w = re.match(r"s_\w+ m0,", s)
-            for r in since:
-                since[r] += wait_states(s)
-            if m:
-                since[m.group(2)] = 0
-            elif re.match(r"s_\w+ (s\d+|s\[\d+:\d+\]),", s):
-                # a scalar write replaces the vector one
-                for r in sgprs(s.split(None, 1)[1].split(",")[0].strip()):
-                    since.pop(r, None)
-            if w:
-                since["m0"] = 0
+        copies, bad = copy_operand_violations(instructions(body))
+        assert not bad, f"{layout}: {bad[:3]}"
         assert copies >= 80, layout
+
+
+def copy_operand_violations(lines):
+    """(number of copies to LDS, list of violations) in an instruction sequence, in code order:
+    a copy less than 5 wait states after a v_readfirstlane/v_readlane wrote a scalar register of
+    its descriptor (a scalar write of that register in between clears it), or right after a
+    write of M0."""
+    since = {}  # scalar register (or m0) -> wait states since its last write of concern
+    copies, bad = 0, []
+    for s in lines:
+        if re.match(r"buffer_load\S* .* lds$", s):
+            copies += 1
+            ops = [o.strip() for o in s.split(None, 1)[1].split(",")]
+            for r in sgprs(ops[1]):
+                if since.get(r, 99) < 5:
+                    bad.append(f"{s} reads {r} {since[r]} wait states after a vector write")
+            if since.get("m0", 99) < 1:
+                bad.append(f"{s} right after a write of m0")
+        m = re.match(r"v_read(firstlane|lane)_b32 (s\d+),", s)
+        w = re.match(r"s_\w+ m0,", s)
+        for r in since:
+            since[r] += wait_states(s)
+        if m:
+            since[m.group(2)] = 0
+        elif re.match(r"s_\w+ (s\d+|s\[\d+:\d+\]),", s):
+            # a scalar write replaces the vector one
+            for r in sgprs(s.split(None, 1)[1].split(",")[0].strip()):
+                since.pop(r, None)
+        if w:
+            since["m0"] = 0
+    return copies, bad
+
+
+def test_copy_operand_check_flags_hazards():
+    """The check above on hand-written sequences: it flags a descriptor word or M0 written too
+    shortly before a copy, and passes the padded and the unrelated cases."""
+    load = "buffer_load_dwordx4 v139, s[16:19], 0 offen lds"
+    cases = {
+        ("v_readfirstlane_b32 s18, v128", load): 1,                     # size word, no wait
+        ("v_readfirstlane_b32 s16, v1", "s_nop 2", load): 1,            # 3 wait states
+        ("v_readfirstlane_b32 s18, v128", "s_nop 4", load): 0,          # 5 wait states
+        ("v_readfirstlane_b32 s30, v128", load): 0,                     # not a descriptor word
+        ("v_readfirstlane_b32 s18, v128", "s_mov_b32 s18, s5", load): 0,  # rewritten by a scalar op
+        ("s_mov_b32 m0, s67", load): 1,                                 # M0, no wait
+        ("s_add_i32 m0, s4, 0x1000", "s_nop 0", load): 0,               # M0, one wait state
+        ("s_mov_b32 m0, s67", "v_readfirstlane_b32 s17, v2", load): 1,  # M0 waited, s17 not
+    }
+    for seq, n in cases.items():
+        copies, bad = copy_operand_violations(list(seq))
+        assert copies == 1 and len(bad) == n, (seq, bad)
 
 
 @pytest.mark.skipif(hipcc_missing, reason="needs hipcc")
