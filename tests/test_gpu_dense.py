@@ -119,7 +119,8 @@ def test_integer_exact_8192_full():
     """The headline shape and launch configuration (8192^3, B stored N x K, large tiles) on
     integer entries in [-4, 4]: every partial sum is an integer below 2^24, exact in fp32 in
     any order, so the whole 8192 x 8192 output must equal the oracle bit for bit (fp32
-    output), and the bf16 output must be its correct rounding."""
+    output), and the bf16 output must be its correct rounding.  The same B stored K x N (its
+    transpose, the other form of the kernel) must give the same fp32 output."""
     M = N = K = 8192
     rng = np.random.default_rng(8192)
     A = int_bf16(rng, (M, K))
@@ -128,10 +129,14 @@ def test_integer_exact_8192_full():
     dA, dB = dev_bf16(A), dev_bf16(B)
     out = ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.float32)
     out16 = ptg.gemm(dA, dB, b_layout=wl.B_NK, out_dtype=torch.bfloat16)
-    del dA, dB
+    dBt = dB.t().contiguous()
+    del dB
+    out_kn = ptg.gemm(dA, dBt, b_layout=wl.B_KN, out_dtype=torch.float32)
+    del dA, dBt
     v = oracle.gemm(A, B, wl.B_NK)
     exact(out, v, "integer 8192^3 fp32")
     exact(out16, v, "integer 8192^3 bf16")
+    exact(out_kn, v, "integer 8192^3 fp32, B stored K x N")
 
 
 @pytest.mark.parametrize("layout", [wl.B_KN, wl.B_NK])
