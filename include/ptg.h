@@ -345,8 +345,9 @@ ptg_status ptg_watchdog(uint32_t* value, int32_t clear);
 
 /* Library version, and the tile configuration the dense path would pick for (M, N, K):
  * writes BM, BN, BK, stages, consumer waves, producer waves into cfg[0..5].  Producer waves 0
- * marks the one-role kernel, whose waves both copy and compute (B stored N x K, K a multiple
- * of 32, at least 128 tiles of 256 x 256).  For tests and logging; returns
+ * marks the one-role kernel, whose waves both copy and compute (either B layout, K a multiple
+ * of 32, and at least 128 tiles of 256 x 256 or more tiles of 128 x 128 than the device has
+ * compute units).  For tests and logging; returns
  * PTG_ERR_INVALID_ARG for a NULL cfg. */
 int32_t ptg_version(void);
 ptg_status ptg_describe_config(int64_t M, int64_t N, int64_t K, ptg_layout b_layout, int32_t cfg[6]);

@@ -482,9 +482,16 @@ uint64_t mat_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
 }  // namespace
 
 bool onerole_fits(const DenseLaunch& d) {
-  // 32-deep k-steps, enough 256 x 256 tiles to fill the chip, no split, no gathered start
-  return d.K % 32 == 0 && d.splits <= 1 && d.gidx == nullptr && d.P == nullptr &&
-         ((d.M + 255) / 256) * ((d.N + 255) / 256) >= 128;
+  // 32-deep k-steps, no split, no gathered start; and enough 256 x 256 tiles to fill the chip
+  // (at least 128), or more 128 x 128 tiles than CUs: there the medium tile needs a second,
+  // partial round, while these tiles take one.  From 72 to 121 tiles of 256 x 256 (K = 512 to
+  // 8192) this kernel measured 7-19% faster than the medium tile; at 64 (2048^2, 256 medium
+  // tiles: one full round) the medium tile was faster.
+  if (d.K % 32 != 0 || d.splits > 1 || d.gidx != nullptr || d.P != nullptr) return false;
+  const int64_t large = ((d.M + 255) / 256) * ((d.N + 255) / 256);
+  const int64_t medium = ((d.M + 127) / 128) * ((d.N + 127) / 128);
+  const int cus = device_compute_units();
+  return large >= 128 || (cus > 0 && medium > cus);
 }
 
 template <bool KN>

@@ -2,7 +2,7 @@
 tiles in five LDS slots) against the fp64 CPU oracle.
 
 ptg_gemm takes this kernel when K is a multiple of 32 and the output has at least 128 tiles of
-256 x 256, with B stored N x K or K x N (whose fragments are read with transposing LDS reads).  The cases cover every remainder of the unrolled k-loop (ten
+256 x 256 (or more tiles of 128 x 128 than the device has CUs), with B stored N x K or K x N (whose fragments are read with transposing LDS reads).  The cases cover every remainder of the unrolled k-loop (ten
 32-deep steps per pass: one to ten steps after zero, one or two passes), output grids whose 16 x 16 tile blocks and 4-row strips are partial
 (including the reversed odd block rows), ragged M and N, every epilogue and both output types,
 and strided operands and outputs inside guard bands.  Integer data make the fp32 result exact
@@ -45,7 +45,9 @@ def test_routing():
     assert onerole(8192, 8192, 8192, wl.B_KN)
     assert not onerole(4096, 4096, 264)                # K not a multiple of 32
     assert not onerole(4096, 4096, 264, wl.B_KN)
-    assert not onerole(2048, 2048, 1024)               # 64 tiles: too few to fill the chip
+    assert not onerole(2048, 2048, 1024)               # 64 tiles; 256 medium tiles fill one round
+    assert onerole(2304, 2304, 512)                    # 81 tiles; 324 medium tiles need two rounds
+    assert onerole(4096, 1536, 4096, wl.B_KN)          # 96 tiles
     cfg = ptg.describe_config(8192, 8192, 8192, wl.B_NK)
     assert (cfg["BM"], cfg["BN"], cfg["BK"], cfg["stages"]) == (256, 256, 32, 5)
 
@@ -129,6 +131,19 @@ def test_strided_operands_and_guard_bands(out_dtype, layout):
     inside = torch.zeros_like(g, dtype=torch.bool)
     inside[1:M + 1, 8:8 + N] = True
     assert bool(torch.isnan(g[~inside]).all()), "guard band overwritten"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fewer_large_tiles_than_half_the_chip(layout):
+    """A grid of 9 x 9 large tiles (81, under 128, but 324 medium tiles: more than one round),
+    ragged in M and N, integer data, bit-exact."""
+    M, N, K = 2304 - 40, 2304 - 8, 384
+    assert onerole(M, N, K, layout)
+    rng = np.random.default_rng(2304 + layout)
+    A, B = int_bf16(rng, (M, K)), b_of(rng, N, K, layout)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ptg.gemm(dev_bf16(A), dev_bf16(B), b_layout=layout, out=out)
+    exact(out, oracle.gemm(A, B, layout), f"one-role 81 tiles layout={layout}")
 
 
 def test_repeat_and_layouts_agree():
